@@ -1,0 +1,191 @@
+"""Leviathan acceptance walked down a draft tree (float64).
+
+Parity: pinned (tests/test_oracle_accept.py) by exact enumeration of the
+first- and second-token marginals on tiny trees (they must equal the
+verifier's distributions), a 50,000-step chi-square test of the first emitted
+token, the closed form for the expected number of emitted tokens of an i.i.d.
+chain, a brute-force greedy check at T = 0, the inverse-CDF definition on
+hand-worked cases, and the special cases the pages fix.
+
+Rule (page "推测解码与 EAGLE-3", section "不变量：Leviathan 拒绝采样" and
+build steps 1-3): a draft token d drawn from the draft distribution p is
+accepted with probability min(1, q(d)/p(d)), q being the verifier's
+distribution; on rejection one token is drawn from the residual
+(q - p)_+ / ||(q - p)_+||_1 and the step stops; when every draft is accepted
+a bonus token is drawn from the verifier's distribution after the last one.
+The comparison is strict and a draft token with p(d) <= 0 is accepted (step
+1); a residual of zero mass falls back to the distribution being corrected
+(step 2).  The same rule appears with the letters swapped on page
+"EAGLE-1/2/3 拆解", section "无损性的来源与它的证明位置".
+
+Trees.  A node counts only if all nodes on its root path are accepted (page
+"EAGLE-1/2/3 拆解", section "一个可核对的经验性质"), so the walk starts at the
+root and descends.  The pages give the rule for one child per node only.
+Reading used for several children (all drawn independently from the same
+draft distribution p_v of their parent): test the children in ascending node
+id; after each rejection replace the distribution being tested by its
+residual against p_v; sample the terminal token from the distribution left
+after the last rejection.  With one child this is exactly the pages' rule,
+and it keeps the output distribution equal to q (checked by enumeration).
+
+Temperature.  q = softmax(logits / T); T = 0 means greedy decoding: a draft is
+accepted iff it equals the verifier's argmax (lowest id on ties) and the
+terminal token is that argmax (page "EAGLE-1/2/3 拆解", opening section,
+Temperature = 0 is greedy decoding, and the eagenerate flow section: the
+longest passing prefix plus one corrected token lands each cycle).
+
+Near ties.  Decisions whose |u - min(1, ratio)| < TIE_BAND and samples whose
+threshold u * W lies within SAMPLE_BAND * W of an edge of the chosen bucket
+are flagged; a flagged sequence-step is excluded from bit-exact comparison
+with another implementation and logged.
+"""
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+from .validate import ERR_NONFINITE, ERR_TOKEN, ERR_TREE, validate_tree
+
+TIE_BAND = 1e-6
+SAMPLE_BAND = 1e-9
+
+
+def target_distribution(logit_row, T):
+    """q = softmax(logits / T), float64."""
+    x = np.asarray(logit_row, dtype=np.float64) / float(T)
+    e = np.exp(x - x.max())
+    return e / e.sum()
+
+
+def accept_rule(q_x, p_x, u):
+    """Build step 1: accept when p(x) <= 0, else iff u < min(1, q(x)/p(x))."""
+    if p_x <= 0.0:
+        return True, np.inf
+    thr = min(1.0, q_x / p_x)
+    return bool(u < thr), thr
+
+
+def residual(q, p):
+    """Build step 2: (q - p)_+ normalised; zero mass returns q unchanged."""
+    raw = np.maximum(0.0, q - p)
+    s = raw.sum()
+    if s == 0.0:
+        return np.array(q, dtype=np.float64, copy=True)
+    return raw / s
+
+
+def sample_inverse_cdf(dist, u):
+    """Token drawn from `dist` with uniform u in [0, 1).
+
+    Reading (the pages do not fix the sampling procedure): inverse CDF in
+    ascending token id -- the smallest i whose running sum exceeds u times the
+    total; if rounding leaves none, the last i with positive mass.  Returns
+    (i, margin) with margin the distance of u * total to the nearer edge of
+    bucket i, relative to the total.
+    """
+    cdf = np.cumsum(dist)
+    total = cdf[-1]
+    t = float(u) * total
+    i = int(np.searchsorted(cdf, t, side="right"))
+    if i >= len(dist):
+        i = int(np.nonzero(np.asarray(dist) > 0)[0][-1])
+    lo = cdf[i - 1] if i > 0 else 0.0
+    margin = min(abs(t - lo), abs(cdf[i] - t)) / total
+    return i, float(margin)
+
+
+@dataclass
+class AcceptResult:
+    accept_len: int                      # accepted drafts a (-1 on error)
+    path: List[int]                      # node ids root..deepest accepted (a + 1)
+    out_tokens: List[int]                # a accepted drafts, then the terminal token
+    final_dist: Optional[np.ndarray]     # distribution the terminal token came from
+    decisions: list = field(default_factory=list)  # (node, child, kind, u, value, margin, accepted)
+    near_tie: bool = False
+    error: int = 0
+
+
+def _fail(err):
+    return AcceptResult(-1, [], [], None, [], False, err)
+
+
+def accept_tree(tokens, parents, n_nodes, draft_p, logits, T, u_accept, u_sample,
+                max_depth, n_max=None):
+    """One sequence's acceptance walk.
+
+    tokens/parents/u_accept/u_sample: [n_max]; draft_p/logits: [n_max][V].
+    Node 0 is the pending root; row v of draft_p is the distribution the
+    children of v were drawn from, row v of logits the verifier's logits
+    after v.
+    """
+    n = int(n_nodes)
+    if n_max is None:
+        n_max = len(parents)
+    ok, _ = validate_tree(parents, n, n_max, max_depth)
+    if not ok:
+        return _fail(ERR_TREE)
+    V = np.asarray(logits[0]).shape[-1]
+    toks = [int(t) for t in tokens[:n]]
+    if any(t < 0 or t >= V for t in toks[1:]):
+        return _fail(ERR_TOKEN)
+    children = [[] for _ in range(n)]
+    for j in range(1, n):
+        children[int(parents[j])].append(j)
+
+    v = 0
+    path = [0]
+    out = []
+    decisions = []
+    near = False
+    while True:
+        lrow = np.asarray(logits[v], dtype=np.float64)
+        if not np.all(np.isfinite(lrow)):
+            return _fail(ERR_NONFINITE)
+        if T == 0:
+            best = int(np.argmax(lrow))
+            nxt = next((c for c in children[v] if toks[c] == best), None)
+            decisions.append((v, -1 if nxt is None else nxt, "argmax", None, best, None,
+                              nxt is not None))
+            out.append(best)
+            if nxt is None:
+                final = np.zeros(V)
+                final[best] = 1.0
+                break
+            path.append(nxt)
+            v = nxt
+            continue
+
+        cur = target_distribution(lrow, T)
+        prow = None
+        nxt = None
+        for c in children[v]:
+            x = toks[c]
+            px = float(draft_p[v][x])
+            if not np.isfinite(px):
+                return _fail(ERR_NONFINITE)
+            u = float(u_accept[c])
+            acc, thr = accept_rule(cur[x], px, u)
+            margin = abs(u - thr) if np.isfinite(thr) else np.inf
+            near |= margin < TIE_BAND
+            decisions.append((v, c, "accept-test", u, thr, margin, acc))
+            if acc:
+                nxt = c
+                break
+            if prow is None:
+                prow = np.asarray(draft_p[v], dtype=np.float64)
+                if not np.all(np.isfinite(prow)):
+                    return _fail(ERR_NONFINITE)
+            cur = residual(cur, prow)
+        if nxt is not None:
+            path.append(nxt)
+            out.append(toks[nxt])
+            v = nxt
+            continue
+        us = float(u_sample[v])
+        tok, margin = sample_inverse_cdf(cur, us)
+        near |= margin < SAMPLE_BAND
+        decisions.append((v, -1, "sample", us, tok, margin, None))
+        out.append(tok)
+        final = cur
+        break
+    return AcceptResult(len(path) - 1, path, out, final, decisions, near, 0)

@@ -1,0 +1,35 @@
+"""KV commit of the accepted path (plain copies).
+
+Parity: pinned (tests/test_oracle_commit.py) by the bookkeeping invariants of
+page "推测解码与 EAGLE-3", section "KV cache 回滚" and build step 4, and the
+page's batched-rollback exercise worked out by hand under tests/golden/.
+
+The verify pass has written the K/V of every tree node into cache rows
+prefix_len + i.  Rollback is either a physical cache with a logical length
+that is cut back on rejection, or a scratch area committed on acceptance
+(section "KV cache 回滚").  For a tree, the accepted path's rows are in
+general scattered, so they are gathered to the rows right after the prefix:
+row prefix_len + i receives the pre-commit row prefix_len + path[i], for the
+root (i = 0) and the a accepted drafts.
+
+Reading of the logical length (build step 4 sets it to prefix_length + j + 1
+on rejection at position j): j is the number of accepted drafts and the +1 is
+the root, the previous step's emitted token whose KV this pass produced.  The
+terminal (corrected or bonus) token has no KV yet; it becomes the next root.
+"""
+import numpy as np
+
+
+def kv_commit(k, v, prefix_len, path, accept_len):
+    """k, v: [Hkv][L_cap][d] of one sequence.  Returns (k', v', new_len)."""
+    k = np.asarray(k)
+    v = np.asarray(v)
+    if accept_len < 0:
+        return k.copy(), v.copy(), int(prefix_len)
+    L = int(prefix_len)
+    k2 = k.copy()
+    v2 = v.copy()
+    for i in range(int(accept_len) + 1):
+        k2[:, L + i] = k[:, L + int(path[i])]
+        v2[:, L + i] = v[:, L + int(path[i])]
+    return k2, v2, L + int(accept_len) + 1
