@@ -1,0 +1,210 @@
+"""Thin Python binding of libspecverify.so (include/spec_verify.h).
+
+Argument marshalling only: tensors are handed to the C ABI as device
+pointers together with torch's current HIP stream, and every step of the
+verify path runs in the library's kernels.  Output tensors are allocated with
+torch (device memory is torch's job here).  There is no fallback: if the
+shared library is missing, `load()` raises.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspecverify.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "spec_verify.h")
+
+SPEC_F32, SPEC_BF16 = 0, 1
+DEVERR_TREE, DEVERR_TOKEN, DEVERR_NONFINITE, DEVERR_CAPACITY, DEVERR_SYNC = 1, 2, 4, 8, 16
+TIE_DTYPE = np.dtype([("b", "<i4"), ("node", "<i4"), ("kind", "<i4"), ("u", "<f4"),
+                      ("margin", "<f8")])
+
+_lib = None
+
+
+class SpecError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        msg = _lib.spec_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+
+
+def declared_functions():
+    """Names of the functions include/spec_verify.h declares."""
+    with open(HEADER) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z_]+)\s*\(", text)))
+
+
+def load():
+    """Load the HIP library (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                           "`python -m eagle_tree_verification_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    lib.spec_verify_tree_attn.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, Z, P, P]
+    lib.spec_verify_tree_attn.restype = I
+    lib.spec_verify_tree_attn_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.spec_verify_tree_attn_workspace_size.restype = Z
+    lib.spec_accept_tree.argtypes = [P, P, P, P, P, I, I, I, I, F, P, P, P, P, P, P, P, P, I, P,
+                                     P, Z, P, P]
+    lib.spec_accept_tree.restype = I
+    lib.spec_accept_tree_workspace_size.argtypes = [I, I, I]
+    lib.spec_accept_tree_workspace_size.restype = Z
+    lib.spec_kv_commit.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P]
+    lib.spec_kv_commit.restype = I
+    lib.spec_status_string.argtypes = [I]
+    lib.spec_status_string.restype = ctypes.c_char_p
+    lib.spec_abi_version.argtypes = []
+    lib.spec_abi_version.restype = I
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, status):
+    if status != 0:
+        raise SpecError(fn, status)
+
+
+def _dev(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _kv_dtype(t):
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    raise TypeError(f"unsupported KV dtype {t.dtype}")
+
+
+def verify_tree_attn_workspace_size(B, n_max, Hq, Hkv, head_dim, L_cap, dtype):
+    return int(load().spec_verify_tree_attn_workspace_size(B, n_max, Hq, Hkv, head_dim, L_cap, dtype))
+
+
+def accept_tree_workspace_size(B, n_max, V):
+    return int(load().spec_accept_tree_workspace_size(B, n_max, V))
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def verify_tree_attn(q, k_cache, v_cache, prefix_len, n_nodes, parents, *, scale=None, out=None,
+                     workspace=None, dev_error=None, stream=None):
+    """Tree-masked attention; returns out [B][n_max][Hq][d] float32."""
+    lib = load()
+    B, n_max, Hq, d = q.shape
+    _, Hkv, L_cap, _ = k_cache.shape
+    dt = _kv_dtype(k_cache)
+    for t, nm in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, nm, k_cache.dtype)
+    for t, nm in ((prefix_len, "prefix_len"), (n_nodes, "n_nodes"), (parents, "parents")):
+        _dev(t, nm, torch.int32)
+    if out is None:
+        out = torch.empty((B, n_max, Hq, d), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(d))
+    ws, wsb = _workspace(verify_tree_attn_workspace_size(B, n_max, Hq, Hkv, d, L_cap, dt),
+                         q.device, workspace)
+    st = lib.spec_verify_tree_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(prefix_len),
+                                   _ptr(n_nodes), _ptr(parents), B, n_max, Hq, Hkv, d, L_cap,
+                                   float(scale), dt, _ptr(out), _ptr(ws), wsb, _ptr(dev_error),
+                                   _stream(stream))
+    _check("spec_verify_tree_attn", st)
+    return out
+
+
+def accept_tree(tokens, parents, n_nodes, draft_p, logits, temperature, u_accept, u_sample,
+                max_depth, *, final_dist=False, tie_cap=0, workspace=None, dev_error=None,
+                outputs=None, stream=None):
+    """Acceptance walk; returns a dict of device tensors.
+
+    Keys: accept_len [B], path [B][max_depth+1], out_tokens [B][max_depth+1],
+    n_out [B], final_dist [B][V] or None, tie_log (uint8 bytes of tie_cap
+    spec_tie_t records) or None, tie_count [1] or None.
+    """
+    lib = load()
+    B, n_max, V = logits.shape
+    dev = logits.device
+    for t, nm in ((tokens, "tokens"), (parents, "parents"), (n_nodes, "n_nodes")):
+        _dev(t, nm, torch.int32)
+    for t, nm in ((draft_p, "draft_p"), (logits, "logits"), (u_accept, "u_accept"),
+                  (u_sample, "u_sample")):
+        _dev(t, nm, torch.float32)
+    o = outputs or {}
+
+    def _out(key, shape):
+        t = o.get(key)
+        return torch.empty(shape, dtype=torch.int32, device=dev) if t is None else _dev(t, key, torch.int32)
+
+    acc = _out("accept_len", (B,))
+    path = _out("path", (B, max_depth + 1))
+    toks = _out("out_tokens", (B, max_depth + 1))
+    nout = _out("n_out", (B,))
+    fd = torch.empty((B, V), dtype=torch.float32, device=dev) if final_dist else None
+    tlog = torch.zeros(max(tie_cap, 1) * TIE_DTYPE.itemsize, dtype=torch.uint8, device=dev) if tie_cap else None
+    tcount = torch.zeros(1, dtype=torch.int32, device=dev) if tie_cap else None
+    ws, wsb = _workspace(accept_tree_workspace_size(B, n_max, V), dev, workspace)
+    st = lib.spec_accept_tree(_ptr(tokens), _ptr(parents), _ptr(n_nodes), _ptr(draft_p),
+                              _ptr(logits), B, n_max, V, int(max_depth), float(temperature),
+                              _ptr(u_accept), _ptr(u_sample), _ptr(acc), _ptr(path), _ptr(toks),
+                              _ptr(nout), _ptr(fd), _ptr(tlog), int(tie_cap), _ptr(tcount),
+                              _ptr(ws), wsb, _ptr(dev_error), _stream(stream))
+    _check("spec_accept_tree", st)
+    return {"accept_len": acc, "path": path, "out_tokens": toks, "n_out": nout,
+            "final_dist": fd, "tie_log": tlog, "tie_count": tcount}
+
+
+def decode_ties(tie_log, tie_count):
+    """Host copy of the logged near-tie records."""
+    if tie_log is None:
+        return np.zeros(0, dtype=TIE_DTYPE)
+    cnt = int(tie_count.item())
+    cap = tie_log.numel() // TIE_DTYPE.itemsize
+    raw = tie_log.cpu().numpy().view(TIE_DTYPE)
+    return raw[: min(cnt, cap)].copy()
+
+
+def kv_commit(k_cache, v_cache, prefix_len, path, accept_len, max_depth, *, dev_error=None,
+              stream=None):
+    """Commit the accepted paths in place (k_cache, v_cache, prefix_len)."""
+    lib = load()
+    B, Hkv, L_cap, d = k_cache.shape
+    dt = _kv_dtype(k_cache)
+    _dev(k_cache, "k_cache")
+    _dev(v_cache, "v_cache", k_cache.dtype)
+    for t, nm in ((prefix_len, "prefix_len"), (path, "path"), (accept_len, "accept_len")):
+        _dev(t, nm, torch.int32)
+    st = lib.spec_kv_commit(_ptr(k_cache), _ptr(v_cache), _ptr(prefix_len), _ptr(path),
+                            _ptr(accept_len), B, Hkv, d, L_cap, int(max_depth), dt,
+                            _ptr(dev_error), _stream(stream))
+    _check("spec_kv_commit", st)

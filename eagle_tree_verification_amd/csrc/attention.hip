@@ -1,0 +1,640 @@
+// Tree-masked attention for draft-tree verification (gfx950).
+//
+// Every draft-tree node attends to the whole committed prefix and to the
+// nodes on its own root path, itself included: the verifier's attention uses
+// a non-causal mask that follows the tree (page "推测解码与 EAGLE-3", section
+// "KV cache 回滚"; page "EAGLE-1/2/3 拆解", section on EAGLE-2's two stages,
+// identity initial tree mask; page "EAGLE-3 完全拆解", section on the
+// training-time mask, ancestors only).  The tree rows sit right behind the
+// prefix in the cache, so one sweep over keys [0, L + n) serves every node:
+// prefix keys are visible to all nodes and key L + j is visible to node i iff
+// bit j of i's ancestor mask is set.  Only the dot products the mask needs
+// for the prefix part are dense; the tree part is one 64-key tile.
+//
+// Two implementations:
+//   * attn_mfma_kernel (bf16, head_dim 128): one workgroup per (sequence,
+//     KV head, row block, prefix split).  All n * (Hq/Hkv) query rows of a KV
+//     head share each K/V tile, so the tile is streamed once from HBM into
+//     LDS and every wave contracts it with its own 32- or 64-row Q block on
+//     the matrix cores (v_mfma_f32_32x32x16_bf16).  Scores are produced
+//     transposed (keys x query rows) so each lane owns one query row and the
+//     online-softmax row statistics need a single cross-lane exchange.
+//   * attn_valu_kernel (f32 or bf16, any head_dim): one wave per (sequence,
+//     node, head) on the vector ALU; used for small or f32 problems.
+// Splits of the prefix are merged by attn_merge_kernel (log-sum-exp).
+#include <math.h>
+
+#include "common.hpp"
+
+namespace specv {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// Tree validation and ancestor masks.  anc[j] has bit i set iff node i is on
+// the root path of node j (j included).  Returns false for an invalid tree.
+// Called by every thread of the block; blockDim.x >= 64.
+// ---------------------------------------------------------------------------
+__device__ bool build_ancestors(const int32_t* par_b, int n, uint64_t* anc, int* flag) {
+  if (threadIdx.x == 0) *flag = 0;
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < n) {
+    uint64_t m = 1ull << t;
+    bool bad = (t == 0) ? (par_b[0] != -1) : false;
+    int j = t;
+    while (!bad && j > 0) {
+      const int p = par_b[j];
+      if (p < 0 || p >= j) {
+        bad = true;
+      } else {
+        m |= 1ull << p;
+        j = p;
+      }
+    }
+    anc[t] = m;
+    if (bad) atomicOr(flag, 1);
+  }
+  __syncthreads();
+  return *flag == 0;
+}
+
+// ---------------------------------------------------------------------------
+// Vector-ALU path: one wave per (b, node, query head).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(64) void attn_valu_kernel(
+    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+    const int32_t* __restrict__ prefix_len, const int32_t* __restrict__ n_nodes,
+    const int32_t* __restrict__ parents, int n_max, int Hq, int Hkv, int d, int L_cap,
+    float c, float* __restrict__ out, int32_t* dev_error) {
+  __shared__ uint64_t anc[64];
+  __shared__ int flag;
+  __shared__ int rows[64];
+  __shared__ float qs[128];
+  const int b = blockIdx.y;
+  const int i = blockIdx.x / Hq;
+  const int h = blockIdx.x % Hq;
+  const int lane = threadIdx.x;
+  const bool reporter = (blockIdx.x == 0 && lane == 0);
+  const int n = n_nodes[b];
+  const int L = prefix_len[b];
+  if (n < 1 || n > n_max) {
+    if (reporter) report(dev_error, SPEC_DEVERR_TREE);
+    return;
+  }
+  if (L < 0 || (int64_t)L + n > L_cap) {
+    if (reporter) report(dev_error, SPEC_DEVERR_CAPACITY);
+    return;
+  }
+  if (!build_ancestors(parents + (size_t)b * n_max, n, anc, &flag)) {
+    if (reporter) report(dev_error, SPEC_DEVERR_TREE);
+    return;
+  }
+  if (i >= n) return;
+
+  const uint64_t a = anc[i];
+  const bool mine = lane < n && ((a >> lane) & 1ull);
+  const uint64_t bal = __ballot(mine);
+  if (mine) rows[__popcll(bal & ((1ull << lane) - 1ull))] = L + lane;
+  const int npath = __popcll(bal);
+  const int g = h / (Hq / Hkv);
+  const T* qrow = q + (((size_t)b * n_max + i) * Hq + h) * d;
+  for (int k = lane; k < d; k += 64) qs[k] = load_as_f32(qrow + k);
+  __syncthreads();
+
+  const T* kb = kc + ((size_t)b * Hkv + g) * (size_t)L_cap * d;
+  const T* vb = vc + ((size_t)b * Hkv + g) * (size_t)L_cap * d;
+  const int total = L + npath;
+  float m = -INFINITY, l = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int c0 = 0; c0 < total; c0 += 64) {
+    const int t = c0 + lane;
+    const bool valid = t < total;
+    const int row = valid ? (t < L ? t : rows[t - L]) : 0;
+    float s = -INFINITY;
+    if (valid) {
+      const T* kr = kb + (size_t)row * d;
+      float dot = 0.f;
+      for (int k = 0; k < d; ++k) dot = fmaf(qs[k], load_as_f32(kr + k), dot);
+      s = dot * c;
+    }
+    const float mn = fmaxf(m, wave_max(s));
+    const float alpha = exp2f(m - mn);
+    const float p = valid ? exp2f(s - mn) : 0.f;
+    l = l * alpha + wave_sum(p);
+    acc0 *= alpha;
+    acc1 *= alpha;
+    const int cnt = min(64, total - c0);
+    for (int kk = 0; kk < cnt; ++kk) {
+      const float w = __shfl(p, kk);
+      const int r = __shfl(row, kk);
+      const T* vr = vb + (size_t)r * d;
+      if (lane < d) acc0 = fmaf(w, load_as_f32(vr + lane), acc0);
+      if (lane + 64 < d) acc1 = fmaf(w, load_as_f32(vr + lane + 64), acc1);
+    }
+    m = mn;
+  }
+  float* orow = out + (((size_t)b * n_max + i) * Hq + h) * d;
+  const float inv = 1.f / l;
+  if (lane < d) orow[lane] = acc0 * inv;
+  if (lane + 64 < d) orow[lane + 64] = acc1 * inv;
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core path (bf16, head_dim 128).
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int KT = 64;              // keys per tile
+constexpr int HD = 128;             // head dim
+constexpr int KS_STRIDE = HD + 8;   // K tile row stride in LDS (bf16 elements)
+constexpr int VT_STRIDE = KT + 8;   // transposed V tile row stride (bf16 elements)
+
+struct MfmaArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* prefix_len;
+  const int32_t* n_nodes;
+  const int32_t* parents;
+  int B, n_max, Hq, Hkv, G, L_cap;
+  int RB;      // row blocks per (b, g)
+  int S_max;   // prefix splits
+  int chunk;   // prefix keys per split (multiple of KT)
+  int units;   // B * Hkv * S_max
+  int sort;    // map units to sequences longest prefix first
+  float c;     // scale * log2(e)
+  float* out;
+  float* part_o;     // [B*Hkv][RB*RPW][S_max][HD]
+  float2* part_ml;   // [B*Hkv][RB*RPW][S_max]  (running max, running sum)
+  int32_t* dev_error;
+};
+
+// Position of key k (0..15) inside its 16-key group of a transposed V row:
+// bits 2 and 3 swapped, so that the 8 keys one lane half feeds to a 32x32x16
+// contraction step (keys 4h..4h+3 and 8+4h..8+4h+3) are contiguous.
+__device__ __forceinline__ int vt_pos(int k) {
+  return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+
+template <int NB, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
+  constexpr int NT = NW * 64;
+  constexpr int RPW = NW * NB * 32;            // query rows per workgroup
+  constexpr int CH = KT * HD / 8 / NT;         // 16-byte chunks per thread per tile (K or V)
+  constexpr int GPT = (KT / 4) * (HD / 8) / NT;  // V 4x8 transpose groups per thread
+  static_assert(CH == GPT * 4, "tile split");
+
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KS_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][HD * VT_STRIDE];
+  __shared__ uint64_t anc[64];
+  __shared__ int flag;
+  __shared__ int sorted_b;
+  __shared__ int lens[256];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 31;
+  const int lh = lane >> 5;
+
+  // Block index -> (unit, row block).  The row blocks of one unit land on the
+  // same XCD (same blockIdx mod 8) and are dispatched close together, so the
+  // second one reads the unit's K/V from that XCD's L2.
+  const int w = blockIdx.x;
+  const int rb = (w >> 3) % a.RB;
+  const int u = (w / (8 * a.RB)) * 8 + (w & 7);
+  if (u >= a.units) return;
+  const int s = u % a.S_max;
+  const int g = (u / a.S_max) % a.Hkv;
+  const int rank = u / (a.S_max * a.Hkv);
+  int b = rank;
+  if (a.sort) {
+    // rank-th longest prefix (ties: lower sequence id first)
+    for (int t = tid; t < a.B; t += NT) lens[t] = a.prefix_len[t];
+    __syncthreads();
+    for (int t = tid; t < a.B; t += NT) {
+      const int Lt = lens[t];
+      int r = 0;
+      for (int j = 0; j < a.B; ++j) {
+        const int Lj = lens[j];
+        r += (Lj > Lt) || (Lj == Lt && j < t);
+      }
+      if (r == rank) sorted_b = t;
+    }
+    __syncthreads();
+    b = sorted_b;
+  }
+
+  const int n = a.n_nodes[b];
+  const int L = a.prefix_len[b];
+  const bool reporter = (g == 0 && rb == 0 && s == 0 && tid == 0);
+  if (n < 1 || n > a.n_max) {
+    if (reporter) report(a.dev_error, SPEC_DEVERR_TREE);
+    return;
+  }
+  if (L < 0 || (int64_t)L + n > a.L_cap) {
+    if (reporter) report(a.dev_error, SPEC_DEVERR_CAPACITY);
+    return;
+  }
+  const int nsplit = L > 0 ? (L + a.chunk - 1) / a.chunk : 1;
+  if (s >= nsplit) return;
+  const int Mb = n * a.G;
+  if (rb * RPW >= Mb) return;
+  if (!build_ancestors(a.parents + (size_t)b * a.n_max, n, anc, &flag)) {
+    if (reporter) report(a.dev_error, SPEC_DEVERR_TREE);
+    return;
+  }
+  const bool last = (s == nsplit - 1);
+
+  // ---- Q fragments (B operand of S^T = K Q^T): lane holds query row lr of
+  // its 32-row block, head dims 16*ks + 8*lh .. +7.
+  bf16x8_t qf[NB][8];
+  uint64_t anc_r[NB];
+  int row_i[NB], row_h[NB];
+  bool rvalid[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int r = rb * RPW + (wave * NB + nb) * 32 + lr;
+    rvalid[nb] = r < Mb;
+    const int i = rvalid[nb] ? r / a.G : 0;
+    const int hh = rvalid[nb] ? r % a.G : 0;
+    row_i[nb] = i;
+    row_h[nb] = hh;
+    anc_r[nb] = rvalid[nb] ? anc[i] : 0ull;
+    const uint16_t* qp = a.q + (((size_t)b * a.n_max + i) * a.Hq + (size_t)g * a.G + hh) * HD + lh * 8;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (rvalid[nb]) {
+        qf[nb][ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 16);
+      } else {
+        qf[nb][ks] = bf16x8_t{};
+      }
+    }
+  }
+
+  f32x16_t o[NB][4];
+  float mrow[NB], lrow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    mrow[nb] = -INFINITY;
+    lrow[nb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[nb][db] = f32x16_t{};
+  }
+
+  const size_t bg = (size_t)b * a.Hkv + g;
+  const uint16_t* kbg = a.k + bg * (size_t)a.L_cap * HD;
+  const uint16_t* vbg = a.v + bg * (size_t)a.L_cap * HD;
+  const int kb0 = s * a.chunk;
+  const int ke0 = min(L, kb0 + a.chunk);
+  const int ntp = ke0 > kb0 ? (ke0 - kb0 + KT - 1) / KT : 0;
+  const int nt = ntp + (last ? 1 : 0);
+
+  uint4 kreg[CH], vreg[CH];
+  auto load_tile = [&](int t) {
+    const int row0 = t < ntp ? kb0 + t * KT : L;
+    const int nrows = t < ntp ? min(KT, ke0 - row0) : n;
+    const uint16_t* kbase = kbg + (size_t)row0 * HD;
+    const uint16_t* vbase = vbg + (size_t)row0 * HD;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int cidx = tid + j * NT;
+      const int r = cidx >> 4;
+      const int col = (cidx & 15) * 8;
+      kreg[j] = r < nrows ? *reinterpret_cast<const uint4*>(kbase + (size_t)r * HD + col)
+                          : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int gj = 0; gj < GPT; ++gj) {
+      const int gi = tid + gj * NT;
+      const int dc = gi & 15;
+      const int kq = gi >> 4;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int r = kq * 4 + kk;
+        vreg[gj * 4 + kk] = r < nrows ? *reinterpret_cast<const uint4*>(vbase + (size_t)r * HD + dc * 8)
+                                      : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    uint16_t* ks_ = Ks[buf];
+    uint16_t* vt_ = Vt[buf];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int cidx = tid + j * NT;
+      const int r = cidx >> 4;
+      const int col = (cidx & 15) * 8;
+      *reinterpret_cast<uint4*>(ks_ + r * KS_STRIDE + col) = kreg[j];
+    }
+#pragma unroll
+    for (int gj = 0; gj < GPT; ++gj) {
+      const int gi = tid + gj * NT;
+      const int dc = gi & 15;
+      const int kq = gi >> 4;
+      const int kpos = vt_pos(kq * 4);
+      const uint32_t* x0 = reinterpret_cast<const uint32_t*>(&vreg[gj * 4 + 0]);
+      const uint32_t* x1 = reinterpret_cast<const uint32_t*>(&vreg[gj * 4 + 1]);
+      const uint32_t* x2 = reinterpret_cast<const uint32_t*>(&vreg[gj * 4 + 2]);
+      const uint32_t* x3 = reinterpret_cast<const uint32_t*>(&vreg[gj * 4 + 3]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // x_k[e] holds dims (2e, 2e+1) of key k as (low, high) halves.
+        const uint2 lo = make_uint2((x0[e] & 0xffffu) | (x1[e] << 16), (x2[e] & 0xffffu) | (x3[e] << 16));
+        const uint2 hi = make_uint2((x0[e] >> 16) | (x1[e] & 0xffff0000u), (x2[e] >> 16) | (x3[e] & 0xffff0000u));
+        *reinterpret_cast<uint2*>(vt_ + (dc * 8 + 2 * e) * VT_STRIDE + kpos) = lo;
+        *reinterpret_cast<uint2*>(vt_ + (dc * 8 + 2 * e + 1) * VT_STRIDE + kpos) = hi;
+      }
+    }
+  };
+
+  const float cs = a.c;
+  if (nt > 0) {
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+  }
+  for (int t = 0; t < nt; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < nt) load_tile(t + 1);
+    const bool tree = (t >= ntp);
+    const int nrows = tree ? n : min(KT, ke0 - (kb0 + t * KT));
+
+    // S^T (keys x rows) for the two 32-key halves of the tile.
+    f32x16_t sacc[NB][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      sacc[nb][0] = f32x16_t{};
+      sacc[nb][1] = f32x16_t{};
+    }
+    const uint16_t* ks_ = Ks[buf];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(ks_ + (kb * 32 + lr) * KS_STRIDE + ks * 16 + lh * 8);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          sacc[nb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nb][ks], sacc[nb][kb], 0, 0, 0);
+      }
+    }
+
+    // Online softmax; lane (lr, lh) holds keys 8*gq + 4*lh + e4 of each half.
+    bf16x8_t pf[NB][2][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kb * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+          const bool vis = key < nrows && (!tree || ((anc_r[nb] >> key) & 1ull));
+          const float sv = vis ? sacc[nb][kb][e] : -INFINITY;
+          sacc[nb][kb][e] = sv;
+          mt = fmaxf(mt, sv);
+        }
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mn = fmaxf(mrow[nb], mt);
+      const float mu = (mn == -INFINITY) ? 0.f : mn;
+      const float muc = mu * cs;
+      const float alpha = exp2f(mrow[nb] * cs - muc);
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = exp2f(fmaf(sacc[nb][kb][e], cs, -muc));
+          ls += p;
+          pf[nb][kb][e >> 3][e & 7] = static_cast<__bf16>(p);
+        }
+      }
+      lrow[nb] = lrow[nb] * alpha + ls;
+      mrow[nb] = mn;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[nb][db] *= alpha;
+    }
+
+    // O^T (dims x rows) += V^T P^T.
+    const uint16_t* vt_ = Vt[buf];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vt_ + (db * 32 + lr) * VT_STRIDE + kb * 32 + hb * 16 + lh * 8);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            o[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb][kb][hb], o[nb][db], 0, 0, 0);
+        }
+      }
+    }
+
+    if (t + 1 < nt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds dims db*32 + 8*gq + 4*lh + e4 of its query row.
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const float lt = lrow[nb] + __shfl_xor(lrow[nb], 32);
+    if (!rvalid[nb]) continue;
+    const int r = rb * RPW + (wave * NB + nb) * 32 + lr;
+    if (a.S_max == 1) {
+      const float inv = 1.f / lt;
+      float* op = a.out + (((size_t)b * a.n_max + row_i[nb]) * a.Hq + (size_t)g * a.G + row_h[nb]) * HD;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+          *reinterpret_cast<float4*>(op + db * 32 + gq * 8 + lh * 4) =
+              make_float4(o[nb][db][gq * 4 + 0] * inv, o[nb][db][gq * 4 + 1] * inv,
+                          o[nb][db][gq * 4 + 2] * inv, o[nb][db][gq * 4 + 3] * inv);
+    } else {
+      const size_t prow = (bg * (size_t)(a.RB * RPW) + r) * a.S_max + s;
+      float* pp = a.part_o + prow * HD;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+          *reinterpret_cast<float4*>(pp + db * 32 + gq * 8 + lh * 4) =
+              make_float4(o[nb][db][gq * 4 + 0], o[nb][db][gq * 4 + 1], o[nb][db][gq * 4 + 2],
+                          o[nb][db][gq * 4 + 3]);
+      if (lh == 0) a.part_ml[prow] = make_float2(mrow[nb], lt);
+    }
+  }
+}
+
+// Log-sum-exp merge of prefix splits: one block (HD threads) per query row.
+__global__ __launch_bounds__(HD) void attn_merge_kernel(MfmaArgs a, int rows_per_bg) {
+  const int r = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int n = a.n_nodes[b];
+  const int L = a.prefix_len[b];
+  if (n < 1 || n > a.n_max || L < 0 || (int64_t)L + n > a.L_cap) return;
+  if (r >= n * a.G) return;
+  // an invalid tree was skipped by the main kernel; skip it here as well
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  if (threadIdx.x < n) {
+    const int p = a.parents[(size_t)b * a.n_max + threadIdx.x];
+    if (threadIdx.x == 0 ? p != -1 : (p < 0 || p >= (int)threadIdx.x)) atomicOr(&bad, 1);
+  }
+  __syncthreads();
+  if (bad) return;
+  const int nsplit = L > 0 ? (L + a.chunk - 1) / a.chunk : 1;
+  const size_t base = (((size_t)b * a.Hkv + g) * rows_per_bg + r) * a.S_max;
+  float mstar = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) mstar = fmaxf(mstar, a.part_ml[base + s].x);
+  float lsum = 0.f, acc = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float2 ml = a.part_ml[base + s];
+    const float wgt = exp2f((ml.x - mstar) * a.c);
+    lsum += ml.y * wgt;
+    acc += a.part_o[(base + s) * HD + threadIdx.x] * wgt;
+  }
+  const int i = r / a.G;
+  const int hh = r % a.G;
+  a.out[(((size_t)b * a.n_max + i) * a.Hq + (size_t)g * a.G + hh) * HD + threadIdx.x] = acc / lsum;
+}
+
+// ---------------------------------------------------------------------------
+// Host planning.
+// ---------------------------------------------------------------------------
+struct Plan {
+  bool mfma = false;
+  int nb = 0, nw = 0, rpw = 0, rb = 0, S_max = 1, chunk = 0, units = 0, sort = 0;
+  size_t ws = 0;
+};
+
+Plan make_plan(int B, int n_max, int Hq, int Hkv, int d, int L_cap, int dtype) {
+  Plan p;
+  p.mfma = (dtype == SPEC_BF16 && d == HD);
+  if (!p.mfma) return p;
+  const int G = Hq / Hkv;
+  const int M = n_max * G;
+  if (M <= 64) {
+    p.nb = 1; p.nw = 2;
+  } else if (M <= 128) {
+    p.nb = 1; p.nw = 4;
+  } else {
+    p.nb = 2; p.nw = 4;
+  }
+  p.rpw = p.nw * p.nb * 32;
+  p.rb = (M + p.rpw - 1) / p.rpw;
+  const long base = (long)B * Hkv * p.rb;
+  const long target = 2L * device_cu_count();
+  long S = base >= target ? 1 : (target + base - 1) / base;
+  const long smax_by_len = (L_cap + 127) / 128;
+  if (S > smax_by_len) S = smax_by_len;
+  if (S < 1) S = 1;
+  long chunk = (L_cap + S - 1) / S;
+  chunk = (chunk + KT - 1) / KT * KT;
+  p.chunk = (int)chunk;
+  p.S_max = (int)((L_cap + chunk - 1) / chunk);
+  p.units = B * Hkv * p.S_max;
+  p.sort = (p.S_max == 1 && B >= 8 && B <= 256) ? 1 : 0;
+  if (p.S_max > 1) {
+    const size_t rows = (size_t)B * Hkv * p.rb * p.rpw * p.S_max;
+    p.ws = rows * HD * sizeof(float) + rows * sizeof(float2) + 256;
+  }
+  return p;
+}
+
+spec_status_t check_args(const void* q, const void* k, const void* v, const int32_t* pl,
+                         const int32_t* nn, const int32_t* par, int B, int n_max, int Hq,
+                         int Hkv, int d, int L_cap, float scale, int dtype, const float* out) {
+  if (!q || !k || !v || !pl || !nn || !par || !out) return SPEC_E_NULL;
+  if (B <= 0 || n_max <= 0 || n_max > SPEC_MAX_NODES || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
+      L_cap < n_max)
+    return SPEC_E_SHAPE;
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_E_DTYPE;
+  if (d != 16 && d != 32 && d != 64 && d != 128) return SPEC_E_DTYPE;
+  if (!(scale > 0.f) || !isfinite(scale)) return SPEC_E_VALUE;
+  if ((long)B * n_max * Hq > (1L << 30) || (long)B * Hkv * L_cap > (1L << 31) / 1) return SPEC_E_SHAPE;
+  return SPEC_OK;
+}
+
+}  // namespace
+}  // namespace specv
+
+using namespace specv;
+
+extern "C" size_t spec_verify_tree_attn_workspace_size(int32_t B, int32_t n_max, int32_t Hq,
+                                                      int32_t Hkv, int32_t head_dim, int32_t L_cap,
+                                                      int32_t dtype) {
+  if (B <= 0 || n_max <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || L_cap <= 0) return 0;
+  return make_plan(B, n_max, Hq, Hkv, head_dim, L_cap, dtype).ws;
+}
+
+extern "C" spec_status_t spec_verify_tree_attn(
+    const void* q, const void* k_cache, const void* v_cache, const int32_t* prefix_len,
+    const int32_t* n_nodes, const int32_t* parents, int32_t B, int32_t n_max, int32_t Hq,
+    int32_t Hkv, int32_t head_dim, int32_t L_cap, float scale, int32_t dtype, float* out,
+    void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream) {
+  spec_status_t st = check_args(q, k_cache, v_cache, prefix_len, n_nodes, parents, B, n_max, Hq,
+                                Hkv, head_dim, L_cap, scale, dtype, out);
+  if (st != SPEC_OK) return st;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  const float c = scale * kLog2e;
+  const Plan p = make_plan(B, n_max, Hq, Hkv, head_dim, L_cap, dtype);
+  if (!p.mfma) {
+    dim3 grid(n_max * Hq, B);
+    if (dtype == SPEC_F32) {
+      hipLaunchKernelGGL(attn_valu_kernel<float>, grid, dim3(64), 0, strm,
+                         static_cast<const float*>(q), static_cast<const float*>(k_cache),
+                         static_cast<const float*>(v_cache), prefix_len, n_nodes, parents, n_max,
+                         Hq, Hkv, head_dim, L_cap, c, out, dev_error);
+    } else {
+      hipLaunchKernelGGL(attn_valu_kernel<uint16_t>, grid, dim3(64), 0, strm,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+                         static_cast<const uint16_t*>(v_cache), prefix_len, n_nodes, parents, n_max,
+                         Hq, Hkv, head_dim, L_cap, c, out, dev_error);
+    }
+    SPEC_HIP_TRY(hipGetLastError());
+    return SPEC_OK;
+  }
+  if (p.ws > 0 && (workspace == nullptr || workspace_bytes < p.ws)) return SPEC_E_WORKSPACE;
+
+  MfmaArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k_cache);
+  a.v = static_cast<const uint16_t*>(v_cache);
+  a.prefix_len = prefix_len;
+  a.n_nodes = n_nodes;
+  a.parents = parents;
+  a.B = B; a.n_max = n_max; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.L_cap = L_cap;
+  a.RB = p.rb; a.S_max = p.S_max; a.chunk = p.chunk; a.units = p.units; a.sort = p.sort;
+  a.c = c;
+  a.out = out;
+  a.dev_error = dev_error;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  if (p.S_max > 1) {
+    const size_t rows = (size_t)B * Hkv * p.rb * p.rpw * p.S_max;
+    char* ws = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_ml = reinterpret_cast<float2*>(ws + rows * HD * sizeof(float));
+  }
+  const unsigned grid = (unsigned)(((p.units + 7) / 8) * 8 * p.rb);
+  if (p.nb == 1 && p.nw == 2)
+    hipLaunchKernelGGL((attn_mfma_kernel<1, 2>), dim3(grid), dim3(128), 0, strm, a);
+  else if (p.nb == 1 && p.nw == 4)
+    hipLaunchKernelGGL((attn_mfma_kernel<1, 4>), dim3(grid), dim3(256), 0, strm, a);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<2, 4>), dim3(grid), dim3(256), 0, strm, a);
+  SPEC_HIP_TRY(hipGetLastError());
+  if (p.S_max > 1) {
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(p.rb * p.rpw, Hkv, B), dim3(HD), 0, strm, a,
+                       p.rb * p.rpw);
+    SPEC_HIP_TRY(hipGetLastError());
+  }
+  return SPEC_OK;
+}

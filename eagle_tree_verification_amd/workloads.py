@@ -260,7 +260,8 @@ def make_workload(cfg, *, T: Optional[float] = None, token_mode: Optional[str] =
                   head_dim: Optional[int] = None, kv_dtype: Optional[str] = None,
                   parents: Optional[Sequence[np.ndarray]] = None,
                   seed: Optional[int] = None, poison: bool = False,
-                  l_cap: Optional[int] = None) -> Workload:
+                  l_cap: Optional[int] = None,
+                  prefix_lens: Optional[Sequence[int]] = None) -> Workload:
     """Draw one workload from a named config with optional overrides.
 
     drafts: int, or a per-sequence list for ragged trees.
@@ -270,6 +271,7 @@ def make_workload(cfg, *, T: Optional[float] = None, token_mode: Optional[str] =
       Default: "topk" at T == 0, else "iid".
     poison: fill every element the path must never read (cache rows past the
       tree, logits/p/q rows past n_nodes) with NaN.
+    prefix_lens: explicit per-sequence prefix lengths (within `prefix`'s hi).
     """
     if isinstance(cfg, int):
         cfg = CONFIGS[cfg]
@@ -300,7 +302,10 @@ def make_workload(cfg, *, T: Optional[float] = None, token_mode: Optional[str] =
 
     # prefix lengths
     lo, hi = cfg.prefix
-    if lo == hi:
+    if prefix_lens is not None:
+        prefix_len = np.asarray(prefix_lens, dtype=np.int32)
+        assert prefix_len.shape == (B,) and prefix_len.max() <= hi
+    elif lo == hi:
         prefix_len = np.full(B, lo, dtype=np.int32)
     else:
         prefix_len = rngs[_S_PREFIX].integers(lo, hi, endpoint=True, size=B).astype(np.int32)
@@ -312,6 +317,8 @@ def make_workload(cfg, *, T: Optional[float] = None, token_mode: Optional[str] =
     for b in range(B):
         if parents is not None:
             pb = np.asarray(parents[b], dtype=np.int32)
+        elif drafts_b[b] == 0:
+            pb = np.array([-1], dtype=np.int32)
         elif cfg.chain:
             pb = chain_parents(int(drafts_b[b]))
         else:
@@ -412,4 +419,25 @@ def small_cases():
         "c3-mini-t1": dict(cfg=3, prefix=(517, 517), vocab=3001, T=1.0),
         "c4-mini": dict(cfg=4, batch=5, prefix=(1, 700), vocab=5003),
         "c5-mini": dict(cfg=5, batch=2, prefix=(190, 190), vocab=4099),
+    }
+
+
+def to_device(w: Workload, device="cuda"):
+    """Copy a workload's arrays into device tensors (dict keyed like the fields)."""
+    import torch
+
+    def kv(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if w.kv_dtype == "bf16":
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.to(device)
+
+    def plain(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    return {
+        "q": kv(w.q), "k_cache": kv(w.k_cache), "v_cache": kv(w.v_cache),
+        "prefix_len": plain(w.prefix_len), "n_nodes": plain(w.n_nodes),
+        "parents": plain(w.parents), "tokens": plain(w.tokens), "logits": plain(w.logits),
+        "draft_p": plain(w.draft_p), "u_accept": plain(w.u_accept), "u_sample": plain(w.u_sample),
     }

@@ -1,0 +1,212 @@
+/*
+ * spec_verify.h -- C ABI of the EAGLE-2/3 tree-verification library for
+ * AMD MI355X (gfx950).  ABI version 1.
+ *
+ * One verify step of speculative decoding with a draft tree is three calls,
+ * issued in this order on one HIP stream:
+ *
+ *   spec_verify_tree_attn  attention of every tree node over the committed
+ *                          prefix KV plus its own ancestors (tree mask);
+ *   spec_accept_tree       the Leviathan acceptance rule walked down the tree;
+ *   spec_kv_commit         gather the accepted path's KV rows behind the
+ *                          prefix and advance the logical length.
+ *
+ * Pages the operations follow (cited by title and section):
+ *   [LESSON] "推测解码与 EAGLE-3": section "不变量：Leviathan 拒绝采样"
+ *            (the rule and one pass returning N+1 distributions), section
+ *            "KV cache 回滚" (rollback; tree attention is one attention call
+ *            with a mask that follows the tree), build steps 1-4;
+ *   [GUIDE]  "EAGLE-1/2/3 拆解": section "一个可核对的经验性质" (a node is
+ *            accepted only if its whole root path is), section on EAGLE-2's
+ *            two stages (the tree mask starts as the identity);
+ *   [TTT]    "EAGLE-3 完全拆解": section on the training-time attention mask
+ *            (each token sees only its ancestors).
+ *
+ * Common conventions
+ *   - Every array pointer is a DEVICE pointer owned by the caller.  The
+ *     library keeps no pointer after the stream work completes, holds no
+ *     global mutable state and allocates no device memory; scratch space
+ *     comes from the caller's `workspace`, sized by the *_workspace_size
+ *     functions for the same arguments and the same current device.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  All work is
+ *     asynchronous on it; outputs are valid once the caller synchronises.
+ *   - A negative status is returned, before anything is launched, for any
+ *     problem the host can see (NULL pointers, sizes, dtype, scalars,
+ *     workspace size).  SPEC_E_HIP reports a failed launch.
+ *   - Problems only the device can see are OR-ed into *dev_error (a device
+ *     int32, may be NULL) as SPEC_DEVERR_* bits; the affected sequence is
+ *     skipped (attention output rows left untouched; accept_len = -1).  The
+ *     library never clears *dev_error; the caller zeroes it.
+ *   - Trees: node 0 of sequence b is the pending root (the token emitted by
+ *     the previous step, whose KV this verify pass produced); parents[b][0]
+ *     = -1 and 0 <= parents[b][j] < j for 1 <= j < n_nodes[b] (topological
+ *     ids).  Tree node j's K/V sit in cache row prefix_len[b] + j.
+ *   - Limits: n_max <= 64, head_dim in {16, 32, 64, 128}, Hq % Hkv == 0.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_ABI_VERSION 1
+#define SPEC_MAX_NODES 64
+
+typedef int32_t spec_status_t;
+
+enum {
+  SPEC_OK = 0,
+  SPEC_E_NULL = -1,        /* a required pointer is NULL                          */
+  SPEC_E_SHAPE = -2,       /* a size argument is out of range                     */
+  SPEC_E_DTYPE = -3,       /* unsupported dtype / head_dim combination            */
+  SPEC_E_VALUE = -4,       /* bad scalar (temperature < 0 or NaN, scale <= 0)     */
+  SPEC_E_WORKSPACE = -5,   /* workspace NULL or smaller than required             */
+  SPEC_E_HIP = -6,         /* a HIP runtime call or launch failed                 */
+  SPEC_E_UNSUPPORTED = -7  /* the current device cannot run this configuration    */
+};
+
+enum { SPEC_F32 = 0, SPEC_BF16 = 1 };
+
+enum {
+  SPEC_DEVERR_TREE = 1,       /* n_nodes outside [1, n_max], bad parents, depth > max_depth */
+  SPEC_DEVERR_TOKEN = 2,      /* a draft token outside [0, V)                              */
+  SPEC_DEVERR_NONFINITE = 4,  /* NaN/Inf in a logits or draft-probability entry read       */
+  SPEC_DEVERR_CAPACITY = 8,   /* prefix_len < 0 or prefix_len + n_nodes > L_cap            */
+  SPEC_DEVERR_SYNC = 16       /* an inter-workgroup wait hit its bound (walk abandoned)    */
+};
+
+/* One near-tie record of spec_accept_tree (kind 0: accept test, 1: sample). */
+typedef struct {
+  int32_t b;      /* sequence                                             */
+  int32_t node;   /* child tested (kind 0) or node sampled at (kind 1)    */
+  int32_t kind;
+  float u;        /* the uniform used                                     */
+  double margin;  /* |u - min(1, ratio)|, or distance of u*W to the chosen
+                     bucket's nearer edge divided by W                     */
+} spec_tie_t;
+
+/*
+ * spec_verify_tree_attn -- tree-masked attention ([LESSON] "KV cache 回滚";
+ * [GUIDE] identity initial tree mask; [TTT] ancestors-only mask).
+ *
+ * For every sequence b, tree node i < n_nodes[b] and query head h:
+ *   out[b][i][h] = softmax(scale * q[b][i][h] . K^T) V
+ * over the keys/values of KV head h / (Hq/Hkv) in cache rows
+ * [0, prefix_len[b]) (the committed prefix) and rows prefix_len[b] + j for
+ * every j on the root-to-i path, i included -- exactly the last row of causal
+ * attention over "prefix, then path(i)".
+ *
+ *   q          [B][n_max][Hq][head_dim], dtype; already position-encoded
+ *   k_cache,   [B][Hkv][L_cap][head_dim], dtype; the caller has written the
+ *   v_cache    tree's K/V into rows [prefix_len[b], prefix_len[b]+n_nodes[b])
+ *   prefix_len [B] int32, n_nodes [B] int32, parents [B][n_max] int32
+ *   scale      softmax scale (> 0; pass 1/sqrt(head_dim) for the usual one)
+ *   dtype      SPEC_BF16 (any head_dim; the 128 case uses matrix cores) or
+ *              SPEC_F32 (vector ALU only)
+ *   out        [B][n_max][Hq][head_dim] float32; rows i >= n_nodes[b] and
+ *              rows of failed sequences are not written
+ *   workspace  >= spec_verify_tree_attn_workspace_size(...) bytes
+ * Device errors: SPEC_DEVERR_TREE, SPEC_DEVERR_CAPACITY.
+ */
+spec_status_t spec_verify_tree_attn(
+    const void* q, const void* k_cache, const void* v_cache,
+    const int32_t* prefix_len, const int32_t* n_nodes, const int32_t* parents,
+    int32_t B, int32_t n_max, int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t L_cap,
+    float scale, int32_t dtype, float* out,
+    void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream);
+
+size_t spec_verify_tree_attn_workspace_size(
+    int32_t B, int32_t n_max, int32_t Hq, int32_t Hkv, int32_t head_dim, int32_t L_cap,
+    int32_t dtype);
+
+/*
+ * spec_accept_tree -- the acceptance walk ([LESSON] "不变量：Leviathan 拒绝
+ * 采样" and build steps 1-3; [GUIDE] prefix property of tree acceptance).
+ *
+ * q_v = softmax(logits[b][v] / temperature), in float64.  Starting at the
+ * root v = 0: the children c of v are tested in ascending id; child c (token
+ * x) is accepted if draft_p[b][v][x] <= 0, else iff
+ *   u_accept[b][c] < min(1, cur(x) / draft_p[b][v][x]),
+ * where cur starts as q_v and, after each rejected child, becomes the
+ * residual norm(max(0, cur - p_v)) (a zero-mass residual leaves cur as it
+ * is).  On acceptance the walk descends to c.  When no child is accepted
+ * (or v is a leaf) the terminal token is drawn from cur with u_sample[b][v]
+ * by inverse CDF in ascending token id (smallest i whose running sum exceeds
+ * u * total mass); at a leaf that is the bonus token from q_v.
+ * temperature == 0 is greedy: a child is accepted iff its token is the
+ * argmax of logits[b][v] (lowest id on ties), and the terminal token is that
+ * argmax.  All vocab-wide arithmetic is float64.
+ *
+ *   tokens, parents        [B][n_max] int32 (tokens[b][0], the root, unused)
+ *   n_nodes                [B] int32
+ *   draft_p, logits        [B][n_max][V] float32; row v of draft_p is the
+ *                          distribution v's children were drawn from; rows
+ *                          are read only for nodes the walk visits
+ *   max_depth              bound on tree depth; path/out_tokens hold
+ *                          max_depth + 1 entries per sequence
+ *   temperature            >= 0
+ *   u_accept, u_sample     [B][n_max] float32 uniforms in [0, 1)
+ *   accept_len  (out)      [B] int32: accepted drafts a (-1 on device error)
+ *   path        (out)      [B][max_depth+1] int32: root..deepest accepted
+ *                          node (a + 1 entries), then -1
+ *   out_tokens  (out)      [B][max_depth+1] int32: the a accepted tokens,
+ *                          then the terminal token, then -1
+ *   n_out       (out)      [B] int32: a + 1 (0 on device error)
+ *   final_dist  (out, nullable) [B][V] float32: normalised distribution the
+ *                          terminal token was drawn from (one-hot at T = 0)
+ *   tie_log     (out, nullable) up to tie_cap records of decisions with
+ *                          |u - min(1, ratio)| < 1e-6 and samples whose
+ *                          margin < 1e-9; *tie_count (device int32, required
+ *                          when tie_log is given) is reset by the call and
+ *                          counts all such events, logged or not
+ *   workspace              >= spec_accept_tree_workspace_size(...) bytes
+ * Device errors: SPEC_DEVERR_TREE, _TOKEN, _NONFINITE, _SYNC.
+ */
+spec_status_t spec_accept_tree(
+    const int32_t* tokens, const int32_t* parents, const int32_t* n_nodes,
+    const float* draft_p, const float* logits,
+    int32_t B, int32_t n_max, int32_t V, int32_t max_depth, float temperature,
+    const float* u_accept, const float* u_sample,
+    int32_t* accept_len, int32_t* path, int32_t* out_tokens, int32_t* n_out,
+    float* final_dist, spec_tie_t* tie_log, int32_t tie_cap, int32_t* tie_count,
+    void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream);
+
+size_t spec_accept_tree_workspace_size(int32_t B, int32_t n_max, int32_t V);
+
+/*
+ * spec_kv_commit -- commit the accepted path ([LESSON] "KV cache 回滚" and
+ * build step 4).  For every sequence with accept_len[b] = a >= 0 and every
+ * KV head: cache row prefix_len[b] + i receives the pre-commit row
+ * prefix_len[b] + path[b][i] for i = 0..a (K and V), then prefix_len[b]
+ * becomes prefix_len[b] + a + 1 (the root and the a accepted drafts; the
+ * terminal token is the next step's root).  A path equal to 0..a moves no
+ * bytes (logical truncation).  Sequences with accept_len < 0 are untouched.
+ * Not idempotent: call exactly once per step, after spec_accept_tree.
+ *
+ *   k_cache, v_cache [B][Hkv][L_cap][head_dim], dtype (in/out)
+ *   prefix_len       [B] int32 (in/out)
+ *   path, accept_len as written by spec_accept_tree with the same max_depth
+ * Device errors: SPEC_DEVERR_TREE (path not increasing / out of range),
+ * SPEC_DEVERR_CAPACITY.
+ */
+spec_status_t spec_kv_commit(
+    void* k_cache, void* v_cache, int32_t* prefix_len,
+    const int32_t* path, const int32_t* accept_len,
+    int32_t B, int32_t Hkv, int32_t head_dim, int32_t L_cap, int32_t max_depth,
+    int32_t dtype, int32_t* dev_error, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* spec_status_string(spec_status_t status);
+
+/* SPEC_ABI_VERSION of the loaded library. */
+int32_t spec_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,80 @@
+"""The C-ABI library loads, exports every function include/spec_verify.h
+declares, and rejects bad arguments on the host before touching a device
+(no kernel is launched by these tests)."""
+import ctypes
+
+import pytest
+
+from eagle_tree_verification_amd import api
+
+SPEC_E_NULL, SPEC_E_SHAPE, SPEC_E_DTYPE, SPEC_E_VALUE = -1, -2, -3, -4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return api.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = api.declared_functions()
+    assert set(names) == {"spec_verify_tree_attn", "spec_verify_tree_attn_workspace_size",
+                          "spec_accept_tree", "spec_accept_tree_workspace_size", "spec_kv_commit",
+                          "spec_status_string", "spec_abi_version"}
+    for nm in names:
+        assert hasattr(lib, nm), nm
+
+
+def test_version_and_status_strings(lib):
+    assert lib.spec_abi_version() == 1
+    for s in range(-7, 1):
+        assert len(lib.spec_status_string(s)) > 0
+    assert lib.spec_status_string(-99) == b"unknown status"
+
+
+def _buf():
+    return ctypes.cast(ctypes.create_string_buffer(64), ctypes.c_void_p)
+
+
+def test_attention_host_checks(lib):
+    P = _buf()
+    f = lib.spec_verify_tree_attn
+    args = [P] * 6 + [1, 6, 4, 4, 16, 64, 0.25, 0, P, None, 0, None, None]
+    assert f(*([None] + args[1:])) == SPEC_E_NULL
+    bad = list(args); bad[7] = 65          # n_max > 64
+    assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[8], bad[9] = 6, 4  # Hq % Hkv != 0
+    assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[10] = 48         # head_dim
+    assert f(*bad) == SPEC_E_DTYPE
+    bad = list(args); bad[13] = 7          # dtype
+    assert f(*bad) == SPEC_E_DTYPE
+    bad = list(args); bad[12] = -1.0       # scale
+    assert f(*bad) == SPEC_E_VALUE
+
+
+def test_accept_host_checks(lib):
+    P = _buf()
+    f = lib.spec_accept_tree
+    args = [P] * 5 + [2, 6, 100, 5, 1.0, P, P, P, P, P, P, None, None, 0, None, P, 1 << 20, None, None]
+    assert f(*([None] + args[1:])) == SPEC_E_NULL
+    bad = list(args); bad[6] = 65
+    assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[9] = -0.5
+    assert f(*bad) == SPEC_E_VALUE
+    bad = list(args); bad[9] = float("nan")
+    assert f(*bad) == SPEC_E_VALUE
+    bad = list(args); bad[17] = P          # tie_log without tie_count
+    assert f(*bad) == SPEC_E_NULL
+
+
+def test_commit_host_checks(lib):
+    P = _buf()
+    f = lib.spec_kv_commit
+    args = [P] * 5 + [2, 4, 16, 64, 5, 0, None, None]
+    assert f(*([None] + args[1:])) == SPEC_E_NULL
+    bad = list(args); bad[9] = 64          # max_depth
+    assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[8] = 0           # L_cap
+    assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[10] = 3          # dtype
+    assert f(*bad) == SPEC_E_DTYPE

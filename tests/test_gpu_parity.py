@@ -1,0 +1,133 @@
+"""GPU parity of the three C-ABI calls against the oracle on reduced configs.
+
+Each case keeps its config's head layout, head dim, dtype and tree budget but
+shrinks the prefix and vocabulary so the oracle finishes in seconds; all still
+span several 64-key tiles with a ragged tail.  Inputs are poisoned with NaN
+everywhere the path must not read.  Bars: attention within 1e-5 (f32) /
+2e-2 (bf16) absolute; accepted lengths, paths, emitted tokens and committed KV
+bit-exact except sequence-steps with a logged near tie; residual
+distributions within 1e-5 absolute.
+"""
+import numpy as np
+import pytest
+import torch
+
+from eagle_tree_verification_amd.workloads import make_workload, small_cases, to_device
+from gpu_helpers import (compare_accept, compare_attention, compare_commit, kv_host, run_gpu_step,
+                         say)
+
+pytestmark = pytest.mark.gpu
+
+CASES = small_cases()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_step_parity(hip_lib, name):
+    w = make_workload(poison=True, **CASES[name])
+    say(f"[gpu] step parity {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} "
+        f"L={w.prefix_len.tolist()} n={w.n_nodes.tolist()} V={w.V} T={w.T}")
+    dev = to_device(w)
+    host = run_gpu_step(w, dev)
+    assert host["dev_error"] == 0
+    worst = compare_attention(w, host["attn"])
+    excluded = compare_accept(w, host)
+    say(f"[gpu]   attention max|diff|={worst:.3g}; near-tie sequences excluded: {excluded}")
+    assert len(excluded) <= max(1, w.B // 4)
+    compare_commit(w, host, kv_host(dev["k_cache"], w.kv_dtype), kv_host(dev["v_cache"], w.kv_dtype),
+                   dev["prefix_len"].cpu().numpy())
+
+
+@pytest.mark.parametrize("T", [0.0, 0.7, 1.0, 2.5])
+def test_ragged_trees_and_temperatures(hip_lib, T):
+    # ragged n_nodes (including a single-root tree), empty and tiny prefixes
+    w = make_workload(4, batch=6, prefix=(0, 150), vocab=2053, drafts=[60, 1, 0, 17, 33, 8],
+                      T=T, poison=True, seed=77, prefix_lens=[0, 1, 63, 64, 150, 97])
+    say(f"[gpu] ragged T={T} L={w.prefix_len.tolist()} n={w.n_nodes.tolist()}")
+    dev = to_device(w)
+    host = run_gpu_step(w, dev)
+    assert host["dev_error"] == 0
+    compare_attention(w, host["attn"])
+    compare_accept(w, host)
+    compare_commit(w, host, kv_host(dev["k_cache"], w.kv_dtype), kv_host(dev["v_cache"], w.kv_dtype),
+                   dev["prefix_len"].cpu().numpy())
+
+
+@pytest.mark.parametrize("hq,hkv,d,dt", [(4, 4, 16, "f32"), (8, 2, 64, "bf16"), (6, 3, 32, "f32"),
+                                         (16, 16, 128, "f32"), (12, 4, 128, "bf16")])
+def test_attention_layouts(hip_lib, hq, hkv, d, dt):
+    w = make_workload(4, batch=3, prefix=(70, 200), vocab=64, hq=hq, hkv=hkv, head_dim=d,
+                      kv_dtype=dt, poison=True, seed=hq * 100 + d)
+    say(f"[gpu] attention layout hq={hq} hkv={hkv} d={d} {dt}")
+    dev = to_device(w)
+    host = run_gpu_step(w, dev, commit=False)
+    compare_attention(w, host["attn"])
+
+
+def test_device_errors_are_reported(hip_lib):
+    w = make_workload(4, batch=4, prefix=(20, 40), vocab=500, poison=False, seed=5)
+    w.parents[0, 5] = 7          # parent after child: bad tree
+    w.tokens[1, 3] = w.V         # token out of range
+    w.logits[2, 0, 10] = np.nan  # the root row is always read
+    w.prefix_len[3] = w.L_cap - 2  # tree does not fit
+    say("[gpu] device error bits")
+    dev = to_device(w)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.full((w.B, w.n_max, w.Hq, w.d), -7.0, device="cuda")
+    from eagle_tree_verification_amd import api
+    api.verify_tree_attn(dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"],
+                         dev["n_nodes"], dev["parents"], out=out, dev_error=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == api.DEVERR_TREE | api.DEVERR_CAPACITY
+    assert torch.all(out[0] == -7.0) and torch.all(out[3] == -7.0)
+    err.zero_()
+    acc = api.accept_tree(dev["tokens"], dev["parents"], dev["n_nodes"], dev["draft_p"],
+                          dev["logits"], 1.0, dev["u_accept"], dev["u_sample"], w.max_depth,
+                          dev_error=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == api.DEVERR_TREE | api.DEVERR_TOKEN | api.DEVERR_NONFINITE
+    al = acc["accept_len"].cpu().numpy()
+    assert list(al[:3]) == [-1, -1, -1] and al[3] >= 0
+    assert np.all(acc["path"][:3].cpu().numpy() == -1)
+    # the commit skips failed sequences; the fourth one overflows the cache
+    before = dev["prefix_len"].clone()
+    err.zero_()
+    api.kv_commit(dev["k_cache"], dev["v_cache"], dev["prefix_len"], acc["path"], acc["accept_len"],
+                  w.max_depth, dev_error=err)
+    torch.cuda.synchronize()
+    after = dev["prefix_len"].cpu().numpy()
+    assert np.all(after[:3] == before[:3].cpu().numpy())
+
+
+def test_host_errors_are_returned(hip_lib):
+    from eagle_tree_verification_amd import api
+    w = make_workload(1, T=1.0)
+    dev = to_device(w)
+    with pytest.raises(api.SpecError) as e:
+        api.accept_tree(dev["tokens"], dev["parents"], dev["n_nodes"], dev["draft_p"], dev["logits"],
+                        -1.0, dev["u_accept"], dev["u_sample"], w.max_depth)
+    assert e.value.status == -4
+    with pytest.raises(api.SpecError) as e:
+        api.verify_tree_attn(dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"],
+                             dev["n_nodes"], dev["parents"], scale=0.0)
+    assert e.value.status == -4
+
+
+def test_commit_in_place_hazard(hip_lib):
+    # path [0, 2, 5]: row 2 is read for slot 1 and overwritten by slot 2
+    from eagle_tree_verification_amd import api
+    B, Hkv, L_cap, d, L = 2, 3, 64, 128, 9
+    rng = np.random.default_rng(0)
+    k = torch.from_numpy(rng.standard_normal((B, Hkv, L_cap, d), dtype=np.float32)).cuda()
+    v = torch.from_numpy(rng.standard_normal((B, Hkv, L_cap, d), dtype=np.float32)).cuda()
+    k0, v0 = k.clone(), v.clone()
+    plen = torch.tensor([L, L], dtype=torch.int32, device="cuda")
+    path = torch.tensor([[0, 2, 5, -1], [0, 1, 2, 3]], dtype=torch.int32, device="cuda")
+    alen = torch.tensor([2, 3], dtype=torch.int32, device="cuda")
+    say("[gpu] commit hazard")
+    api.kv_commit(k, v, plen, path, alen, 3)
+    torch.cuda.synchronize()
+    for src, dst in ((0, 0), (2, 1), (5, 2)):
+        assert torch.equal(k[0, :, L + dst], k0[0, :, L + src])
+        assert torch.equal(v[0, :, L + dst], v0[0, :, L + src])
+    assert torch.equal(k[1], k0[1]) and torch.equal(v[1], v0[1])
+    assert plen.cpu().tolist() == [L + 3, L + 4]
