@@ -26,6 +26,8 @@ Conventions (shared with the C ABI):
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import Optional, Sequence
 
@@ -75,8 +77,9 @@ CONFIGS = {
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even); return the bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    # finite values cannot wrap in uint32 (largest: 0xFF7FFFFF + 0x8000); NaNs are patched below
+    r = ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         r[nan] = 0x7FC0
@@ -261,7 +264,8 @@ def make_workload(cfg, *, T: Optional[float] = None, token_mode: Optional[str] =
                   parents: Optional[Sequence[np.ndarray]] = None,
                   seed: Optional[int] = None, poison: bool = False,
                   l_cap: Optional[int] = None,
-                  prefix_lens: Optional[Sequence[int]] = None) -> Workload:
+                  prefix_lens: Optional[Sequence[int]] = None,
+                  threads: Optional[int] = None) -> Workload:
     """Draw one workload from a named config with optional overrides.
 
     drafts: int, or a per-sequence list for ragged trees.
@@ -298,7 +302,8 @@ def make_workload(cfg, *, T: Optional[float] = None, token_mode: Optional[str] =
     n_max = int(drafts_b.max()) + 1
 
     ss = np.random.SeedSequence(cfg.seed)
-    rngs = [np.random.Generator(np.random.Philox(s)) for s in ss.spawn(9)]
+    subs = ss.spawn(9)
+    rngs = [np.random.Generator(np.random.Philox(s)) for s in subs]
 
     # prefix lengths
     lo, hi = cfg.prefix
@@ -328,29 +333,20 @@ def make_workload(cfg, *, T: Optional[float] = None, token_mode: Optional[str] =
     max_depth = int(max(node_depths(par[b, : n_nodes[b]]).max() for b in range(B)))
     max_depth = max(max_depth, 1)
 
-    # Q / K / V
+    # per-sequence data, each sequence from its own child streams
     d, Hq, Hkv = cfg.head_dim, cfg.hq, cfg.hkv
     dt = cfg.kv_dtype
-    r = rngs[_S_QKV]
     fill = np.float32(np.nan) if poison else np.float32(0.0)
-    q32 = r.standard_normal(size=(B, n_max, Hq, d), dtype=np.float32)
-    for b in range(B):
-        q32[b, n_nodes[b]:] = fill
-    q = _to_storage(q32, dt)
-    del q32
+    fill_st = _to_storage(np.array([fill], np.float32), dt)[0]
     sdt = np.uint16 if dt == "bf16" else np.float32
+    q = np.empty((B, n_max, Hq, d), dtype=sdt)
     k_cache = np.empty((B, Hkv, L_cap, d), dtype=sdt)
     v_cache = np.empty((B, Hkv, L_cap, d), dtype=sdt)
-    fill_st = _to_storage(np.array([fill], np.float32), dt)[0]
-    for b in range(B):
-        rows = int(prefix_len[b] + n_nodes[b])
-        for cache in (k_cache, v_cache):
-            cache[b, :, :rows] = _to_storage(
-                r.standard_normal(size=(Hkv, rows, d), dtype=np.float32), dt)
-            cache[b, :, rows:] = fill_st
+    logits = np.empty((B, n_max, V), dtype=np.float32)
+    draft_p = np.empty((B, n_max, V), dtype=np.float32)
+    tokens = np.full((B, n_max), -1, dtype=np.int32)
 
-    # verifier logits and draft distributions
-    rl, rn = rngs[_S_LOGITS], rngs[_S_NOISE]
+    rn = rngs[_S_NOISE]
     if cfg.alpha is not None:
         a_lo, a_hi = cfg.alpha
         alpha_t = (np.full(B, a_lo) if a_lo == a_hi else rn.uniform(a_lo, a_hi, size=B))
@@ -360,25 +356,32 @@ def make_workload(cfg, *, T: Optional[float] = None, token_mode: Optional[str] =
     else:
         alpha_t = np.full(B, np.nan)
         noise = np.full(B, cfg.noise_std)
-    logits = np.empty((B, n_max, V), dtype=np.float32)
-    draft_p = np.empty((B, n_max, V), dtype=np.float32)
-    for b in range(B):
-        nb = int(n_nodes[b])
-        lb = rl.normal(0.0, cfg.logit_std, size=(nb, V)).astype(np.float32)
-        eps = rn.standard_normal(size=(nb, V), dtype=np.float32)
-        logits[b, :nb] = lb
-        draft_p[b, :nb] = _softmax_rows64(lb.astype(np.float64) + noise[b] * eps).astype(np.float32)
-        if nb < n_max:
-            logits[b, nb:] = fill
-            draft_p[b, nb:] = fill
+    root_tok = rngs[_S_TOKENS].integers(V, size=B)
+    kids_ss = [subs[_S].spawn(B) for _S in (_S_QKV, _S_LOGITS, _S_NOISE, _S_TOKENS)]
 
-    # draft tokens
-    rt = rngs[_S_TOKENS]
-    tokens = np.full((B, n_max), -1, dtype=np.int32)
-    for b in range(B):
+    def one(b):
+        rq, rl, rn_b, rt = (np.random.Generator(np.random.Philox(k[b])) for k in kids_ss)
         nb = int(n_nodes[b])
+        rows = int(prefix_len[b] + nb)
+        qb = np.full((n_max, Hq, d), fill, dtype=np.float32)
+        qb[:nb] = rq.standard_normal(size=(nb, Hq, d), dtype=np.float32)
+        q[b] = _to_storage(qb, dt)
+        for cache in (k_cache, v_cache):
+            cache[b, :, :rows] = _to_storage(
+                rq.standard_normal(size=(Hkv, rows, d), dtype=np.float32), dt)
+            cache[b, :, rows:] = fill_st
+        lb = rl.standard_normal(size=(nb, V), dtype=np.float32) * np.float32(cfg.logit_std)
+        eps = rn_b.standard_normal(size=(nb, V), dtype=np.float32)
+        x = lb + np.float32(noise[b]) * eps
+        x -= x.max(axis=-1, keepdims=True)
+        np.exp(x, out=x)
+        x /= x.sum(axis=-1, keepdims=True, dtype=np.float64).astype(np.float32)
+        logits[b, :nb] = lb
+        draft_p[b, :nb] = x
+        logits[b, nb:] = fill
+        draft_p[b, nb:] = fill
         pb = par[b, :nb]
-        tokens[b, 0] = rt.integers(V)
+        tokens[b, 0] = root_tok[b]
         for v in range(nb):
             kids = np.nonzero(pb == v)[0]
             if len(kids) == 0:
@@ -393,6 +396,14 @@ def make_workload(cfg, *, T: Optional[float] = None, token_mode: Optional[str] =
                 tokens[b, kids] = np.minimum(np.searchsorted(cdf, u, side="right"), V - 1)
             else:
                 raise ValueError(token_mode)
+
+    workers = max(1, min(B, threads or len(os.sched_getaffinity(0)), 16))
+    if workers == 1:
+        for b in range(B):
+            one(b)
+    else:
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(one, range(B)))
 
     u_accept = rngs[_S_UACC].random(size=(B, n_max), dtype=np.float32)
     u_sample = rngs[_S_USAMP].random(size=(B, n_max), dtype=np.float32)
