@@ -1,0 +1,282 @@
+"""Benchmark of one verify step on one MI355X.
+
+A step is the whole hot path over one batch: spec_verify_tree_attn (one
+layer), spec_accept_tree and spec_kv_commit, back to back on one stream, with
+every input resident in HBM.  Between steps the committed lengths are restored
+from a pristine copy (outside the timed events) so every step does the same
+work; the commit's row moves leave tree K/V rows permuted, which changes
+values but not the amount of work.
+
+Prints one JSON line.  `value` is verified tree tokens per second (draft nodes
+per step / mean step time); committed tokens per second are reported beside
+it.  `roofline` covers the attention kernel, the dominant one, with
+algorithmic bytes (what the method must move) over its mean event-timed
+duration.  `cpu_baseline` times the oracle on a bounded sample of the same
+workload on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--config 4] [--gpus 1]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+PROFILE_PMC = os.path.join(ROOT, "profiles", "attention_pmc.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def node_depths(parents, n):
+    d = np.zeros(n, np.int64)
+    for j in range(1, n):
+        d[j] = d[parents[j]] + 1
+    return d
+
+
+def attention_cost(w):
+    """Algorithmic HBM bytes and flops of one tree-attention launch."""
+    s = 2 if w.kv_dtype == "bf16" else 4
+    n = w.n_nodes.astype(np.int64)
+    L = w.prefix_len.astype(np.int64)
+    bytes_ = (L.sum() * w.Hkv * w.d * 2 * s          # prefix K and V
+              + n.sum() * w.Hkv * w.d * 2 * s        # tree K and V
+              + n.sum() * w.Hq * w.d * s             # Q
+              + n.sum() * w.Hq * w.d * 4             # fp32 output
+              + 4 * n.sum() + 8 * w.B)               # parents, lengths
+    keys = 0
+    for b in range(w.B):
+        keys += (L[b] * n[b] + (node_depths(w.parents[b], int(n[b])) + 1).sum())
+    flops = 4 * w.d * w.Hq * keys
+    return int(bytes_), int(flops)
+
+
+def accept_bytes(w, accept_len, path):
+    """Algorithmic bytes of the acceptance walk: one logits row per visited
+    node, one draft row per visited node with a rejected child, tokens,
+    parents and uniforms, outputs."""
+    total = 0
+    for b in range(w.B):
+        a = int(accept_len[b])
+        pb = w.parents[b, : w.n_nodes[b]]
+        total += (a + 1) * w.V * 4
+        if w.T > 0:
+            for i in range(a + 1):
+                v = int(path[b, i])
+                kids = np.nonzero(pb == v)[0]
+                if i < a:
+                    rejected = (kids < int(path[b, i + 1])).sum()
+                else:
+                    rejected = len(kids)
+                if rejected:
+                    total += w.V * 4
+        total += 16 * int(w.n_nodes[b]) + 8 * (w.max_depth + 1) + 8
+    return total
+
+
+def commit_bytes(w, accept_len, path):
+    s = 2 if w.kv_dtype == "bf16" else 4
+    total = 0
+    for b in range(w.B):
+        a = int(accept_len[b])
+        if a > 0 and any(int(path[b, i]) != i for i in range(a + 1)):
+            total += 2 * a * w.Hkv * w.d * 2 * s
+        total += 8 + 4 * (a + 1)
+    return total
+
+
+def pmc_traffic(per_launch_algo):
+    """HBM bytes per attention launch from the committed counter summary, if
+    it was taken on the current attention source."""
+    if not os.path.exists(PROFILE_PMC):
+        return None
+    with open(PROFILE_PMC) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "eagle_tree_verification_amd", "csrc", "attention.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("attention_source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The oracle (as it stands) on a bounded sample of sequences of the same
+    workload: attention of every node and head, the walk and the commit."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    t0 = time.perf_counter()
+    drafts = 0
+    done = 0
+    with threadpool_limits(limits=cores):
+        for b in range(w.B):
+            n = int(w.n_nodes[b])
+            k, v = w.kv_f64(b)
+            oracle.tree_attention(w.q_f64(b), k, v, int(w.prefix_len[b]), w.parents[b, :n],
+                                  scale=w.scale)
+            r = oracle.accept_tree(w.tokens[b], w.parents[b], n, w.draft_p[b], w.logits[b], w.T,
+                                   w.u_accept[b], w.u_sample[b], w.max_depth, n_max=w.n_max)
+            oracle.kv_commit(w.k_cache[b], w.v_cache[b], int(w.prefix_len[b]), r.path,
+                             r.accept_len)
+            drafts += n - 1
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": drafts / dt, "unit": "verified tree tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"first {done} of {w.B} sequences of the same workload (all nodes and heads "
+                      f"of tree attention in float64, the acceptance walk and the commit), "
+                      f"{dt:.1f} s on {cores} host threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="run one plain device copy of this size first (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the verify path is per-sequence independent and would shard by sequence "
+              "with no exchange).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from eagle_tree_verification_amd import api
+    from eagle_tree_verification_amd.workloads import CONFIGS, make_workload, to_device
+
+    api.load()
+    cfg = CONFIGS[args.config]
+    t_gen = time.perf_counter()
+    w = make_workload(args.config)
+    log(f"[bench] generated {cfg.name} in {time.perf_counter() - t_gen:.1f} s")
+    dev = to_device(w)
+    torch.cuda.synchronize()
+    if args.copy_probe_mb:
+        a = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device="cuda")
+        b_ = torch.empty_like(a)
+        b_.copy_(a)
+        torch.cuda.synchronize()
+        del a, b_
+
+    kv_dt = api.SPEC_BF16 if w.kv_dtype == "bf16" else api.SPEC_F32
+    ws_attn = torch.empty(max(1, api.verify_tree_attn_workspace_size(
+        w.B, w.n_max, w.Hq, w.Hkv, w.d, w.L_cap, kv_dt)), dtype=torch.uint8, device="cuda")
+    ws_acc = torch.empty(api.accept_tree_workspace_size(w.B, w.n_max, w.V), dtype=torch.uint8,
+                         device="cuda")
+    out = torch.empty((w.B, w.n_max, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    outs = {"accept_len": torch.empty(w.B, dtype=torch.int32, device="cuda"),
+            "path": torch.empty((w.B, w.max_depth + 1), dtype=torch.int32, device="cuda"),
+            "out_tokens": torch.empty((w.B, w.max_depth + 1), dtype=torch.int32, device="cuda"),
+            "n_out": torch.empty(w.B, dtype=torch.int32, device="cuda")}
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    plen0 = dev["prefix_len"].clone()
+
+    def step(ev=None):
+        dev["prefix_len"].copy_(plen0)
+        if ev:
+            ev[0].record()
+        api.verify_tree_attn(dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"],
+                             dev["n_nodes"], dev["parents"], out=out, workspace=ws_attn,
+                             dev_error=err)
+        if ev:
+            ev[1].record()
+        api.accept_tree(dev["tokens"], dev["parents"], dev["n_nodes"], dev["draft_p"],
+                        dev["logits"], w.T, dev["u_accept"], dev["u_sample"], w.max_depth,
+                        workspace=ws_acc, dev_error=err, outputs=outs)
+        if ev:
+            ev[2].record()
+        api.kv_commit(dev["k_cache"], dev["v_cache"], dev["prefix_len"], outs["path"],
+                      outs["accept_len"], w.max_depth, dev_error=err)
+        if ev:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if int(err.item()) != 0:
+        raise RuntimeError(f"device error bits {int(err.item())}")
+
+    t_attn = np.array([e[0].elapsed_time(e[1]) for e in events])
+    t_acc = np.array([e[1].elapsed_time(e[2]) for e in events])
+    t_com = np.array([e[2].elapsed_time(e[3]) for e in events])
+    t_step = np.array([e[0].elapsed_time(e[3]) for e in events])
+    ms = float(t_step.mean())
+    accept_len = outs["accept_len"].cpu().numpy()
+    path = outs["path"].cpu().numpy()
+    verified = w.verified_tokens
+    committed = int((accept_len + 1).sum())
+    a_bytes, a_flops = attention_cost(w)
+    acc_b = accept_bytes(w, accept_len, path)
+    com_b = commit_bytes(w, accept_len, path)
+    attn_ms = float(t_attn.mean())
+    achieved = a_bytes / (attn_ms * 1e-3) / 1e9
+    intensity = a_flops / a_bytes
+    ridge = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    traffic = pmc_traffic(a_bytes)
+    roof = {"bound": "hbm" if intensity < ridge else "mfma",
+            "kernel": "attn_mfma_kernel" if (w.kv_dtype == "bf16" and w.d == 128) else "attn_valu_kernel",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": a_bytes, "flops_per_launch": a_flops,
+            "mean_launch_ms": round(attn_ms, 4),
+            "mfma_tflops": round(a_flops / (attn_ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(a_flops / (attn_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)}
+    if roof["bound"] == "mfma":
+        roof.update({"achieved": roof["mfma_tflops"], "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": roof["mfma_frac"]})
+    rec = {
+        "metric": "verified tree tokens/s + committed tokens/s at 1 GPU; % peak HBM GB/s",
+        "value": round(verified / (ms * 1e-3), 1),
+        "unit": "verified tree tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: batch {w.B}, {w.Hq} q / {w.Hkv} kv heads, head_dim "
+                               f"{w.d}, {w.kv_dtype} KV, prefix {cfg.prefix[0]}-{cfg.prefix[1]}, "
+                               f"{cfg.drafts}-draft depth-{cfg.depth} trees, vocab {w.V}, T={w.T}",
+                   "global_batch": w.B, "prefix_mean": float(w.prefix_len.mean()),
+                   "tree_drafts": cfg.drafts, "tree_depth": cfg.depth, "vocab": w.V,
+                   "temperature": w.T, "parallelism": "single GPU"},
+        "committed_tokens_per_s": round(committed / (ms * 1e-3), 1),
+        "tokens_per_step": {"verified": verified, "committed": committed},
+        "kernels_ms": {"verify_tree_attn": round(attn_ms, 4), "accept_tree": round(float(t_acc.mean()), 4),
+                       "kv_commit": round(float(t_com.mean()), 4)},
+        "step_algorithmic_GBps": round((a_bytes + acc_b + com_b) / (ms * 1e-3) / 1e9, 1),
+        "accept_algorithmic_GBps": round(acc_b / (t_acc.mean() * 1e-3) / 1e9, 1),
+        "ms_per_step_wall_incl_length_restore": round(wall / args.steps * 1e3, 4),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

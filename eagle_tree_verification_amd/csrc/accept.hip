@@ -12,21 +12,27 @@
 // (all drawn from p_v) are tested in ascending id against the running
 // residual: after k rejections the distribution being tested is
 // max(0, q - C_k p) / Z_k with C_0 = 0, Z_0 = 1, C_{k+1} = C_k + Z_k and
-// Z_{k+1} = sum(max(0, q - C_{k+1} p)), so each rejection costs one vocab pass
-// and no row is materialised.  Temperature 0 is greedy decoding (accept iff
-// the token is the verifier's argmax; emit the argmax).
+// Z_{k+1} = sum(max(0, q - C_{k+1} p)), so no row is materialised.
+// Temperature 0 is greedy decoding (accept iff the token is the verifier's
+// argmax; emit the argmax).
 //
-// Shape on the GPU.  The walk is serial along the tree but each step is a
-// vocab-wide reduction over 32k-128k entries, so every sequence gets KP
-// workgroups, each owning a contiguous slice of the vocabulary.  They run
-// the same control flow and meet at a per-sequence barrier (one atomic
-// counter) after every pass, exchanging one or two float64 partials; the
-// combined values are formed in slice order, so every workgroup takes the
-// same decisions.  KP > 1 uses a cooperative launch so that all workgroups
-// are resident; every wait is bounded.  All vocab arithmetic is float64: the
-// verifier row is read once per visited node (max and sum of exp), once more
-// per rejected child (residual mass), and the terminal sample reads the final
-// row again (slice masses, then one workgroup scans its slice).
+// Shape on the GPU.  The walk is serial along the tree but every step is a
+// reduction over the 32k-128k vocabulary, so a sequence gets KP workgroups,
+// each owning a slice of NT * W * NG entries (thread t reads W consecutive
+// entries of each of its NG groups, groups NT * W entries apart, so loads are
+// coalesced 16-byte vectors).  The workgroups run the same control flow and
+// meet at a per-sequence barrier (one atomic counter) after every pass,
+// exchanging two float64 partials; partials are combined in slice order, so
+// every workgroup takes the same decisions.  A visited node costs one pass
+// (max and sum of exp, online per batch); a rejected child one pass of
+// max(0, exp(z - M) - C S p); the terminal token needs no extra pass: the
+// slice masses of the current residual are already known, and only the
+// workgroup whose slice holds the threshold scans it in order.  All vocab
+// arithmetic is float64 (z = logit / T); exp runs on the vector ALU with a
+// Cody-Waite argument reduction and a degree-13 Taylor polynomial (arguments
+// are never positive here), within one ulp.  KP > 1 is a cooperative launch
+// (all workgroups resident); a batch too large to be resident at once is
+// walked in consecutive groups.  Every inter-workgroup wait is bounded.
 #include <math.h>
 #include <stdlib.h>
 
@@ -40,6 +46,57 @@ constexpr double kTieBand = 1e-6;
 constexpr double kSampleBand = 1e-9;
 constexpr double kDegenerate = 1e-12;
 
+// exp(y) for y <= 0 in float64: y = n ln2 + r with |r| <= ln2 / 2 (ln2 split
+// in two parts so n * ln2_hi is exact), exp(r) by its Taylor series to degree
+// 13 (truncation below 5e-18 relative), then scaled by 2^n.  Underflows to 0.
+__device__ __forceinline__ double exp_nonpos(double y) {
+  constexpr double kLog2e = 1.4426950408889634;
+  constexpr double kLn2Hi = 6.93147180369123816490e-01;
+  constexpr double kLn2Lo = 1.90821492927058770002e-10;
+  const double n = rint(y * kLog2e);
+  double r = fma(-n, kLn2Hi, y);
+  r = fma(-n, kLn2Lo, r);
+  double p = 1.0 / 6227020800.0;             // 1/13!
+  p = fma(p, r, 1.0 / 479001600.0);          // 1/12!
+  p = fma(p, r, 1.0 / 39916800.0);
+  p = fma(p, r, 1.0 / 3628800.0);
+  p = fma(p, r, 1.0 / 362880.0);
+  p = fma(p, r, 1.0 / 40320.0);
+  p = fma(p, r, 1.0 / 5040.0);
+  p = fma(p, r, 1.0 / 720.0);
+  p = fma(p, r, 1.0 / 120.0);
+  p = fma(p, r, 1.0 / 24.0);
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  const double v = ldexp(p, (int)n);
+  return y < -745.5 ? 0.0 : v;
+}
+
+// exp(y) for y <= 0 (or -inf) in float64, for the per-entry passes: y =
+// (64 q + j) ln2 / 64 + r with |r| <= ln2 / 128, exp(r) by its Taylor series to
+// degree 5 (truncation below 4e-17 relative), times tab[j] = 2^(j/64) and 2^q.
+// Within two ulp; no branch, so it can run on every lane of a slice pass.
+__device__ __forceinline__ double exp_tab(double y, const double* tab) {
+  constexpr double kInvLn2x64 = 92.33248261689366;  // 64 / ln2
+  constexpr double kLn2Hi64 = 6.93147180369123816490e-01 / 64;
+  constexpr double kLn2Lo64 = 1.90821492927058770002e-10 / 64;
+  const double yc = fmax(y, -746.0);
+  const double n = rint(yc * kInvLn2x64);
+  double r = fma(-n, kLn2Hi64, yc);
+  r = fma(-n, kLn2Lo64, r);
+  double p = 1.0 / 120.0;
+  p = fma(p, r, 1.0 / 24.0);
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  const int ni = (int)n;
+  const double v = ldexp(tab[ni & 63] * p, ni >> 6);
+  return y < -745.5 ? 0.0 : v;
+}
+
 struct AcceptArgs {
   const int32_t* tokens;
   const int32_t* parents;
@@ -47,7 +104,7 @@ struct AcceptArgs {
   const float* draft_p;
   const float* logits;
   int B, n_max, V, max_depth, greedy;
-  double T;
+  double inv_T;
   const float* u_accept;
   const float* u_sample;
   int32_t* accept_len;
@@ -58,10 +115,11 @@ struct AcceptArgs {
   spec_tie_t* tie_log;
   int tie_cap;
   int32_t* tie_count;
+  int b0;       // first sequence of this launch
   int KP;       // workgroups per sequence
-  int chunk;    // vocabulary entries per workgroup
-  int* bar;     // [B] arrival counters (zeroed before the launch)
-  double* part; // [B][KP][2 slots][2]
+  int chunk;    // vocabulary entries per workgroup (NT * W * NG)
+  int* bar;     // [group size] arrival counters (zeroed before the launch)
+  double* part; // [group size][KP][2 slots][2]
   int32_t* dev_error;
   int spin_limit;
 };
@@ -80,6 +138,19 @@ __device__ double block_sum(double v, double* red) {
   return t;
 }
 
+__device__ float block_max(float v, double* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  const int wv = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wv] = (double)v;
+  __syncthreads();
+  float t = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) t = fmaxf(t, (float)red[k]);
+  return t;
+}
+
 __device__ __forceinline__ void lse_combine(double& m, double& s, double m2, double s2) {
   if (m2 == -INFINITY) return;
   if (m == -INFINITY) {
@@ -88,10 +159,10 @@ __device__ __forceinline__ void lse_combine(double& m, double& s, double m2, dou
     return;
   }
   if (m2 > m) {
-    s = s * exp(m - m2) + s2;
+    s = s * exp_nonpos(m - m2) + s2;
     m = m2;
   } else {
-    s += s2 * exp(m2 - m);
+    s += s2 * exp_nonpos(m2 - m);
   }
 }
 
@@ -116,7 +187,7 @@ __device__ void block_lse(double& m, double& s, double* red) {
   s = ss;
 }
 
-// argmax with lowest index on ties; NaN-free inputs (NaN is flagged separately)
+// argmax with lowest index on ties; NaN never wins (flagged separately)
 __device__ __forceinline__ void amax_combine(float& v, int& i, float v2, int i2) {
   if (v2 > v || (v2 == v && i2 < i)) {
     v = v2;
@@ -158,7 +229,7 @@ __device__ int block_or(int f, int* s_or) {
 // ---- inter-workgroup exchange ---------------------------------------------
 // Publishes this workgroup's two partials, waits until all KP workgroups of
 // the sequence have published theirs, and loads every partial into xs.
-__device__ bool exchange(const AcceptArgs& a, int b, int part, int& gen, double v0, double v1,
+__device__ bool exchange(const AcceptArgs& a, int bl, int part, int& gen, double v0, double v1,
                          double (*xs)[2], int* s_ok) {
   if (a.KP == 1) {
     __syncthreads();
@@ -173,14 +244,20 @@ __device__ bool exchange(const AcceptArgs& a, int b, int part, int& gen, double 
   ++gen;
   __syncthreads();
   if (threadIdx.x == 0) {
-    double* dst = a.part + (((size_t)b * a.KP + part) * 2 + slot) * 2;
+    // Everything the workgroups share here (partials, arrival counter) is
+    // read and written with device-coherent atomic accesses, so no cache-wide
+    // release/acquire fence is needed (on this chip those write back and
+    // invalidate the whole L2, which every later pass would pay for).  The
+    // partial stores only have to complete before the arrival is counted.
+    double* dst = a.part + (((size_t)bl * a.KP + part) * 2 + slot) * 2;
     __hip_atomic_store(dst, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(dst + 1, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_add(a.bar + b, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // all outstanding memory operations done
+    __hip_atomic_fetch_add(a.bar + bl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int target = gen * a.KP;
     int ok = 1, spins = 0;
-    while (__hip_atomic_load(a.bar + b, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(2);
+    while (__hip_atomic_load(a.bar + bl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(1);
       if (++spins > a.spin_limit) {
         ok = 0;
         break;
@@ -191,7 +268,7 @@ __device__ bool exchange(const AcceptArgs& a, int b, int part, int& gen, double 
   __syncthreads();
   if (!*s_ok) return false;
   if ((int)threadIdx.x < a.KP) {
-    const double* src = a.part + (((size_t)b * a.KP + threadIdx.x) * 2 + slot) * 2;
+    const double* src = a.part + (((size_t)bl * a.KP + threadIdx.x) * 2 + slot) * 2;
     xs[threadIdx.x][0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     xs[threadIdx.x][1] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -236,36 +313,84 @@ __device__ void write_outputs(const AcceptArgs& a, int b, int depth, const int* 
   }
 }
 
-// Load one element group of the slice: 4 entries with VEC, else 1.
-template <bool VEC>
-__device__ __forceinline__ int load_group(const float* row, int i, int hi, float* x) {
-  if (VEC) {
-    const float4 f = *reinterpret_cast<const float4*>(row + i);
-    x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
-    return 4;
-  }
-  x[0] = row[i];
-  return 1;
+// Element k of a thread's slice share: group k / W (NT * W entries apart),
+// entry k % W within the thread's W consecutive entries of that group.
+template <int W>
+__device__ __forceinline__ int elem_index(int lo, int k) {
+  return lo + ((k / W) * NT + (int)threadIdx.x) * W + (k % W);
 }
 
-template <bool VEC>
+// Loads group g (W consecutive entries) of this thread's share of a row
+// slice; entries past `hi` read as `fill`.
+template <int W>
+__device__ __forceinline__ void load_group(const float* row, int lo, int hi, int g, float fill, float* x) {
+  const int i = elem_index<W>(lo, g * W);
+  if (W == 4) {
+    if (i < hi) {
+      const float4 f = *reinterpret_cast<const float4*>(row + i);
+      x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
+    } else {
+      x[0] = x[1] = x[2] = x[3] = fill;
+    }
+  } else {
+    x[0] = i < hi ? row[i] : fill;
+  }
+}
+
+template <int W, int BG>
+__device__ __forceinline__ void load_batch(const float* row, int lo, int hi, int g0, float fill,
+                                           float (*xv)[W]) {
+#pragma unroll
+  for (int gb = 0; gb < BG; ++gb) load_group<W>(row, lo, hi, g0 + gb, fill, xv[gb]);
+}
+
+// Streams this thread's NG groups of a row slice (two rows when R2) through
+// `body(g0, x, y)`, BG groups at a time, with the next batch's loads issued
+// before the current batch is processed.  Groups past the slice read as fill
+// and touch no memory.
+template <int NG, int W, int BG, bool R2, typename F>
+__device__ __forceinline__ void stream_slice(const float* r1, float f1, const float* r2, float f2,
+                                             int lo, int hi, F body) {
+  float xa[BG][W], xb[BG][W], ya[BG][W], yb[BG][W];
+  load_batch<W, BG>(r1, lo, hi, 0, f1, xa);
+  if (R2) load_batch<W, BG>(r2, lo, hi, 0, f2, ya);
+#pragma unroll 1
+  for (int g0 = 0; g0 < NG; g0 += 2 * BG) {
+    load_batch<W, BG>(r1, lo, hi, g0 + BG, f1, xb);
+    if (R2) load_batch<W, BG>(r2, lo, hi, g0 + BG, f2, yb);
+    body(g0, xa, ya);
+    if (g0 + BG >= NG) break;
+    load_batch<W, BG>(r1, lo, hi, g0 + 2 * BG, f1, xa);
+    if (R2) load_batch<W, BG>(r2, lo, hi, g0 + 2 * BG, f2, ya);
+    body(g0 + BG, xb, yb);
+  }
+}
+
+template <int NG, int W>
 __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
-  constexpr int W = VEC ? 4 : 1;
+  constexpr int BG = NG < 2 ? NG : 2;  // groups loaded together
   __shared__ int s_par[SPEC_MAX_NODES];
   __shared__ int s_tok[SPEC_MAX_NODES];
   __shared__ int s_path[SPEC_MAX_NODES + 1];
   __shared__ int s_out[SPEC_MAX_NODES + 1];
   __shared__ double red[2 * (NT / 64)];
   __shared__ double xs[SPEC_MAX_NODES][2];
-  __shared__ double scan[NT];
-  __shared__ int s_ok, s_or, s_hit;
+  __shared__ double cur_sums[SPEC_MAX_NODES];
+  __shared__ double scan[NG][NT];
+  __shared__ double gtot[NG];
+  __shared__ int s_ok, s_or, s_hit, s_gsel, s_tsel;
+  __shared__ double s_before;
+  __shared__ double s_tab[64];
 
-  const int b = blockIdx.x / a.KP;
+  const int bl = blockIdx.x / a.KP;   // sequence within this launch's group
+  const int b = a.b0 + bl;
   const int part = blockIdx.x % a.KP;
   const int tid = threadIdx.x;
   const int lo = part * a.chunk;
   const int hi = min(a.V, lo + a.chunk);
   const bool writer0 = (part == 0);
+
+  if (tid < 64) s_tab[tid] = 2.0 * exp_nonpos((double)(tid - 64) / 64.0 * 0.6931471805599453);
 
   // ---- validation (identical in every workgroup of the sequence) ----------
   const int n = a.n_nodes[b];
@@ -291,7 +416,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       int dep = 0, j = tid;
       while (j > 0 && dep <= a.max_depth) {
         const int p = s_par[j];
-        if (p < 0 || p >= j) break;  // reported above by thread j
+        if (p < 0 || p >= j) break;  // reported by thread j
         j = p;
         ++dep;
       }
@@ -308,7 +433,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   int gen = 0;
   int v = 0, depth = 0;
   if (tid == 0) s_path[0] = 0;
-  const double T = a.T;
+  const double invT = a.inv_T;
   const size_t rows_b = (size_t)b * a.n_max;
 
   for (;;) {
@@ -318,27 +443,30 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
     if (a.greedy) {
       float bv = -INFINITY;
       int bi = 0x7fffffff, nf = 0;
-      for (int i = lo + tid * W; i < hi; i += NT * W) {
-        float x[4];
-        const int cnt = load_group<VEC>(lrow, i, hi, x);
-        for (int k = 0; k < cnt; ++k) {
-          if (!isfinite(x[k])) nf = 1;
-          amax_combine(bv, bi, x[k], i + k);
-        }
-      }
+      stream_slice<NG, W, BG, false>(lrow, -INFINITY, lrow, 0.f, lo, hi,
+          [&](int g0, float (*xv)[W], float (*)[W]) {
+#pragma unroll
+            for (int gb = 0; gb < BG; ++gb)
+#pragma unroll
+              for (int j = 0; j < W; ++j) {
+                const int i = elem_index<W>(lo, (g0 + gb) * W + j);
+                if (i < hi) {
+                  nf |= !isfinite(xv[gb][j]);
+                  amax_combine(bv, bi, xv[gb][j], i);
+                }
+              }
+          });
       nf = block_or(nf, &s_or);
       block_argmax(bv, bi, red);
-      if (!exchange(a, b, part, gen, (double)bv, (double)bi + (nf ? 0.5 : 0.0), xs, &s_ok)) {
+      if (!exchange(a, bl, part, gen, (double)bv, nf ? -1.0 : (double)bi, xs, &s_ok)) {
         if (writer0) write_failure(a, b, SPEC_DEVERR_SYNC);
         return;
       }
       float gv = -INFINITY;
       int gi = 0x7fffffff, gnf = 0;
       for (int k = 0; k < a.KP; ++k) {
-        const double enc = xs[k][1];
-        const int ik = (int)enc;
-        if (enc != (double)ik) gnf = 1;
-        amax_combine(gv, gi, (float)xs[k][0], ik);
+        if (xs[k][1] < 0.0) gnf = 1;
+        amax_combine(gv, gi, (float)xs[k][0], (int)xs[k][1]);
       }
       if (gnf) {
         if (writer0) write_failure(a, b, SPEC_DEVERR_NONFINITE);
@@ -367,26 +495,34 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       return;
     }
 
-    // ---- T > 0: max and sum of exp of the verifier row (float64) ----------
-    double m = -INFINITY, ssum = 0.0;
+    // ---- T > 0: max and sum of exp(z) over the slice, online per batch ----
+    double m = -INFINITY, es = 0.0;
     int nf = 0;
-    for (int i = lo + tid * W; i < hi; i += NT * W) {
-      float x[4];
-      const int cnt = load_group<VEC>(lrow, i, hi, x);
-      for (int k = 0; k < cnt; ++k) {
-        if (!isfinite(x[k])) nf = 1;
-        const double z = (double)x[k] / T;
-        if (z > m) {
-          ssum = ssum * exp(m - z) + 1.0;
-          m = z;
-        } else {
-          ssum += exp(z - m);
-        }
-      }
-    }
+    stream_slice<NG, W, BG, false>(lrow, -INFINITY, lrow, 0.f, lo, hi,
+        [&](int g0, float (*xv)[W], float (*)[W]) {
+          float bmax = -INFINITY;
+#pragma unroll
+          for (int gb = 0; gb < BG; ++gb)
+#pragma unroll
+            for (int j = 0; j < W; ++j) {
+              const bool valid = elem_index<W>(lo, (g0 + gb) * W + j) < hi;
+              nf |= valid && !isfinite(xv[gb][j]);
+              bmax = fmaxf(bmax, xv[gb][j]);
+            }
+          if (bmax == -INFINITY) return;  // nothing valid in this batch
+          const double zb = (double)bmax * invT;
+          if (zb > m) {
+            es *= exp_tab(m - zb, s_tab);  // m = -inf: es is still 0
+            m = zb;
+          }
+#pragma unroll
+          for (int gb = 0; gb < BG; ++gb)
+#pragma unroll
+            for (int j = 0; j < W; ++j) es += exp_tab(fma((double)xv[gb][j], invT, -m), s_tab);
+        });
     nf = block_or(nf, &s_or);
-    block_lse(m, ssum, red);
-    if (!exchange(a, b, part, gen, m, nf ? -1.0 : ssum, xs, &s_ok)) {
+    block_lse(m, es, red);
+    if (!exchange(a, bl, part, gen, m, nf ? -1.0 : es, xs, &s_ok)) {
       if (writer0) write_failure(a, b, SPEC_DEVERR_SYNC);
       return;
     }
@@ -400,14 +536,35 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       if (writer0) write_failure(a, b, SPEC_DEVERR_NONFINITE);
       return;
     }
+    // slice masses of q (in units of S) for the sample when no child is rejected
+    if (tid < a.KP) cur_sums[tid] = xs[tid][1] * exp_nonpos(xs[tid][0] - M);
+    __syncthreads();
+
+    // r = max(0, exp(z - M) - CS p) for one group of W entries
+    auto r_group = [&](int g, double CS, bool use_p, double* rv, int* pnf) {
+      float xv[W], pv[W];
+      load_group<W>(lrow, lo, hi, g, -INFINITY, xv);
+      if (use_p) {
+        load_group<W>(prow, lo, hi, g, 0.f, pv);
+      } else {
+#pragma unroll
+        for (int j = 0; j < W; ++j) pv[j] = 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        *pnf |= !isfinite(pv[j]);
+        const double e = exp_tab(fma((double)xv[j], invT, -M), s_tab);
+        rv[j] = fmax(0.0, e - CS * (double)pv[j]);
+      }
+    };
 
     // ---- children in ascending id against the running residual ------------
     double C = 0.0, Z = 1.0;
     int nxt = -1;
-    for (int c = v + 1; c < n && nxt < 0; ++c) {
+    for (int c = v + 1; c < n; ++c) {
       if (s_par[c] != v) continue;
-      const int x = s_tok[c];
-      const float pxf = prow[x];
+      const int xt = s_tok[c];
+      const float pxf = prow[xt];
       if (!isfinite(pxf)) {
         if (writer0) write_failure(a, b, SPEC_DEVERR_NONFINITE);
         return;
@@ -417,7 +574,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
         nxt = c;
         break;
       }
-      const double qx = exp((double)lrow[x] / T - M) / S;
+      const double qx = exp_nonpos((double)lrow[xt] * invT - M) / S;
       const double cur = fmax(0.0, qx - C * px) / Z;
       const double thr = fmin(1.0, cur / px);
       const float uf = a.u_accept[rows_b + c];
@@ -427,40 +584,45 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
         nxt = c;
         break;
       }
-      // rejected: residual mass for the next coefficient
+      // rejected: residual mass for the next coefficient, in units of S
       const double Cn = C + Z;
       double zp = 0.0;
       int pnf = 0;
-      for (int i = lo + tid * W; i < hi; i += NT * W) {
-        float xl[4], xp[4];
-        const int cnt = load_group<VEC>(lrow, i, hi, xl);
-        load_group<VEC>(prow, i, hi, xp);
-        for (int k = 0; k < cnt; ++k) {
-          if (!isfinite(xp[k])) pnf = 1;
-          const double q = exp((double)xl[k] / T - M) / S;
-          zp += fmax(0.0, q - Cn * (double)xp[k]);
-        }
-      }
+      const double CnS = Cn * S;
+      stream_slice<NG, W, BG, true>(lrow, -INFINITY, prow, 0.f, lo, hi,
+          [&](int, float (*xv)[W], float (*pv)[W]) {
+#pragma unroll
+            for (int gb = 0; gb < BG; ++gb)
+#pragma unroll
+              for (int j = 0; j < W; ++j) {
+                pnf |= !isfinite(pv[gb][j]);
+                const double e = exp_tab(fma((double)xv[gb][j], invT, -M), s_tab);
+                zp += fmax(0.0, e - CnS * (double)pv[gb][j]);
+              }
+          });
       pnf = block_or(pnf, &s_or);
       zp = block_sum(zp, red);
-      if (!exchange(a, b, part, gen, zp, (double)pnf, xs, &s_ok)) {
+      if (!exchange(a, bl, part, gen, zp, (double)pnf, xs, &s_ok)) {
         if (writer0) write_failure(a, b, SPEC_DEVERR_SYNC);
         return;
       }
-      double Zn = 0.0;
+      double Zs = 0.0;
       int gp = 0;
       for (int k = 0; k < a.KP; ++k) {
-        Zn += xs[k][0];
+        Zs += xs[k][0];
         gp |= (xs[k][1] != 0.0);
       }
       if (gp) {
         if (writer0) write_failure(a, b, SPEC_DEVERR_NONFINITE);
         return;
       }
+      const double Zn = Zs / S;
       if (Zn > 0.0) {
         if (writer0 && tid == 0 && Zn < kDegenerate * Z) log_tie(a, b, c, 2, uf, Zn / Z);
         C = Cn;
         Z = Zn;
+        if (tid < a.KP) cur_sums[tid] = xs[tid][0];
+        __syncthreads();
       }
     }
     if (nxt >= 0) {
@@ -474,108 +636,117 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       continue;
     }
 
-    // ---- terminal token: inverse CDF over r = max(0, q - C p) ------------
+    // ---- terminal token: inverse CDF over r (slice masses in cur_sums) ----
     const bool use_p = (C != 0.0);
-    double wp = 0.0;
-    for (int i = lo + tid * W; i < hi; i += NT * W) {
-      float xl[4], xp[4] = {0.f, 0.f, 0.f, 0.f};
-      const int cnt = load_group<VEC>(lrow, i, hi, xl);
-      if (use_p) load_group<VEC>(prow, i, hi, xp);
-      for (int k = 0; k < cnt; ++k) {
-        const double q = exp((double)xl[k] / T - M) / S;
-        wp += fmax(0.0, q - C * (double)xp[k]);
-      }
-    }
-    wp = block_sum(wp, red);
-    if (!exchange(a, b, part, gen, wp, 0.0, xs, &s_ok)) {
-      if (writer0) write_failure(a, b, SPEC_DEVERR_SYNC);
-      return;
-    }
+    const double CS = C * S;
     double Wt = 0.0;
-    for (int k = 0; k < a.KP; ++k) Wt += xs[k][0];
+    for (int k = 0; k < a.KP; ++k) Wt += cur_sums[k];
     const float usf = a.u_sample[rows_b + v];
     const double thr = (double)usf * Wt;
-    // the slice holding the threshold (running sum in slice order)
     int sel = -1, last_pos = -1;
     double off = 0.0, off_sel = 0.0;
     for (int k = 0; k < a.KP; ++k) {
-      if (xs[k][0] > 0.0) last_pos = k;
-      if (sel < 0 && off + xs[k][0] > thr) {
+      if (cur_sums[k] > 0.0) last_pos = k;
+      if (sel < 0 && off + cur_sums[k] > thr) {
         sel = k;
         off_sel = off;
       }
-      off += xs[k][0];
+      off += cur_sums[k];
     }
     if (sel < 0) {
       sel = last_pos;
-      off_sel = off - xs[last_pos][0];
+      off_sel = off - cur_sums[last_pos];
     }
+    int dummy = 0;
     if (a.final_dist) {
       float* fd = a.final_dist + (size_t)b * a.V;
-      for (int i = lo + tid; i < hi; i += NT) {
-        const double q = exp((double)lrow[i] / T - M) / S;
-        fd[i] = (float)(fmax(0.0, q - C * (use_p ? (double)prow[i] : 0.0)) / Wt);
+#pragma unroll 1
+      for (int g = 0; g < NG; ++g) {
+        double rv[W];
+        r_group(g, CS, use_p, rv, &dummy);
+#pragma unroll
+        for (int j = 0; j < W; ++j) {
+          const int i = elem_index<W>(lo, g * W + j);
+          if (i < hi) fd[i] = (float)(rv[j] / Wt);
+        }
       }
     }
     if (part != sel) return;
 
-    // scan of this slice: each thread sums a contiguous run, then the thread
-    // whose run holds the threshold walks it element by element, comparing
-    // run-local sums so that the walk repeats the run total's rounding.
-    const int len = hi - lo;
-    const int per = (len + NT - 1) / NT;
-    const int r0 = min(hi, lo + tid * per);
-    const int r1 = min(hi, r0 + per);
-    double tsum = 0.0;
-    for (int i = r0; i < r1; ++i) {
-      const double q = exp((double)lrow[i] / T - M) / S;
-      tsum += fmax(0.0, q - C * (use_p ? (double)prow[i] : 0.0));
+    // ordered scan of this slice: groups of NT * W entries, then threads,
+    // then the W entries of one thread
+#pragma unroll 1
+    for (int g = 0; g < NG; ++g) {
+      double rv[W];
+      r_group(g, CS, use_p, rv, &dummy);
+      double t = 0.0;
+#pragma unroll
+      for (int j = 0; j < W; ++j) t += rv[j];
+      scan[g][tid] = t;
     }
-    scan[tid] = tsum;
+    __syncthreads();
+    if (tid < NG) {
+      double t = 0.0;
+      for (int k = 0; k < NT; ++k) t += scan[tid][k];
+      gtot[tid] = t;
+    }
     __syncthreads();
     if (tid == 0) {
       double run = off_sel;
-      for (int k = 0; k < NT; ++k) {
-        const double t = scan[k];
-        scan[k] = run;  // exclusive prefix in slice order
-        run += t;
-      }
-      s_hit = 0x7fffffff;
-    }
-    __syncthreads();
-    const double target = thr - scan[tid];
-    double margin = 0.0;
-    int tok = -1;
-    if (r0 < r1 && target >= 0.0 && target < tsum) {
-      double run = 0.0;
-      for (int i = r0; i < r1; ++i) {
-        const double q = exp((double)lrow[i] / T - M) / S;
-        const double r = fmax(0.0, q - C * (use_p ? (double)prow[i] : 0.0));
-        if (run + r > target) {
-          tok = i;
-          margin = fmin(target - run, run + r - target) / Wt;
-          break;
+      int gs = -1, ts = -1;
+      for (int g = 0; g < NG && gs < 0; ++g) {
+        if (run + gtot[g] > thr) {
+          gs = g;
+          for (int k = 0; k < NT; ++k) {
+            if (run + scan[g][k] > thr) {
+              ts = k;
+              break;
+            }
+            run += scan[g][k];
+          }
+        } else {
+          run += gtot[g];
         }
-        run += r;
       }
-      if (tok >= 0) atomicMin(&s_hit, tok);
+      s_gsel = gs;
+      s_tsel = ts;
+      s_before = run;
+      s_hit = -1;
     }
     __syncthreads();
-    if (s_hit == 0x7fffffff) {
+    double margin = 0.0;
+    if (tid == s_tsel && s_gsel >= 0) {
+      const int g = s_gsel;
+      double rv[W];
+      r_group(g, CS, use_p, rv, &dummy);
+      double run = s_before;
+      int tok = -1;
+#pragma unroll
+      for (int j = 0; j < W; ++j) {
+        if (tok < 0 && run + rv[j] > thr) {
+          tok = elem_index<W>(lo, g * W + j);
+          margin = fmin(thr - run, run + rv[j] - thr) / Wt;
+        }
+        run += rv[j];
+      }
+      if (tok >= 0) s_hit = tok;
+    }
+    __syncthreads();
+    if (s_hit < 0) {
       // rounding left the threshold past this slice: its last positive entry
       int lastpos = -1;
-      for (int i = r0; i < r1; ++i) {
-        const double q = exp((double)lrow[i] / T - M) / S;
-        const double r = fmax(0.0, q - C * (use_p ? (double)prow[i] : 0.0));
-        if (r > 0.0) lastpos = i;
+#pragma unroll 1
+      for (int g = 0; g < NG; ++g) {
+        double rv[W];
+        r_group(g, CS, use_p, rv, &dummy);
+#pragma unroll
+        for (int j = 0; j < W; ++j)
+          if (rv[j] > 0.0) lastpos = max(lastpos, elem_index<W>(lo, g * W + j));
       }
-      __syncthreads();
-      if (tid == 0) s_hit = -1;
-      __syncthreads();
       if (lastpos >= 0) atomicMax(&s_hit, lastpos);
       __syncthreads();
       if (tid == 0) log_tie(a, b, v, 1, usf, 0.0);
-    } else if (tok >= 0 && tok == s_hit && margin < kSampleBand) {
+    } else if (tid == s_tsel && margin < kSampleBand) {
       log_tie(a, b, v, 1, usf, margin);
     }
     __syncthreads();
@@ -586,37 +757,94 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   }
 }
 
-__global__ void accept_init_kernel(int* bar, int B, int32_t* tie_count) {
+__global__ void accept_init_kernel(int* bar, int n, int32_t* tie_count) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < B) bar[i] = 0;
+  if (i < n) bar[i] = 0;
   if (i == 0 && tie_count) *tie_count = 0;
 }
 
+typedef void (*accept_fn)(AcceptArgs);
+
+accept_fn pick_kernel(int w, int ng) {
+  if (w == 4) {
+    switch (ng) {
+      case 1: return accept_kernel<1, 4>;
+      case 2: return accept_kernel<2, 4>;
+      case 4: return accept_kernel<4, 4>;
+      case 8: return accept_kernel<8, 4>;
+      default: return accept_kernel<16, 4>;
+    }
+  }
+  switch (ng) {
+    case 1: return accept_kernel<1, 1>;
+    case 2: return accept_kernel<2, 1>;
+    case 4: return accept_kernel<4, 1>;
+    case 8: return accept_kernel<8, 1>;
+    default: return accept_kernel<16, 1>;
+  }
+}
+
+// Groups per thread are capped so the sample scan's [NG][NT] float64 table
+// stays at 32 KB of LDS.
+constexpr int kMaxNG = 16;
+
 struct AcceptPlan {
-  int KP = 1;
-  int chunk = 0;
-  bool vec = false;
+  int KP = 1;      // workgroups per sequence
+  int NG = 1;      // element groups per thread
+  int W = 1;       // entries per group: 4 when rows allow 16-byte loads
+  int chunk = 0;   // entries per workgroup
   size_t ws = 0;
   size_t bar_bytes = 0;
 };
 
-AcceptPlan make_accept_plan(int B, int n_max, int V) {
+int resident_per_cu(int w, int ng) {
+  static int cache[2][5] = {{0}};
+  const int wi = w == 4 ? 1 : 0;
+  int ni = 0;
+  while ((1 << ni) < ng) ++ni;
+  if (cache[wi][ni] > 0) return cache[wi][ni];
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(pick_kernel(w, ng)), NT, 0) != hipSuccess)
+    per_cu = 1;
+  if (per_cu < 1) per_cu = 1;
+  cache[wi][ni] = per_cu;
+  return per_cu;
+}
+
+// KP workgroups of NT threads per sequence, each over NG groups of W entries.
+// The largest KP (most parallel vocabulary passes) whose B * KP workgroups
+// are all resident at once, so the whole batch walks in one cooperative
+// launch; beyond that (very large batches) the fewest workgroups per
+// sequence, walked in consecutive groups of sequences.
+AcceptPlan make_accept_plan(int B, int V) {
   AcceptPlan p;
-  p.vec = (V % 4) == 0;
+  p.W = (V % 4) == 0 ? 4 : 1;
+  const long per_group = (long)NT * p.W;
   const int cus = device_cu_count();
-  long kp = (2L * cus + B - 1) / B;
-  const long by_v = (V + 2047) / 2048;
-  if (kp > by_v) kp = by_v;
-  if (kp > SPEC_MAX_NODES) kp = SPEC_MAX_NODES;
-  if (const char* env = getenv("SPEC_ACCEPT_PARTS")) {
+  long forced = 0;
+  if (const char* env = getenv("SPEC_ACCEPT_PARTS")) {  // tuning sweeps
     const long e = atol(env);
-    if (e >= 1 && e <= SPEC_MAX_NODES) kp = e;
+    if (e >= 1 && e <= SPEC_MAX_NODES) forced = e;
   }
-  if (kp < 1) kp = 1;
-  int chunk = (int)((V + kp - 1) / kp);
-  if (p.vec) chunk = (chunk + 3) / 4 * 4;
-  p.chunk = chunk;
-  p.KP = (V + chunk - 1) / chunk;
+  int best_ng = kMaxNG;
+  if (forced) {
+    const long need = (V + forced * per_group - 1) / (forced * per_group);
+    best_ng = 1;
+    while (best_ng < need && best_ng < kMaxNG) best_ng *= 2;
+  } else {
+    for (int ng = 1; ng <= kMaxNG; ng *= 2) {
+      const long kp = (V + per_group * ng - 1) / (per_group * ng);
+      if (kp > SPEC_MAX_NODES) continue;
+      if ((long)B * kp <= (long)resident_per_cu(p.W, ng) * cus) {
+        best_ng = ng;
+        break;
+      }
+    }
+  }
+  p.NG = best_ng;
+  p.chunk = (int)(per_group * best_ng);
+  p.KP = (V + p.chunk - 1) / p.chunk;
   p.bar_bytes = ((size_t)B * sizeof(int) + 255) / 256 * 256;
   p.ws = p.bar_bytes + (size_t)B * p.KP * 4 * sizeof(double);
   return p;
@@ -629,7 +857,8 @@ using namespace specv;
 
 extern "C" size_t spec_accept_tree_workspace_size(int32_t B, int32_t n_max, int32_t V) {
   if (B <= 0 || n_max <= 0 || V <= 0) return 0;
-  return make_accept_plan(B, n_max, V).ws;
+  (void)n_max;
+  return make_accept_plan(B, V).ws;
 }
 
 extern "C" spec_status_t spec_accept_tree(
@@ -643,11 +872,13 @@ extern "C" spec_status_t spec_accept_tree(
       !accept_len || !path || !out_tokens || !n_out)
     return SPEC_E_NULL;
   if (tie_log && !tie_count) return SPEC_E_NULL;
-  if (B <= 0 || n_max <= 0 || n_max > SPEC_MAX_NODES || V <= 0 || max_depth < 0 ||
-      max_depth >= SPEC_MAX_NODES || (tie_log && tie_cap < 0))
+  if (B <= 0 || n_max <= 0 || n_max > SPEC_MAX_NODES || V <= 0 ||
+      V > SPEC_MAX_NODES * NT * kMaxNG * (V % 4 == 0 ? 4 : 1) || max_depth < 0 || max_depth >= SPEC_MAX_NODES ||
+      (tie_log && tie_cap < 0))
     return SPEC_E_SHAPE;
   if (!(temperature >= 0.f) || !isfinite(temperature)) return SPEC_E_VALUE;
-  AcceptPlan p = make_accept_plan(B, n_max, V);
+  AcceptPlan p = make_accept_plan(B, V);
+  if (p.KP > SPEC_MAX_NODES) return SPEC_E_SHAPE;
   if (!workspace || workspace_bytes < p.ws) return SPEC_E_WORKSPACE;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
 
@@ -656,50 +887,46 @@ extern "C" spec_status_t spec_accept_tree(
   a.draft_p = draft_p; a.logits = logits;
   a.B = B; a.n_max = n_max; a.V = V; a.max_depth = max_depth;
   a.greedy = temperature == 0.f ? 1 : 0;
-  a.T = (double)temperature;
+  a.inv_T = a.greedy ? 0.0 : 1.0 / (double)temperature;
   a.u_accept = u_accept; a.u_sample = u_sample;
   a.accept_len = accept_len; a.path = path; a.out_tokens = out_tokens; a.n_out = n_out;
   a.final_dist = final_dist; a.tie_log = tie_log; a.tie_cap = tie_cap; a.tie_count = tie_count;
+  a.KP = p.KP;
   a.chunk = p.chunk;
   a.bar = static_cast<int*>(workspace);
   a.part = reinterpret_cast<double*>(static_cast<char*>(workspace) + p.bar_bytes);
   a.dev_error = dev_error;
   a.spin_limit = 1 << 22;
+  const accept_fn fn = pick_kernel(p.W, p.NG);
 
-  // Cooperative launches need every workgroup resident: shrink KP to fit.
-  int kp = p.KP;
-  if (kp > 1) {
-    int per_cu = 0;
-    const void* fn = p.vec ? reinterpret_cast<const void*>(accept_kernel<true>)
-                           : reinterpret_cast<const void*>(accept_kernel<false>);
-    SPEC_HIP_TRY(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, 0));
-    const long resident = (long)per_cu * device_cu_count();
-    if ((long)B * kp > resident) {
-      kp = (int)(resident / B);
-      if (kp < 1) kp = 1;
-      int chunk = (V + kp - 1) / kp;
-      if (p.vec) chunk = (chunk + 3) / 4 * 4;
-      a.chunk = chunk;
-      kp = (V + chunk - 1) / chunk;
-    }
+  // Sequences per launch: all of them, unless the KP > 1 workgroups of every
+  // sequence cannot be resident together (cooperative launches need that).
+  int group = B;
+  if (p.KP > 1) {
+    const long resident = (long)resident_per_cu(p.W, p.NG) * device_cu_count();
+    if (resident < p.KP) return SPEC_E_UNSUPPORTED;
+    group = (int)(resident / p.KP < B ? resident / p.KP : B);
   }
-  a.KP = kp;
-
-  const int ib = (B + 255) / 256;
-  hipLaunchKernelGGL(accept_init_kernel, dim3(ib), dim3(256), 0, strm, a.bar, B, tie_count);
+  hipLaunchKernelGGL(accept_init_kernel, dim3((group + 255) / 256), dim3(256), 0, strm, a.bar,
+                     group, tie_count);
   SPEC_HIP_TRY(hipGetLastError());
-  const unsigned grid = (unsigned)((long)B * kp);
-  if (kp == 1) {
-    if (p.vec)
-      hipLaunchKernelGGL(accept_kernel<true>, dim3(grid), dim3(NT), 0, strm, a);
-    else
-      hipLaunchKernelGGL(accept_kernel<false>, dim3(grid), dim3(NT), 0, strm, a);
-    SPEC_HIP_TRY(hipGetLastError());
-  } else {
-    void* args[] = {&a};
-    const void* fn = p.vec ? reinterpret_cast<const void*>(accept_kernel<true>)
-                           : reinterpret_cast<const void*>(accept_kernel<false>);
-    SPEC_HIP_TRY(hipLaunchCooperativeKernel(fn, dim3(grid), dim3(NT), args, 0, strm));
+  for (int b0 = 0; b0 < B; b0 += group) {
+    const int nb = B - b0 < group ? B - b0 : group;
+    a.b0 = b0;
+    if (b0 > 0 && p.KP > 1) {
+      hipLaunchKernelGGL(accept_init_kernel, dim3((nb + 255) / 256), dim3(256), 0, strm, a.bar,
+                         nb, nullptr);
+      SPEC_HIP_TRY(hipGetLastError());
+    }
+    const unsigned grid = (unsigned)((long)nb * p.KP);
+    if (p.KP == 1) {
+      hipLaunchKernelGGL(fn, dim3(grid), dim3(NT), 0, strm, a);
+      SPEC_HIP_TRY(hipGetLastError());
+    } else {
+      void* args[] = {&a};
+      SPEC_HIP_TRY(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(grid),
+                                              dim3(NT), args, 0, strm));
+    }
   }
   return SPEC_OK;
 }

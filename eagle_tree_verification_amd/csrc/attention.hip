@@ -23,6 +23,8 @@
 //     node, head) on the vector ALU; used for small or f32 problems.
 // Splits of the prefix are merged by attn_merge_kernel (log-sum-exp).
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include "common.hpp"
 
@@ -172,6 +174,10 @@ struct MfmaArgs {
   int32_t* dev_error;
 };
 
+// 2^x on the hardware's transcendental unit (v_exp_f32): results below the
+// normal range flush to zero, which is harmless for softmax weights.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Position of key k (0..15) inside its 16-key group of a transposed V row:
 // bits 2 and 3 swapped, so that the 8 keys one lane half feeds to a 32x32x16
 // contraction step (keys 4h..4h+3 and 8+4h..8+4h+3) are contiguous.
@@ -182,10 +188,11 @@ __device__ __forceinline__ int vt_pos(int k) {
 template <int NB, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
   constexpr int NT = NW * 64;
-  constexpr int RPW = NW * NB * 32;            // query rows per workgroup
-  constexpr int CH = KT * HD / 8 / NT;         // 16-byte chunks per thread per tile (K or V)
-  constexpr int GPT = (KT / 4) * (HD / 8) / NT;  // V 4x8 transpose groups per thread
-  static_assert(CH == GPT * 4, "tile split");
+  constexpr int RPW = NW * NB * 32;                 // query rows per workgroup
+  constexpr int CH = KT * HD / 8 / NT;              // 16-byte K chunks per thread per tile
+  constexpr int KPG = NT >= 512 ? 2 : 4;            // keys per V transpose group
+  constexpr int GPT = (KT / KPG) * (HD / 8) / NT;   // V transpose groups per thread
+  static_assert(CH * NT * 8 == KT * HD && GPT * KPG == CH, "tile split");
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KS_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2][HD * VT_STRIDE];
@@ -253,26 +260,17 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
   // its 32-row block, head dims 16*ks + 8*lh .. +7.
   bf16x8_t qf[NB][8];
   uint64_t anc_r[NB];
-  int row_i[NB], row_h[NB];
-  bool rvalid[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int r = rb * RPW + (wave * NB + nb) * 32 + lr;
-    rvalid[nb] = r < Mb;
-    const int i = rvalid[nb] ? r / a.G : 0;
-    const int hh = rvalid[nb] ? r % a.G : 0;
-    row_i[nb] = i;
-    row_h[nb] = hh;
-    anc_r[nb] = rvalid[nb] ? anc[i] : 0ull;
+    const bool valid = r < Mb;
+    const int i = valid ? r / a.G : 0;
+    const int hh = valid ? r % a.G : 0;
+    anc_r[nb] = valid ? anc[i] : 0ull;
     const uint16_t* qp = a.q + (((size_t)b * a.n_max + i) * a.Hq + (size_t)g * a.G + hh) * HD + lh * 8;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      if (rvalid[nb]) {
-        qf[nb][ks] = *reinterpret_cast<const bf16x8_t*>(qp + ks * 16);
-      } else {
-        qf[nb][ks] = bf16x8_t{};
-      }
-    }
+    for (int ks = 0; ks < 8; ++ks)
+      qf[nb][ks] = valid ? *reinterpret_cast<const bf16x8_t*>(qp + ks * 16) : bf16x8_t{};
   }
 
   f32x16_t o[NB][4];
@@ -303,8 +301,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
     for (int j = 0; j < CH; ++j) {
       const int cidx = tid + j * NT;
       const int r = cidx >> 4;
-      const int col = (cidx & 15) * 8;
-      kreg[j] = r < nrows ? *reinterpret_cast<const uint4*>(kbase + (size_t)r * HD + col)
+      kreg[j] = r < nrows ? *reinterpret_cast<const uint4*>(kbase + (size_t)r * HD + (cidx & 15) * 8)
                           : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
@@ -313,10 +310,10 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
       const int dc = gi & 15;
       const int kq = gi >> 4;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int r = kq * 4 + kk;
-        vreg[gj * 4 + kk] = r < nrows ? *reinterpret_cast<const uint4*>(vbase + (size_t)r * HD + dc * 8)
-                                      : make_uint4(0, 0, 0, 0);
+      for (int kk = 0; kk < KPG; ++kk) {
+        const int r = kq * KPG + kk;
+        vreg[gj * KPG + kk] = r < nrows ? *reinterpret_cast<const uint4*>(vbase + (size_t)r * HD + dc * 8)
+                                        : make_uint4(0, 0, 0, 0);
       }
     }
   };
@@ -326,27 +323,34 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const int cidx = tid + j * NT;
-      const int r = cidx >> 4;
-      const int col = (cidx & 15) * 8;
-      *reinterpret_cast<uint4*>(ks_ + r * KS_STRIDE + col) = kreg[j];
+      *reinterpret_cast<uint4*>(ks_ + (cidx >> 4) * KS_STRIDE + (cidx & 15) * 8) = kreg[j];
     }
 #pragma unroll
     for (int gj = 0; gj < GPT; ++gj) {
       const int gi = tid + gj * NT;
       const int dc = gi & 15;
       const int kq = gi >> 4;
-      const int kpos = vt_pos(kq * 4);
-      const uint32_t* x0 = reinterpret_cast<const uint32_t*>(&vreg[gj * 4 + 0]);
-      const uint32_t* x1 = reinterpret_cast<const uint32_t*>(&vreg[gj * 4 + 1]);
-      const uint32_t* x2 = reinterpret_cast<const uint32_t*>(&vreg[gj * 4 + 2]);
-      const uint32_t* x3 = reinterpret_cast<const uint32_t*>(&vreg[gj * 4 + 3]);
+      const int kpos = vt_pos(kq * KPG);
+      const uint32_t* x0 = reinterpret_cast<const uint32_t*>(&vreg[gj * KPG + 0]);
+      const uint32_t* x1 = reinterpret_cast<const uint32_t*>(&vreg[gj * KPG + 1]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         // x_k[e] holds dims (2e, 2e+1) of key k as (low, high) halves.
-        const uint2 lo = make_uint2((x0[e] & 0xffffu) | (x1[e] << 16), (x2[e] & 0xffffu) | (x3[e] << 16));
-        const uint2 hi = make_uint2((x0[e] >> 16) | (x1[e] & 0xffff0000u), (x2[e] >> 16) | (x3[e] & 0xffff0000u));
-        *reinterpret_cast<uint2*>(vt_ + (dc * 8 + 2 * e) * VT_STRIDE + kpos) = lo;
-        *reinterpret_cast<uint2*>(vt_ + (dc * 8 + 2 * e + 1) * VT_STRIDE + kpos) = hi;
+        const uint32_t lo01 = (x0[e] & 0xffffu) | (x1[e] << 16);
+        const uint32_t hi01 = (x0[e] >> 16) | (x1[e] & 0xffff0000u);
+        uint16_t* d0 = vt_ + (dc * 8 + 2 * e) * VT_STRIDE + kpos;
+        uint16_t* d1 = d0 + VT_STRIDE;
+        if constexpr (KPG == 4) {
+          const uint32_t* x2 = reinterpret_cast<const uint32_t*>(&vreg[gj * KPG + 2]);
+          const uint32_t* x3 = reinterpret_cast<const uint32_t*>(&vreg[gj * KPG + 3]);
+          const uint32_t lo23 = (x2[e] & 0xffffu) | (x3[e] << 16);
+          const uint32_t hi23 = (x2[e] >> 16) | (x3[e] & 0xffff0000u);
+          *reinterpret_cast<uint2*>(d0) = make_uint2(lo01, lo23);
+          *reinterpret_cast<uint2*>(d1) = make_uint2(hi01, hi23);
+        } else {
+          *reinterpret_cast<uint32_t*>(d0) = lo01;
+          *reinterpret_cast<uint32_t*>(d1) = hi01;
+        }
       }
     }
   };
@@ -382,41 +386,55 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
       }
     }
 
-    // Online softmax; lane (lr, lh) holds keys 8*gq + 4*lh + e4 of each half.
+    // Mask only the ragged last prefix tile and the tree tile (uniform branch).
+    // Lane (lr, lh) holds keys 8*gq + 4*lh + e4 of each 32-key half.
+    if (tree || nrows < KT) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = kb * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+            const bool vis = key < nrows && (!tree || ((anc_r[nb] >> key) & 1ull));
+            if (!vis) sacc[nb][kb][e] = -INFINITY;
+          }
+    }
+
+    // Online softmax with the rescale of O skipped unless a row max moved.
     bf16x8_t pf[NB][2][2];
+    float alpha[NB];
+    int moved = 0;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       float mt = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kb * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
-          const bool vis = key < nrows && (!tree || ((anc_r[nb] >> key) & 1ull));
-          const float sv = vis ? sacc[nb][kb][e] : -INFINITY;
-          sacc[nb][kb][e] = sv;
-          mt = fmaxf(mt, sv);
-        }
-      }
+        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[nb][kb][e]);
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       const float mn = fmaxf(mrow[nb], mt);
       const float mu = (mn == -INFINITY) ? 0.f : mn;
       const float muc = mu * cs;
-      const float alpha = exp2f(mrow[nb] * cs - muc);
+      alpha[nb] = fast_exp2(mrow[nb] * cs - muc);
+      moved |= (mn != mrow[nb]);
       float ls = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = exp2f(fmaf(sacc[nb][kb][e], cs, -muc));
+          const float p = fast_exp2(fmaf(sacc[nb][kb][e], cs, -muc));
           ls += p;
           pf[nb][kb][e >> 3][e & 7] = static_cast<__bf16>(p);
         }
-      }
-      lrow[nb] = lrow[nb] * alpha + ls;
+      lrow[nb] = lrow[nb] * alpha[nb] + ls;
       mrow[nb] = mn;
+    }
+    if (__any(moved)) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[nb][db] *= alpha;
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[nb][db] *= alpha[nb];
     }
 
     // O^T (dims x rows) += V^T P^T.
@@ -443,11 +461,13 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const float lt = lrow[nb] + __shfl_xor(lrow[nb], 32);
-    if (!rvalid[nb]) continue;
     const int r = rb * RPW + (wave * NB + nb) * 32 + lr;
+    if (r >= Mb) continue;
+    const int i = r / a.G;
+    const int hh = r % a.G;
     if (a.S_max == 1) {
       const float inv = 1.f / lt;
-      float* op = a.out + (((size_t)b * a.n_max + row_i[nb]) * a.Hq + (size_t)g * a.G + row_h[nb]) * HD;
+      float* op = a.out + (((size_t)b * a.n_max + i) * a.Hq + (size_t)g * a.G + hh) * HD;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -496,7 +516,7 @@ __global__ __launch_bounds__(HD) void attn_merge_kernel(MfmaArgs a, int rows_per
   float lsum = 0.f, acc = 0.f;
   for (int s = 0; s < nsplit; ++s) {
     const float2 ml = a.part_ml[base + s];
-    const float wgt = exp2f((ml.x - mstar) * a.c);
+    const float wgt = fast_exp2((ml.x - mstar) * a.c);
     lsum += ml.y * wgt;
     acc += a.part_o[(base + s) * HD + threadIdx.x] * wgt;
   }
@@ -525,7 +545,14 @@ Plan make_plan(int B, int n_max, int Hq, int Hkv, int d, int L_cap, int dtype) {
   } else if (M <= 128) {
     p.nb = 1; p.nw = 4;
   } else {
-    p.nb = 2; p.nw = 4;
+    p.nb = 1; p.nw = 8;
+  }
+  if (const char* env = getenv("SPEC_ATTN_VARIANT")) {  // "NBxNW", for tuning sweeps
+    int nb = 0, nw = 0;
+    if (sscanf(env, "%dx%d", &nb, &nw) == 2 &&
+        ((nb == 1 && (nw == 2 || nw == 4 || nw == 8)) || (nb == 2 && nw == 4))) {
+      p.nb = nb; p.nw = nw;
+    }
   }
   p.rpw = p.nw * p.nb * 32;
   p.rb = (M + p.rpw - 1) / p.rpw;
@@ -628,6 +655,8 @@ extern "C" spec_status_t spec_verify_tree_attn(
     hipLaunchKernelGGL((attn_mfma_kernel<1, 2>), dim3(grid), dim3(128), 0, strm, a);
   else if (p.nb == 1 && p.nw == 4)
     hipLaunchKernelGGL((attn_mfma_kernel<1, 4>), dim3(grid), dim3(256), 0, strm, a);
+  else if (p.nb == 1 && p.nw == 8)
+    hipLaunchKernelGGL((attn_mfma_kernel<1, 8>), dim3(grid), dim3(512), 0, strm, a);
   else
     hipLaunchKernelGGL((attn_mfma_kernel<2, 4>), dim3(grid), dim3(256), 0, strm, a);
   SPEC_HIP_TRY(hipGetLastError());
