@@ -151,8 +151,11 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int KT = 64;              // keys per tile
 constexpr int HD = 128;             // head dim
-constexpr int KS_STRIDE = HD + 8;   // K tile row stride in LDS (bf16 elements)
-constexpr int VT_STRIDE = KT + 8;   // transposed V tile row stride (bf16 elements)
+constexpr int KS_STRIDE = HD + 8;   // K tile row stride in LDS (bf16 elements): 272 B
+// V tile row stride: 320 B, so the four key rows one transpose read touches
+// per 32 lanes start 64 B apart modulo the 256 B of LDS banks.
+constexpr int VS_STRIDE = HD + 32;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 struct MfmaArgs {
   const uint16_t* q;
@@ -178,24 +181,16 @@ struct MfmaArgs {
 // normal range flush to zero, which is harmless for softmax weights.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Position of key k (0..15) inside its 16-key group of a transposed V row:
-// bits 2 and 3 swapped, so that the 8 keys one lane half feeds to a 32x32x16
-// contraction step (keys 4h..4h+3 and 8+4h..8+4h+3) are contiguous.
-__device__ __forceinline__ int vt_pos(int k) {
-  return (k & ~15) | (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
-
-template <int NB, int NW>
+template <int NB, int NW, int SUB>
 __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
   constexpr int NT = NW * 64;
-  constexpr int RPW = NW * NB * 32;                 // query rows per workgroup
-  constexpr int CH = KT * HD / 8 / NT;              // 16-byte K chunks per thread per tile
-  constexpr int KPG = NT >= 512 ? 2 : 4;            // keys per V transpose group
-  constexpr int GPT = (KT / KPG) * (HD / 8) / NT;   // V transpose groups per thread
-  static_assert(CH * NT * 8 == KT * HD && GPT * KPG == CH, "tile split");
+  constexpr int RPW = NW * NB * 32;                    // query rows per workgroup
+  constexpr int ST = SUB * KT;                         // keys per load stage
+  constexpr int CH = ST * HD / 8 / NT;                 // 16-byte chunks per thread per stage (K or V)
+  static_assert(CH * NT * 8 == ST * HD, "stage split");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KT * KS_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][HD * VT_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][ST * KS_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][ST * VS_STRIDE];
   __shared__ uint64_t anc[64];
   __shared__ int flag;
   __shared__ int sorted_b;
@@ -288,93 +283,61 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
   const uint16_t* vbg = a.v + bg * (size_t)a.L_cap * HD;
   const int kb0 = s * a.chunk;
   const int ke0 = min(L, kb0 + a.chunk);
-  const int ntp = ke0 > kb0 ? (ke0 - kb0 + KT - 1) / KT : 0;
-  const int nt = ntp + (last ? 1 : 0);
+  const int ntp = ke0 > kb0 ? (ke0 - kb0 + ST - 1) / ST : 0;  // prefix stages
+  const int nt = ntp + (last ? 1 : 0);                        // + the tree stage
+
+  // Stage t: rows [row0, row0 + nrows) of the cache.
+  auto stage_rows = [&](int t, int& row0, int& nrows) {
+    row0 = t < ntp ? kb0 + t * ST : L;
+    nrows = t < ntp ? min(ST, ke0 - row0) : n;
+  };
 
   uint4 kreg[CH], vreg[CH];
-  auto load_tile = [&](int t) {
-    const int row0 = t < ntp ? kb0 + t * KT : L;
-    const int nrows = t < ntp ? min(KT, ke0 - row0) : n;
+  auto load_stage = [&](int t) {
+    int row0, nrows;
+    stage_rows(t, row0, nrows);
     const uint16_t* kbase = kbg + (size_t)row0 * HD;
     const uint16_t* vbase = vbg + (size_t)row0 * HD;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const int cidx = tid + j * NT;
       const int r = cidx >> 4;
-      kreg[j] = r < nrows ? *reinterpret_cast<const uint4*>(kbase + (size_t)r * HD + (cidx & 15) * 8)
-                          : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int gj = 0; gj < GPT; ++gj) {
-      const int gi = tid + gj * NT;
-      const int dc = gi & 15;
-      const int kq = gi >> 4;
-#pragma unroll
-      for (int kk = 0; kk < KPG; ++kk) {
-        const int r = kq * KPG + kk;
-        vreg[gj * KPG + kk] = r < nrows ? *reinterpret_cast<const uint4*>(vbase + (size_t)r * HD + dc * 8)
-                                        : make_uint4(0, 0, 0, 0);
-      }
+      const size_t off = (size_t)r * HD + (cidx & 15) * 8;
+      kreg[j] = r < nrows ? *reinterpret_cast<const uint4*>(kbase + off) : make_uint4(0, 0, 0, 0);
+      vreg[j] = r < nrows ? *reinterpret_cast<const uint4*>(vbase + off) : make_uint4(0, 0, 0, 0);
     }
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* ks_ = Ks[buf];
-    uint16_t* vt_ = Vt[buf];
+  auto store_stage = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const int cidx = tid + j * NT;
-      *reinterpret_cast<uint4*>(ks_ + (cidx >> 4) * KS_STRIDE + (cidx & 15) * 8) = kreg[j];
-    }
-#pragma unroll
-    for (int gj = 0; gj < GPT; ++gj) {
-      const int gi = tid + gj * NT;
-      const int dc = gi & 15;
-      const int kq = gi >> 4;
-      const int kpos = vt_pos(kq * KPG);
-      const uint32_t* x0 = reinterpret_cast<const uint32_t*>(&vreg[gj * KPG + 0]);
-      const uint32_t* x1 = reinterpret_cast<const uint32_t*>(&vreg[gj * KPG + 1]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // x_k[e] holds dims (2e, 2e+1) of key k as (low, high) halves.
-        const uint32_t lo01 = (x0[e] & 0xffffu) | (x1[e] << 16);
-        const uint32_t hi01 = (x0[e] >> 16) | (x1[e] & 0xffff0000u);
-        uint16_t* d0 = vt_ + (dc * 8 + 2 * e) * VT_STRIDE + kpos;
-        uint16_t* d1 = d0 + VT_STRIDE;
-        if constexpr (KPG == 4) {
-          const uint32_t* x2 = reinterpret_cast<const uint32_t*>(&vreg[gj * KPG + 2]);
-          const uint32_t* x3 = reinterpret_cast<const uint32_t*>(&vreg[gj * KPG + 3]);
-          const uint32_t lo23 = (x2[e] & 0xffffu) | (x3[e] << 16);
-          const uint32_t hi23 = (x2[e] >> 16) | (x3[e] & 0xffff0000u);
-          *reinterpret_cast<uint2*>(d0) = make_uint2(lo01, lo23);
-          *reinterpret_cast<uint2*>(d1) = make_uint2(hi01, hi23);
-        } else {
-          *reinterpret_cast<uint32_t*>(d0) = lo01;
-          *reinterpret_cast<uint32_t*>(d1) = hi01;
-        }
-      }
+      *reinterpret_cast<uint4*>(Ks[buf] + (cidx >> 4) * KS_STRIDE + (cidx & 15) * 8) = kreg[j];
+      *reinterpret_cast<uint4*>(Vs[buf] + (cidx >> 4) * VS_STRIDE + (cidx & 15) * 8) = vreg[j];
     }
   };
 
-  const float cs = a.c;
-  if (nt > 0) {
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-  }
-  for (int t = 0; t < nt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nt) load_tile(t + 1);
-    const bool tree = (t >= ntp);
-    const int nrows = tree ? n : min(KT, ke0 - (kb0 + t * KT));
+  // Transpose-read source of this lane for the V^T operand of one 32x32x16
+  // contraction step: within each 16-lane group the read hands lane d the
+  // (d % 4)-th entry of the 8-byte chunks of lanes 4j + d / 4, j = 0..3, so
+  // lane L points at key row 4 (L / 32) + (L % 16) / 4 of the step's key
+  // block and head dims 16 ((L / 16) % 2) + 4 (L % 4) .. +3 of the dim block;
+  // it receives head dim L % 32 of keys 4 (L / 32) + 0..3 (and, from the
+  // second read 8 keys further on, keys 8 + 4 (L / 32) + 0..3), matching the
+  // key order of the P^T operand taken straight from the score accumulators.
+  const int tr_key = 4 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_dim = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-    // S^T (keys x rows) for the two 32-key halves of the tile.
+  const float cs = a.c;
+  // One 64-key sub-tile: keys [64 * sub, 64 * sub + nrows) of the stage.
+  auto compute_sub = [&](int buf, int sub, int nrows, bool tree) {
+    // S^T (keys x rows) for the two 32-key halves of the sub-tile.
     f32x16_t sacc[NB][2];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       sacc[nb][0] = f32x16_t{};
       sacc[nb][1] = f32x16_t{};
     }
-    const uint16_t* ks_ = Ks[buf];
+    const uint16_t* ks_ = Ks[buf] + sub * KT * KS_STRIDE;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
@@ -386,7 +349,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
       }
     }
 
-    // Mask only the ragged last prefix tile and the tree tile (uniform branch).
+    // Mask only the ragged last prefix sub-tile and the tree tile (uniform).
     // Lane (lr, lh) holds keys 8*gq + 4*lh + e4 of each 32-key half.
     if (tree || nrows < KT) {
 #pragma unroll
@@ -437,23 +400,46 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
         for (int db = 0; db < 4; ++db) o[nb][db] *= alpha[nb];
     }
 
-    // O^T (dims x rows) += V^T P^T.
-    const uint16_t* vt_ = Vt[buf];
+    // O^T (dims x rows) += V^T P^T, V^T gathered by LDS transpose reads.
+    const uint16_t* vs_ = Vs[buf] + (sub * KT + tr_key) * VS_STRIDE + tr_dim;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(vt_ + (db * 32 + lr) * VT_STRIDE + kb * 32 + hb * 16 + lh * 8);
+          const uint16_t* src = vs_ + (kb * 32 + hb * 16) * VS_STRIDE + db * 32;
+          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (v4i16_t __attribute__((address_space(3)))*)(src));
+          const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (v4i16_t __attribute__((address_space(3)))*)(src + 8 * VS_STRIDE));
+          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
             o[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb][kb][hb], o[nb][db], 0, 0, 0);
         }
       }
     }
+  };
 
-    if (t + 1 < nt) store_tile(buf ^ 1);
+  if (nt > 0) {
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+  }
+  for (int t = 0; t < nt; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < nt) load_stage(t + 1);
+    int row0, nrows;
+    stage_rows(t, row0, nrows);
+    const bool tree = (t >= ntp);
+#pragma unroll
+    for (int sub = 0; sub < SUB; ++sub) {
+      const int rows_sub = nrows - sub * KT;
+      if (rows_sub <= 0) break;
+      compute_sub(buf, sub, min(KT, rows_sub), tree);
+    }
+    if (t + 1 < nt) store_stage(buf ^ 1);
     __syncthreads();
   }
 
@@ -530,7 +516,7 @@ __global__ __launch_bounds__(HD) void attn_merge_kernel(MfmaArgs a, int rows_per
 // ---------------------------------------------------------------------------
 struct Plan {
   bool mfma = false;
-  int nb = 0, nw = 0, rpw = 0, rb = 0, S_max = 1, chunk = 0, units = 0, sort = 0;
+  int nb = 0, nw = 0, sub = 1, rpw = 0, rb = 0, S_max = 1, chunk = 0, units = 0, sort = 0;
   size_t ws = 0;
 };
 
@@ -545,13 +531,15 @@ Plan make_plan(int B, int n_max, int Hq, int Hkv, int d, int L_cap, int dtype) {
   } else if (M <= 128) {
     p.nb = 1; p.nw = 4;
   } else {
-    p.nb = 1; p.nw = 8;
+    p.nb = 1; p.nw = 8; p.sub = 2;
   }
-  if (const char* env = getenv("SPEC_ATTN_VARIANT")) {  // "NBxNW", for tuning sweeps
+  if (const char* env = getenv("SPEC_ATTN_VARIANT")) {  // "NBxNW[xSUB]", tuning sweeps
     int nb = 0, nw = 0;
-    if (sscanf(env, "%dx%d", &nb, &nw) == 2 &&
+    int sub = 1;
+    if (sscanf(env, "%dx%dx%d", &nb, &nw, &sub) >= 2 &&
         ((nb == 1 && (nw == 2 || nw == 4 || nw == 8)) || (nb == 2 && nw == 4))) {
       p.nb = nb; p.nw = nw;
+      p.sub = (nb == 1 && nw == 8 && sub == 2) ? 2 : 1;
     }
   }
   p.rpw = p.nw * p.nb * 32;
@@ -652,13 +640,15 @@ extern "C" spec_status_t spec_verify_tree_attn(
   }
   const unsigned grid = (unsigned)(((p.units + 7) / 8) * 8 * p.rb);
   if (p.nb == 1 && p.nw == 2)
-    hipLaunchKernelGGL((attn_mfma_kernel<1, 2>), dim3(grid), dim3(128), 0, strm, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<1, 2, 1>), dim3(grid), dim3(128), 0, strm, a);
   else if (p.nb == 1 && p.nw == 4)
-    hipLaunchKernelGGL((attn_mfma_kernel<1, 4>), dim3(grid), dim3(256), 0, strm, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<1, 4, 1>), dim3(grid), dim3(256), 0, strm, a);
+  else if (p.nb == 1 && p.nw == 8 && p.sub == 2)
+    hipLaunchKernelGGL((attn_mfma_kernel<1, 8, 2>), dim3(grid), dim3(512), 0, strm, a);
   else if (p.nb == 1 && p.nw == 8)
-    hipLaunchKernelGGL((attn_mfma_kernel<1, 8>), dim3(grid), dim3(512), 0, strm, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<1, 8, 1>), dim3(grid), dim3(512), 0, strm, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<2, 4>), dim3(grid), dim3(256), 0, strm, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<2, 4, 1>), dim3(grid), dim3(256), 0, strm, a);
   SPEC_HIP_TRY(hipGetLastError());
   if (p.S_max > 1) {
     hipLaunchKernelGGL(attn_merge_kernel, dim3(p.rb * p.rpw, Hkv, B), dim3(HD), 0, strm, a,
