@@ -35,6 +35,10 @@
 // walked in consecutive groups.  Every inter-workgroup wait is bounded.
 #include <math.h>
 #include <stdlib.h>
+#include <unistd.h>
+
+#include <atomic>
+#include <chrono>
 
 #include "common.hpp"
 
@@ -118,8 +122,8 @@ struct AcceptArgs {
   int b0;       // first sequence of this launch
   int KP;       // workgroups per sequence
   int chunk;    // vocabulary entries per workgroup (NT * W * NG)
-  int* bar;     // [group size] arrival counters (zeroed before the launch)
-  double* part; // [group size][KP][2 slots][2]
+  uint64_t* slots;  // [group size][2][KP][8] tagged exchange words
+  uint64_t epoch;   // launch id (40 bits), part of every exchange tag
   int32_t* dev_error;
   int spin_limit;
 };
@@ -151,38 +155,41 @@ __device__ float block_max(float v, double* red) {
   return t;
 }
 
-__device__ __forceinline__ void lse_combine(double& m, double& s, double m2, double s2) {
-  if (m2 == -INFINITY) return;
-  if (m == -INFINITY) {
-    m = m2;
-    s = s2;
-    return;
-  }
-  if (m2 > m) {
-    s = s * exp_nonpos(m - m2) + s2;
-    m = m2;
-  } else {
-    s += s2 * exp_nonpos(m2 - m);
-  }
+// Butterfly reductions over one wave.  Every lane ends with the same value,
+// and every wave running them on the same inputs gets the same bits, so all
+// workgroups of a sequence reach identical decisions.
+__device__ __forceinline__ double wave_max_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  return v;
 }
 
-__device__ void block_lse(double& m, double& s, double* red) {
+__device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const double m2 = __shfl_xor(m, o);
-    const double s2 = __shfl_xor(s, o);
-    lse_combine(m, s, m2, s2);
-  }
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Combines per-thread (max, sum of exp relative to max) over the workgroup:
+// one wave max, one rescale per lane, one wave sum, then the NT / 64 wave
+// results.
+__device__ void block_lse(double& m, double& s, double* red) {
+  const double wm = wave_max_d(m);
+  const double ts = wave_sum_d(m == -INFINITY ? 0.0 : s * exp_nonpos(m - wm));
   const int wv = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) {
-    red[2 * wv] = m;
-    red[2 * wv + 1] = s;
+    red[2 * wv] = wm;
+    red[2 * wv + 1] = ts;
   }
   __syncthreads();
-  double mm = -INFINITY, ss = 0.0;
+  double mm = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < NT / 64; ++k) lse_combine(mm, ss, red[2 * k], red[2 * k + 1]);
+  for (int k = 0; k < NT / 64; ++k) mm = fmax(mm, red[2 * k]);
+  double ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k)
+    if (red[2 * k] != -INFINITY) ss += red[2 * k + 1] * exp_nonpos(red[2 * k] - mm);
   m = mm;
   s = ss;
 }
@@ -217,63 +224,65 @@ __device__ void block_argmax(float& v, int& i, double* red) {
   i = bi;
 }
 
-__device__ int block_or(int f, int* s_or) {
-  __syncthreads();
-  if (threadIdx.x == 0) *s_or = 0;
-  __syncthreads();
-  if (f) atomicOr(s_or, 1);
-  __syncthreads();
-  return *s_or;
-}
+__device__ __forceinline__ int block_or(int f, int*) { return __syncthreads_or(f); }
 
 // ---- inter-workgroup exchange ---------------------------------------------
-// Publishes this workgroup's two partials, waits until all KP workgroups of
-// the sequence have published theirs, and loads every partial into xs.
+// Publishes this workgroup's two partials and gathers all KP workgroups'
+// partials into xs.  Each partial travels as four 64-bit words of 16 payload
+// bits under a 48-bit tag (launch id, exchange number), written and read with
+// device-coherent 64-bit atomic accesses.  A word is valid once its tag is
+// current, whatever order the words arrive in, so the readers poll the data
+// itself: one memory round trip per exchange, with no counter, no fence and
+// nothing to clear between calls.  Slots alternate between two buffers; a
+// workgroup reuses a buffer only after every workgroup has published the next
+// exchange, which each does only after reading this one.
 __device__ bool exchange(const AcceptArgs& a, int bl, int part, int& gen, double v0, double v1,
-                         double (*xs)[2], int* s_ok) {
+                         double (*xs)[2], int* s_or) {
+  const int t = threadIdx.x;
+  __syncthreads();  // xs of the previous exchange is no longer read
   if (a.KP == 1) {
-    __syncthreads();
-    if (threadIdx.x == 0) {
+    if (t == 0) {
       xs[0][0] = v0;
       xs[0][1] = v1;
     }
     __syncthreads();
     return true;
   }
-  const int slot = gen & 1;
+  const uint64_t tag = ((a.epoch << 8) | (uint64_t)(gen & 0xff)) & 0xFFFFFFFFFFFFull;
+  uint64_t* slot = a.slots + ((size_t)bl * 2 + (gen & 1)) * (size_t)a.KP * 8;
   ++gen;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    // Everything the workgroups share here (partials, arrival counter) is
-    // read and written with device-coherent atomic accesses, so no cache-wide
-    // release/acquire fence is needed (on this chip those write back and
-    // invalidate the whole L2, which every later pass would pay for).  The
-    // partial stores only have to complete before the arrival is counted.
-    double* dst = a.part + (((size_t)bl * a.KP + part) * 2 + slot) * 2;
-    __hip_atomic_store(dst, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(dst + 1, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);  // all outstanding memory operations done
-    __hip_atomic_fetch_add(a.bar + bl, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int target = gen * a.KP;
-    int ok = 1, spins = 0;
-    while (__hip_atomic_load(a.bar + bl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > a.spin_limit) {
-        ok = 0;
-        break;
+  if (t < 8) {
+    const uint64_t bits = (uint64_t)__double_as_longlong(t < 4 ? v0 : v1);
+    const uint64_t w = (tag << 16) | ((bits >> (16 * (t & 3))) & 0xffffull);
+    __hip_atomic_store(slot + part * 8 + t, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const int nw = a.KP * 8;
+  int bad = 0;
+#pragma unroll
+  for (int r = 0; r < (SPEC_MAX_NODES * 8 + NT - 1) / NT; ++r) {
+    const int i = t + r * NT;  // word i: part i / 8, value (i / 4) % 2, bits 16 (i % 4)
+    uint64_t w = 0;
+    if (i < nw) {
+      int spins = 0;
+      for (;;) {
+        w = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((w >> 16) == tag) break;
+        if (++spins > a.spin_limit) {
+          bad = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
       }
     }
-    *s_ok = ok;
+    // the four words of one value sit in four consecutive lanes
+    const uint64_t p0 = w & 0xffffull;
+    const uint64_t p1 = __shfl_down(p0, 1);
+    const uint64_t p2 = __shfl_down(p0, 2);
+    const uint64_t p3 = __shfl_down(p0, 3);
+    if (i < nw && (i & 3) == 0)
+      xs[i >> 3][(i >> 2) & 1] = __longlong_as_double((long long)(p0 | (p1 << 16) | (p2 << 32) | (p3 << 48)));
   }
-  __syncthreads();
-  if (!*s_ok) return false;
-  if ((int)threadIdx.x < a.KP) {
-    const double* src = a.part + (((size_t)bl * a.KP + threadIdx.x) * 2 + slot) * 2;
-    xs[threadIdx.x][0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    xs[threadIdx.x][1] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  return true;
+  return !block_or(bad, s_or);
 }
 
 __device__ void log_tie(const AcceptArgs& a, int b, int node, int kind, float u, double margin) {
@@ -378,7 +387,8 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   __shared__ double cur_sums[SPEC_MAX_NODES];
   __shared__ double scan[NG][NT];
   __shared__ double gtot[NG];
-  __shared__ int s_ok, s_or, s_hit, s_gsel, s_tsel;
+  __shared__ int s_or, s_hit, s_gsel, s_tsel;
+  __shared__ float s_kp[SPEC_MAX_NODES], s_kl[SPEC_MAX_NODES], s_ku[SPEC_MAX_NODES], s_us;
   __shared__ double s_before;
   __shared__ double s_tab[64];
 
@@ -386,6 +396,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   const int b = a.b0 + bl;
   const int part = blockIdx.x % a.KP;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int lo = part * a.chunk;
   const int hi = min(a.V, lo + a.chunk);
   const bool writer0 = (part == 0);
@@ -458,15 +469,19 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
           });
       nf = block_or(nf, &s_or);
       block_argmax(bv, bi, red);
-      if (!exchange(a, bl, part, gen, (double)bv, nf ? -1.0 : (double)bi, xs, &s_ok)) {
+      if (!exchange(a, bl, part, gen, (double)bv, nf ? -1.0 : (double)bi, xs, &s_or)) {
         if (writer0) write_failure(a, b, SPEC_DEVERR_SYNC);
         return;
       }
-      float gv = -INFINITY;
-      int gi = 0x7fffffff, gnf = 0;
-      for (int k = 0; k < a.KP; ++k) {
-        if (xs[k][1] < 0.0) gnf = 1;
-        amax_combine(gv, gi, (float)xs[k][0], (int)xs[k][1]);
+      const bool has = lane < a.KP;
+      float gv = has ? (float)xs[lane][0] : -INFINITY;
+      int gi = has ? (int)xs[lane][1] : 0x7fffffff;
+      const bool gnf = __any(has && xs[lane][1] < 0.0);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float v2 = __shfl_xor(gv, o);
+        const int i2 = __shfl_xor(gi, o);
+        amax_combine(gv, gi, v2, i2);
       }
       if (gnf) {
         if (writer0) write_failure(a, b, SPEC_DEVERR_NONFINITE);
@@ -495,6 +510,18 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       return;
     }
 
+    // What the child tests and the terminal sample read, loaded now so that
+    // the loads overlap the statistics pass.
+    const bool kid = tid > v && tid < n && s_par[tid] == v;
+    float k_p = 0.f, k_l = 0.f, k_u = 0.f, k_us = 0.f;
+    if (kid) {
+      const int xt = s_tok[tid];
+      k_p = prow[xt];
+      k_l = lrow[xt];
+      k_u = a.u_accept[rows_b + tid];
+    }
+    if (tid == 0) k_us = a.u_sample[rows_b + v];
+
     // ---- T > 0: max and sum of exp(z) over the slice, online per batch ----
     double m = -INFINITY, es = 0.0;
     int nf = 0;
@@ -522,22 +549,29 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
         });
     nf = block_or(nf, &s_or);
     block_lse(m, es, red);
-    if (!exchange(a, bl, part, gen, m, nf ? -1.0 : es, xs, &s_ok)) {
+    if (!exchange(a, bl, part, gen, m, nf ? -1.0 : es, xs, &s_or)) {
       if (writer0) write_failure(a, b, SPEC_DEVERR_SYNC);
       return;
     }
-    double M = -INFINITY, S = 0.0;
-    int gnf = 0;
-    for (int k = 0; k < a.KP; ++k) {
-      if (xs[k][1] < 0.0) gnf = 1;
-      lse_combine(M, S, xs[k][0], xs[k][1]);
-    }
-    if (gnf) {
+    // combine the KP partials, lane k of every wave taking partial k
+    const bool has = lane < a.KP;
+    const double pm = has ? xs[lane][0] : -INFINITY;
+    const double ps = has ? xs[lane][1] : 0.0;
+    if (__any(has && ps < 0.0)) {
       if (writer0) write_failure(a, b, SPEC_DEVERR_NONFINITE);
       return;
     }
+    const double M = wave_max_d(pm);
+    const double pterm = (has && pm != -INFINITY) ? ps * exp_nonpos(pm - M) : 0.0;
+    const double S = wave_sum_d(pterm);
     // slice masses of q (in units of S) for the sample when no child is rejected
-    if (tid < a.KP) cur_sums[tid] = xs[tid][1] * exp_nonpos(xs[tid][0] - M);
+    if (tid < a.KP) cur_sums[tid] = pterm;
+    if (kid) {
+      s_kp[tid] = k_p;
+      s_kl[tid] = k_l;
+      s_ku[tid] = k_u;
+    }
+    if (tid == 0) s_us = k_us;
     __syncthreads();
 
     // r = max(0, exp(z - M) - CS p) for one group of W entries
@@ -564,7 +598,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
     for (int c = v + 1; c < n; ++c) {
       if (s_par[c] != v) continue;
       const int xt = s_tok[c];
-      const float pxf = prow[xt];
+      const float pxf = s_kp[c];
       if (!isfinite(pxf)) {
         if (writer0) write_failure(a, b, SPEC_DEVERR_NONFINITE);
         return;
@@ -574,10 +608,10 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
         nxt = c;
         break;
       }
-      const double qx = exp_nonpos((double)lrow[xt] * invT - M) / S;
+      const double qx = exp_nonpos((double)s_kl[c] * invT - M) / S;
       const double cur = fmax(0.0, qx - C * px) / Z;
       const double thr = fmin(1.0, cur / px);
-      const float uf = a.u_accept[rows_b + c];
+      const float uf = s_ku[c];
       const double u = (double)uf;
       if (writer0 && tid == 0 && fabs(u - thr) < kTieBand) log_tie(a, b, c, 0, uf, fabs(u - thr));
       if (u < thr) {
@@ -602,17 +636,13 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
           });
       pnf = block_or(pnf, &s_or);
       zp = block_sum(zp, red);
-      if (!exchange(a, bl, part, gen, zp, (double)pnf, xs, &s_ok)) {
+      if (!exchange(a, bl, part, gen, zp, (double)pnf, xs, &s_or)) {
         if (writer0) write_failure(a, b, SPEC_DEVERR_SYNC);
         return;
       }
-      double Zs = 0.0;
-      int gp = 0;
-      for (int k = 0; k < a.KP; ++k) {
-        Zs += xs[k][0];
-        gp |= (xs[k][1] != 0.0);
-      }
-      if (gp) {
+      const bool has = lane < a.KP;
+      const double Zs = wave_sum_d(has ? xs[lane][0] : 0.0);
+      if (__any(has && xs[lane][1] != 0.0)) {
         if (writer0) write_failure(a, b, SPEC_DEVERR_NONFINITE);
         return;
       }
@@ -641,7 +671,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
     const double CS = C * S;
     double Wt = 0.0;
     for (int k = 0; k < a.KP; ++k) Wt += cur_sums[k];
-    const float usf = a.u_sample[rows_b + v];
+    const float usf = s_us;
     const double thr = (double)usf * Wt;
     int sel = -1, last_pos = -1;
     double off = 0.0, off_sel = 0.0;
@@ -757,10 +787,25 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   }
 }
 
-__global__ void accept_init_kernel(int* bar, int n, int32_t* tie_count) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) bar[i] = 0;
-  if (i == 0 && tie_count) *tie_count = 0;
+// Clears the near-tie counter (only launched when the caller logs ties).
+__global__ void accept_init_kernel(int32_t* tie_count) {
+  if (threadIdx.x == 0) *tie_count = 0;
+}
+
+// Launch ids for exchange tags: 40 bits, never 0, distinct for 2^40 launches
+// of this process; the start is drawn from the clock and the process id so
+// that words left in reused memory by another process are unlikely to carry a
+// current tag.
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> counter{0};
+  static const uint64_t start = [] {
+    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    return (t * 0x9E3779B97F4A7C15ull) ^ ((uint64_t)getpid() << 20);
+  }();
+  for (;;) {
+    const uint64_t e = (start + counter.fetch_add(1, std::memory_order_relaxed)) & 0xFFFFFFFFFFull;
+    if (e != 0) return e;
+  }
 }
 
 typedef void (*accept_fn)(AcceptArgs);
@@ -794,7 +839,6 @@ struct AcceptPlan {
   int W = 1;       // entries per group: 4 when rows allow 16-byte loads
   int chunk = 0;   // entries per workgroup
   size_t ws = 0;
-  size_t bar_bytes = 0;
 };
 
 int resident_per_cu(int w, int ng) {
@@ -845,8 +889,7 @@ AcceptPlan make_accept_plan(int B, int V) {
   p.NG = best_ng;
   p.chunk = (int)(per_group * best_ng);
   p.KP = (V + p.chunk - 1) / p.chunk;
-  p.bar_bytes = ((size_t)B * sizeof(int) + 255) / 256 * 256;
-  p.ws = p.bar_bytes + (size_t)B * p.KP * 4 * sizeof(double);
+  p.ws = p.KP > 1 ? (size_t)B * 2 * p.KP * 8 * sizeof(uint64_t) : 256;
   return p;
 }
 
@@ -893,8 +936,7 @@ extern "C" spec_status_t spec_accept_tree(
   a.final_dist = final_dist; a.tie_log = tie_log; a.tie_cap = tie_cap; a.tie_count = tie_count;
   a.KP = p.KP;
   a.chunk = p.chunk;
-  a.bar = static_cast<int*>(workspace);
-  a.part = reinterpret_cast<double*>(static_cast<char*>(workspace) + p.bar_bytes);
+  a.slots = static_cast<uint64_t*>(workspace);
   a.dev_error = dev_error;
   a.spin_limit = 1 << 22;
   const accept_fn fn = pick_kernel(p.W, p.NG);
@@ -907,17 +949,14 @@ extern "C" spec_status_t spec_accept_tree(
     if (resident < p.KP) return SPEC_E_UNSUPPORTED;
     group = (int)(resident / p.KP < B ? resident / p.KP : B);
   }
-  hipLaunchKernelGGL(accept_init_kernel, dim3((group + 255) / 256), dim3(256), 0, strm, a.bar,
-                     group, tie_count);
-  SPEC_HIP_TRY(hipGetLastError());
+  if (tie_count) {
+    hipLaunchKernelGGL(accept_init_kernel, dim3(1), dim3(64), 0, strm, tie_count);
+    SPEC_HIP_TRY(hipGetLastError());
+  }
   for (int b0 = 0; b0 < B; b0 += group) {
     const int nb = B - b0 < group ? B - b0 : group;
     a.b0 = b0;
-    if (b0 > 0 && p.KP > 1) {
-      hipLaunchKernelGGL(accept_init_kernel, dim3((nb + 255) / 256), dim3(256), 0, strm, a.bar,
-                         nb, nullptr);
-      SPEC_HIP_TRY(hipGetLastError());
-    }
+    a.epoch = next_epoch();
     const unsigned grid = (unsigned)((long)nb * p.KP);
     if (p.KP == 1) {
       hipLaunchKernelGGL(fn, dim3(grid), dim3(NT), 0, strm, a);

@@ -8,15 +8,20 @@
 // prefix_len + 0..a and the length advances by a + 1.  A chain-shaped path
 // (path[i] == i) moves nothing.  Moves are in place and path[i] >= i, so a
 // row can be both read and written (path [0, 2, 5]: row 2 is read for slot 1
-// and written by slot 2): each workgroup loads every row it moves for one KV
-// head into registers, waits at a barrier, then stores.
+// and written by slot 2): one workgroup per sequence loads every row it moves
+// (all KV heads, K and V) into registers, waits at a barrier, then stores.
+// Moves that do not fit one round are done in rounds of increasing slot within
+// each (head, K/V) plane; a later round reads only rows path[s] >= s beyond
+// every row an earlier round wrote, so rounds never see each other's writes.
+// The workgroup also owns the sequence's length, so no other workgroup can
+// read it after it advances.
 #include "common.hpp"
 
 namespace specv {
 namespace {
 
-constexpr int NT = 256;
-constexpr int MAXCH = (SPEC_MAX_NODES * 128 * 4 / 16 + NT - 1) / NT;  // 16-B chunks per thread
+constexpr int NT = 1024;
+constexpr int CPT = 16;  // 16-byte chunks per thread per round
 
 __global__ __launch_bounds__(NT) void commit_kernel(uint4* kc, uint4* vc, int32_t* prefix_len,
                                                     const int32_t* path, const int32_t* accept_len,
@@ -50,32 +55,43 @@ __global__ __launch_bounds__(NT) void commit_kernel(uint4* kc, uint4* vc, int32_
     return;
   }
   if (s_moves) {
-    // rows 1..a move (row 0 is the root, already in place)
-    const int nchunks = a * row_chunks;
-    for (int g = 0; g < Hkv; ++g) {
-      for (int which = 0; which < 2; ++which) {
-        uint4* base = (which == 0 ? kc : vc) + ((size_t)b * Hkv + g) * (size_t)L_cap * row_chunks +
-                      (size_t)L * row_chunks;
-        uint4 regs[MAXCH];
+    // chunk c = ((g * 2 + kv) * a + slot - 1) * row_chunks + cc: rows 1..a of
+    // every plane (row 0 is the root, already in place)
+    const int plane_chunks = a * row_chunks;
+    const int total = Hkv * 2 * plane_chunks;
+    const size_t plane_stride = (size_t)L_cap * row_chunks;
+    // element offset of chunk c's row `row` (relative to the sequence's
+    // prefix end) in its plane
+    auto offset = [&](int c, int row_of_slot, int* pl_out) -> size_t {
+      const int pl = c / plane_chunks;
+      const int rem = c - pl * plane_chunks;
+      const int slot = 1 + rem / row_chunks;
+      const int cc = rem - (slot - 1) * row_chunks;
+      *pl_out = pl;
+      const int row = row_of_slot ? s_path[slot] : slot;
+      return ((size_t)b * Hkv + (pl >> 1)) * plane_stride + (size_t)(L + row) * row_chunks + cc;
+    };
+    for (int r0 = 0; r0 < total; r0 += NT * CPT) {
+      uint4 regs[CPT];
 #pragma unroll
-        for (int j = 0; j < MAXCH; ++j) {
-          const int c = tid + j * NT;
-          if (c < nchunks) {
-            const int slot = 1 + c / row_chunks;
-            regs[j] = base[(size_t)s_path[slot] * row_chunks + c % row_chunks];
-          }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < MAXCH; ++j) {
-          const int c = tid + j * NT;
-          if (c < nchunks) {
-            const int slot = 1 + c / row_chunks;
-            base[(size_t)slot * row_chunks + c % row_chunks] = regs[j];
-          }
-        }
-        __syncthreads();
+      for (int j = 0; j < CPT; ++j) {
+        const int c = r0 + j * NT + tid;
+        int pl = 0;
+        const size_t off = c < total ? offset(c, 1, &pl) : 0;
+        const uint4* src = (pl & 1) ? vc : kc;
+        regs[j] = c < total ? src[off] : make_uint4(0, 0, 0, 0);
       }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) {
+        const int c = r0 + j * NT + tid;
+        if (c < total) {
+          int pl = 0;
+          const size_t off = offset(c, 0, &pl);
+          ((pl & 1) ? vc : kc)[off] = regs[j];
+        }
+      }
+      __syncthreads();
     }
   }
   if (tid == 0) prefix_len[b] = L + a + 1;
