@@ -79,14 +79,17 @@ enum {
   SPEC_DEVERR_SYNC = 16       /* an inter-workgroup wait hit its bound (walk abandoned)    */
 };
 
-/* One near-tie record of spec_accept_tree (kind 0: accept test, 1: sample). */
+/* One near-tie record of spec_accept_tree (kind 0: accept test, 1: sample,
+ * 2: residual whose mass fell below 1e-12 of the previous one, so rounding
+ * may decide whether it is zero). */
 typedef struct {
   int32_t b;      /* sequence                                             */
-  int32_t node;   /* child tested (kind 0) or node sampled at (kind 1)    */
+  int32_t node;   /* child tested (kinds 0, 2) or node sampled at (kind 1) */
   int32_t kind;
   float u;        /* the uniform used                                     */
-  double margin;  /* |u - min(1, ratio)|, or distance of u*W to the chosen
-                     bucket's nearer edge divided by W                     */
+  double margin;  /* |u - min(1, ratio)|; distance of u*W to the chosen
+                     bucket's nearer edge divided by W; or new / old
+                     residual mass                                         */
 } spec_tie_t;
 
 /*
@@ -163,7 +166,11 @@ size_t spec_verify_tree_attn_workspace_size(
  *                          margin < 1e-9; *tie_count (device int32, required
  *                          when tie_log is given) is reset by the call and
  *                          counts all such events, logged or not
- *   workspace              >= spec_accept_tree_workspace_size(...) bytes
+ *   workspace              >= spec_accept_tree_workspace_size(...) bytes of
+ *                          device memory; needs no initialisation (the words
+ *                          workgroups exchange through it carry a per-launch
+ *                          tag); calls sharing one workspace must be ordered
+ *                          on one stream
  * Device errors: SPEC_DEVERR_TREE, _TOKEN, _NONFINITE, _SYNC.
  */
 spec_status_t spec_accept_tree(
