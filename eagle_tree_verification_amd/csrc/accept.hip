@@ -78,27 +78,33 @@ __device__ __forceinline__ double exp_nonpos(double y) {
   return y < -745.5 ? 0.0 : v;
 }
 
-// exp(y) for y <= 0 (or -inf) in float64, for the per-entry passes: y =
-// (64 q + j) ln2 / 64 + r with |r| <= ln2 / 128, exp(r) by its Taylor series to
-// degree 5 (truncation below 4e-17 relative), times tab[j] = 2^(j/64) and 2^q.
-// Within two ulp; no branch, so it can run on every lane of a slice pass.
+// exp(y) for y <= 0 (or -inf) in float64, for the per-entry passes: with
+// n = round(256 y / ln2) = 256 k + j, exp(y) = 2^k * tab[j] * exp(r), where
+// tab[j] = 2^(j/256), r = y - n ln2 / 256 (ln2 / 256 in two parts, so
+// |r| <= ln2 / 512 up to rounding) and exp(r) is its Taylor series to degree
+// 4 (truncation below 4e-17 relative).  n comes from the low word of
+// y * 256 / ln2 + 1.5 * 2^52, whose addition rounds to an integer.  Within two
+// ulp; -inf and anything below -746 give 0 (ldexp underflows); no branch.
+constexpr int kTabBits = 8;
+constexpr int kTab = 1 << kTabBits;
+
 __device__ __forceinline__ double exp_tab(double y, const double* tab) {
-  constexpr double kInvLn2x64 = 92.33248261689366;  // 64 / ln2
-  constexpr double kLn2Hi64 = 6.93147180369123816490e-01 / 64;
-  constexpr double kLn2Lo64 = 1.90821492927058770002e-10 / 64;
+  constexpr double kInvLn2xT = 369.3299304675746;  // 256 / ln2
+  constexpr double kShift = 6755399441055744.0;     // 1.5 * 2^52
+  constexpr double kLn2HiT = 6.93147180369123816490e-01 / kTab;
+  constexpr double kLn2LoT = 1.90821492927058770002e-10 / kTab;
   const double yc = fmax(y, -746.0);
-  const double n = rint(yc * kInvLn2x64);
-  double r = fma(-n, kLn2Hi64, yc);
-  r = fma(-n, kLn2Lo64, r);
-  double p = 1.0 / 120.0;
-  p = fma(p, r, 1.0 / 24.0);
+  const double t = fma(yc, kInvLn2xT, kShift);
+  const double n = t - kShift;
+  const int ni = __double2loint(t);
+  double r = fma(-n, kLn2HiT, yc);
+  r = fma(-n, kLn2LoT, r);
+  double p = 1.0 / 24.0;
   p = fma(p, r, 1.0 / 6.0);
   p = fma(p, r, 0.5);
   p = fma(p, r, 1.0);
   p = fma(p, r, 1.0);
-  const int ni = (int)n;
-  const double v = ldexp(tab[ni & 63] * p, ni >> 6);
-  return y < -745.5 ? 0.0 : v;
+  return ldexp(tab[ni & (kTab - 1)] * p, ni >> kTabBits);
 }
 
 struct AcceptArgs {
@@ -377,7 +383,10 @@ __device__ __forceinline__ void stream_slice(const float* r1, float f1, const fl
 
 template <int NG, int W>
 __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
-  constexpr int BG = NG < 2 ? NG : 2;  // groups loaded together
+  // groups loaded together: four in the one-row passes, two when the
+  // residual pass streams logits and draft rows side by side
+  constexpr int BG1 = NG < 4 ? NG : 4;
+  constexpr int BG2 = NG < 2 ? NG : 2;
   __shared__ int s_par[SPEC_MAX_NODES];
   __shared__ int s_tok[SPEC_MAX_NODES];
   __shared__ int s_path[SPEC_MAX_NODES + 1];
@@ -390,7 +399,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   __shared__ int s_or, s_hit, s_gsel, s_tsel;
   __shared__ float s_kp[SPEC_MAX_NODES], s_kl[SPEC_MAX_NODES], s_ku[SPEC_MAX_NODES], s_us;
   __shared__ double s_before;
-  __shared__ double s_tab[64];
+  __shared__ double s_tab[kTab];
 
   const int bl = blockIdx.x / a.KP;   // sequence within this launch's group
   const int b = a.b0 + bl;
@@ -401,7 +410,8 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   const int hi = min(a.V, lo + a.chunk);
   const bool writer0 = (part == 0);
 
-  if (tid < 64) s_tab[tid] = 2.0 * exp_nonpos((double)(tid - 64) / 64.0 * 0.6931471805599453);
+  for (int j = tid; j < kTab; j += NT)
+    s_tab[j] = 2.0 * exp_nonpos((double)(j - kTab) / kTab * 0.6931471805599453);
 
   // ---- validation (identical in every workgroup of the sequence) ----------
   const int n = a.n_nodes[b];
@@ -454,10 +464,10 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
     if (a.greedy) {
       float bv = -INFINITY;
       int bi = 0x7fffffff, nf = 0;
-      stream_slice<NG, W, BG, false>(lrow, -INFINITY, lrow, 0.f, lo, hi,
+      stream_slice<NG, W, BG1, false>(lrow, -INFINITY, lrow, 0.f, lo, hi,
           [&](int g0, float (*xv)[W], float (*)[W]) {
 #pragma unroll
-            for (int gb = 0; gb < BG; ++gb)
+            for (int gb = 0; gb < BG1; ++gb)
 #pragma unroll
               for (int j = 0; j < W; ++j) {
                 const int i = elem_index<W>(lo, (g0 + gb) * W + j);
@@ -525,11 +535,11 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
     // ---- T > 0: max and sum of exp(z) over the slice, online per batch ----
     double m = -INFINITY, es = 0.0;
     int nf = 0;
-    stream_slice<NG, W, BG, false>(lrow, -INFINITY, lrow, 0.f, lo, hi,
+    stream_slice<NG, W, BG1, false>(lrow, -INFINITY, lrow, 0.f, lo, hi,
         [&](int g0, float (*xv)[W], float (*)[W]) {
           float bmax = -INFINITY;
 #pragma unroll
-          for (int gb = 0; gb < BG; ++gb)
+          for (int gb = 0; gb < BG1; ++gb)
 #pragma unroll
             for (int j = 0; j < W; ++j) {
               const bool valid = elem_index<W>(lo, (g0 + gb) * W + j) < hi;
@@ -543,7 +553,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
             m = zb;
           }
 #pragma unroll
-          for (int gb = 0; gb < BG; ++gb)
+          for (int gb = 0; gb < BG1; ++gb)
 #pragma unroll
             for (int j = 0; j < W; ++j) es += exp_tab(fma((double)xv[gb][j], invT, -m), s_tab);
         });
@@ -623,10 +633,10 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       double zp = 0.0;
       int pnf = 0;
       const double CnS = Cn * S;
-      stream_slice<NG, W, BG, true>(lrow, -INFINITY, prow, 0.f, lo, hi,
+      stream_slice<NG, W, BG2, true>(lrow, -INFINITY, prow, 0.f, lo, hi,
           [&](int, float (*xv)[W], float (*pv)[W]) {
 #pragma unroll
-            for (int gb = 0; gb < BG; ++gb)
+            for (int gb = 0; gb < BG2; ++gb)
 #pragma unroll
               for (int j = 0; j < W; ++j) {
                 pnf |= !isfinite(pv[gb][j]);
