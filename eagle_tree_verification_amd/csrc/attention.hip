@@ -32,6 +32,7 @@ namespace specv {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazy = 8.f;  // log2 of the largest weight the online softmax lets through
 
 // ---------------------------------------------------------------------------
 // Tree validation and ancestor masks.  anc[j] has bit i set iff node i is on
@@ -376,11 +377,16 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[nb][kb][e]);
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(mrow[nb], mt);
+      // The reference max moves only when the row max exceeds it by more
+      // than 2^kLazy in weight (always at the first finite score), so O and l
+      // are rarely rescaled; weights stay <= 2^kLazy, harmless in fp32 and
+      // bf16, and O and l always share one reference.
+      const bool up = (mt - mrow[nb]) * cs > kLazy;
+      const float mn = up ? mt : mrow[nb];
       const float mu = (mn == -INFINITY) ? 0.f : mn;
       const float muc = mu * cs;
-      alpha[nb] = fast_exp2(mrow[nb] * cs - muc);
-      moved |= (mn != mrow[nb]);
+      alpha[nb] = up ? fast_exp2(mrow[nb] * cs - muc) : 1.f;
+      moved |= up;
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
