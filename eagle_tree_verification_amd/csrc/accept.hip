@@ -28,11 +28,13 @@
 // max(0, exp(z - M) - C S p); the terminal token needs no extra pass: the
 // slice masses of the current residual are already known, and only the
 // workgroup whose slice holds the threshold scans it in order.  All vocab
-// arithmetic is float64 (z = logit / T); exp runs on the vector ALU with a
-// Cody-Waite argument reduction and a degree-13 Taylor polynomial (arguments
-// are never positive here), within one ulp.  KP > 1 is a cooperative launch
-// (all workgroups resident); a batch too large to be resident at once is
-// walked in consecutive groups.  Every inter-workgroup wait is bounded.
+// arithmetic is float64 (z = logit / T); exp runs on the vector ALU (a
+// 256-entry table method in the per-entry passes, a Cody-Waite reduction with
+// a Taylor polynomial elsewhere; arguments are never positive here).  The
+// launch plan keeps all KP workgroups of every sequence of a launch resident
+// at once; a batch too large for that is walked in consecutive groups.  Every
+// inter-workgroup wait is bounded and reports SPEC_DEVERR_SYNC when it gives
+// up, so a walk that cannot complete ends instead of hanging.
 #include <math.h>
 #include <stdlib.h>
 #include <unistd.h>
@@ -272,6 +274,10 @@ __device__ bool exchange(const AcceptArgs& a, int bl, int part, int& gen, double
       int spins = 0;
       for (;;) {
         w = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (a.spin_limit < 0) {  // test hook: every wait gives up at once
+          bad = 1;
+          break;
+        }
         if ((w >> 16) == tag) break;
         if (++spins > a.spin_limit) {
           bad = 1;
@@ -314,6 +320,18 @@ __device__ void write_failure(const AcceptArgs& a, int b, int bits) {
   for (int k = threadIdx.x; k <= a.max_depth; k += NT) {
     a.path[(size_t)b * (a.max_depth + 1) + k] = -1;
     a.out_tokens[(size_t)b * (a.max_depth + 1) + k] = -1;
+  }
+}
+
+// A wait that hit its bound: every workgroup that sees it reports it; the
+// sequence's first workgroup also marks the sequence failed.  Workgroups of
+// the sequence that got past the same exchange may still write outputs, so
+// after SPEC_DEVERR_SYNC the batch's outputs are unspecified.
+__device__ void fail_sync(const AcceptArgs& a, int b, bool writer0) {
+  if (writer0) {
+    write_failure(a, b, SPEC_DEVERR_SYNC);
+  } else if (threadIdx.x == 0) {
+    report(a.dev_error, SPEC_DEVERR_SYNC);
   }
 }
 
@@ -480,7 +498,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       nf = block_or(nf, &s_or);
       block_argmax(bv, bi, red);
       if (!exchange(a, bl, part, gen, (double)bv, nf ? -1.0 : (double)bi, xs, &s_or)) {
-        if (writer0) write_failure(a, b, SPEC_DEVERR_SYNC);
+        fail_sync(a, b, writer0);
         return;
       }
       const bool has = lane < a.KP;
@@ -560,7 +578,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
     nf = block_or(nf, &s_or);
     block_lse(m, es, red);
     if (!exchange(a, bl, part, gen, m, nf ? -1.0 : es, xs, &s_or)) {
-      if (writer0) write_failure(a, b, SPEC_DEVERR_SYNC);
+      fail_sync(a, b, writer0);
       return;
     }
     // combine the KP partials, lane k of every wave taking partial k
@@ -647,7 +665,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       pnf = block_or(pnf, &s_or);
       zp = block_sum(zp, red);
       if (!exchange(a, bl, part, gen, zp, (double)pnf, xs, &s_or)) {
-        if (writer0) write_failure(a, b, SPEC_DEVERR_SYNC);
+        fail_sync(a, b, writer0);
         return;
       }
       const bool has = lane < a.KP;
@@ -868,8 +886,8 @@ int resident_per_cu(int w, int ng) {
 
 // KP workgroups of NT threads per sequence, each over NG groups of W entries.
 // The largest KP (most parallel vocabulary passes) whose B * KP workgroups
-// are all resident at once, so the whole batch walks in one cooperative
-// launch; beyond that (very large batches) the fewest workgroups per
+// are all resident at once, so the whole batch walks in one launch; beyond
+// that (very large batches) the fewest workgroups per
 // sequence, walked in consecutive groups of sequences.
 AcceptPlan make_accept_plan(int B, int V) {
   AcceptPlan p;
@@ -948,11 +966,16 @@ extern "C" spec_status_t spec_accept_tree(
   a.chunk = p.chunk;
   a.slots = static_cast<uint64_t*>(workspace);
   a.dev_error = dev_error;
+  // bound on the polls of one inter-workgroup wait; tests set a negative
+  // bound, which makes every wait give up at once, to drive the failure path
   a.spin_limit = 1 << 22;
+  if (const char* env = getenv("SPEC_ACCEPT_SPIN_LIMIT")) a.spin_limit = atoi(env);
   const accept_fn fn = pick_kernel(p.W, p.NG);
+  const char* coop_env = getenv("SPEC_ACCEPT_COOPERATIVE");
+  const bool cooperative = coop_env && coop_env[0] == '1';
 
   // Sequences per launch: all of them, unless the KP > 1 workgroups of every
-  // sequence cannot be resident together (cooperative launches need that).
+  // sequence cannot be resident together (their exchanges need that).
   int group = B;
   if (p.KP > 1) {
     const long resident = (long)resident_per_cu(p.W, p.NG) * device_cu_count();
@@ -972,9 +995,18 @@ extern "C" spec_status_t spec_accept_tree(
       hipLaunchKernelGGL(fn, dim3(grid), dim3(NT), 0, strm, a);
       SPEC_HIP_TRY(hipGetLastError());
     } else {
-      void* args[] = {&a};
-      SPEC_HIP_TRY(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(grid),
-                                              dim3(NT), args, 0, strm));
+      // The plan keeps every workgroup of the launch resident at once on an
+      // otherwise idle GPU, so an ordinary launch is used (a cooperative one
+      // costs about 17 us more per call); SPEC_ACCEPT_COOPERATIVE=1 asks the
+      // runtime to guarantee residency where the GPU is shared.
+      if (cooperative) {
+        void* args[] = {&a};
+        SPEC_HIP_TRY(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(grid),
+                                                dim3(NT), args, 0, strm));
+      } else {
+        hipLaunchKernelGGL(fn, dim3(grid), dim3(NT), 0, strm, a);
+        SPEC_HIP_TRY(hipGetLastError());
+      }
     }
   }
   return SPEC_OK;

@@ -76,7 +76,8 @@ enum {
   SPEC_DEVERR_TOKEN = 2,      /* a draft token outside [0, V)                              */
   SPEC_DEVERR_NONFINITE = 4,  /* NaN/Inf in a logits or draft-probability entry read       */
   SPEC_DEVERR_CAPACITY = 8,   /* prefix_len < 0 or prefix_len + n_nodes > L_cap            */
-  SPEC_DEVERR_SYNC = 16       /* an inter-workgroup wait hit its bound (walk abandoned)    */
+  SPEC_DEVERR_SYNC = 16       /* an inter-workgroup wait hit its bound (walk abandoned;
+                                 spec_accept_tree outputs of the batch unspecified)        */
 };
 
 /* One near-tie record of spec_accept_tree (kind 0: accept test, 1: sample,
@@ -172,6 +173,13 @@ size_t spec_verify_tree_attn_workspace_size(
  *                          tag); calls sharing one workspace must be ordered
  *                          on one stream
  * Device errors: SPEC_DEVERR_TREE, _TOKEN, _NONFINITE, _SYNC.
+ * The workgroups that share one sequence's vocabulary exchange partial sums
+ * and must be resident together; the call sizes its launch so that they are
+ * on an otherwise idle GPU and uses an ordinary launch.  Where other work may
+ * hold the GPU's compute units, set SPEC_ACCEPT_COOPERATIVE=1 in the
+ * environment to have the runtime guarantee residency (a cooperative launch,
+ * slower to start).  Either way every wait is bounded: a walk that cannot
+ * complete sets SPEC_DEVERR_SYNC instead of hanging.
  */
 spec_status_t spec_accept_tree(
     const int32_t* tokens, const int32_t* parents, const int32_t* n_nodes,

@@ -131,3 +131,37 @@ def test_commit_in_place_hazard(hip_lib):
         assert torch.equal(v[0, :, L + dst], v0[0, :, L + src])
     assert torch.equal(k[1], k0[1]) and torch.equal(v[1], v0[1])
     assert plen.cpu().tolist() == [L + 3, L + 4]
+
+
+def test_accept_wait_bound_reports_sync(hip_lib, monkeypatch):
+    """A host-set negative wait bound makes every vocabulary exchange give up:
+    the call must end normally with SPEC_DEVERR_SYNC set and the failed
+    sequences marked, and the next call with the default bound on the same
+    workspace must be exact again."""
+    import torch
+    from eagle_tree_verification_amd import api
+    w = make_workload(4, batch=8, prefix=(64, 64), vocab=128256, drafts=12, depth=4, seed=5)
+    dev = to_device(w)
+    ws = torch.empty(api.accept_tree_workspace_size(w.B, w.n_max, w.V), dtype=torch.uint8,
+                     device="cuda")
+    say(f"[gpu] wait bound: B={w.B} V={w.V}, forced give-up then default")
+
+    def call():
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        r = api.accept_tree(dev["tokens"], dev["parents"], dev["n_nodes"], dev["draft_p"],
+                            dev["logits"], w.T, dev["u_accept"], dev["u_sample"], w.max_depth,
+                            workspace=ws, dev_error=err)
+        torch.cuda.synchronize()
+        return r, int(err.item())
+
+    monkeypatch.setenv("SPEC_ACCEPT_SPIN_LIMIT", "-1")
+    r0, e0 = call()
+    assert e0 & api.DEVERR_SYNC, e0
+    assert (r0["accept_len"].cpu().numpy() == -1).all()
+    monkeypatch.delenv("SPEC_ACCEPT_SPIN_LIMIT")
+    r, e1 = call()
+    assert e1 == 0
+    host = {k: v.cpu().numpy() for k, v in r.items() if isinstance(v, torch.Tensor)}
+    host["ties"] = np.zeros(0, dtype=api.TIE_DTYPE)
+    host["final_dist"] = None
+    compare_accept(w, host)
