@@ -579,7 +579,9 @@ spec_status_t check_args(const void* q, const void* k, const void* v, const int3
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_E_DTYPE;
   if (d != 16 && d != 32 && d != 64 && d != 128) return SPEC_E_DTYPE;
   if (!(scale > 0.f) || !isfinite(scale)) return SPEC_E_VALUE;
-  if ((long)B * n_max * Hq > (1L << 30) || (long)B * Hkv * L_cap > (1L << 31) / 1) return SPEC_E_SHAPE;
+  // query rows and cache rows are counted in 32-bit ints (grid sizes, row
+  // indices); byte offsets are 64-bit
+  if ((long)B * n_max * Hq > (1L << 30) || (long)B * Hkv * L_cap >= (1L << 31)) return SPEC_E_SHAPE;
   return SPEC_OK;
 }
 
