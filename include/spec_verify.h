@@ -24,10 +24,13 @@
  *
  * Common conventions
  *   - Every array pointer is a DEVICE pointer owned by the caller.  The
- *     library keeps no pointer after the stream work completes, holds no
- *     global mutable state and allocates no device memory; scratch space
- *     comes from the caller's `workspace`, sized by the *_workspace_size
- *     functions for the same arguments and the same current device.
+ *     library keeps no pointer after the stream work completes and allocates
+ *     no device memory; scratch space comes from the caller's `workspace`,
+ *     sized by the *_workspace_size functions for the same arguments and the
+ *     same current device.  Its only host state is cached device properties
+ *     (compute-unit count, occupancy) and an atomic launch counter, so calls
+ *     from several host threads are safe; calls that share a workspace must
+ *     be ordered on one stream.
  *   - `stream` is a hipStream_t (NULL = the null stream).  All work is
  *     asynchronous on it; outputs are valid once the caller synchronises.
  *   - A negative status is returned, before anything is launched, for any
