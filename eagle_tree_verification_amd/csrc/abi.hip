@@ -1,17 +1,24 @@
 // Library-wide entry points: status strings, ABI version, device queries.
+#include <atomic>
+
 #include "common.hpp"
 
 namespace specv {
 
+// Compute units of the current device, cached per device (relaxed atomics:
+// concurrent first calls store the same value).
 int device_cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  if (dev < 64) cached[dev] = cus;
+  if (dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 

@@ -869,18 +869,21 @@ struct AcceptPlan {
   size_t ws = 0;
 };
 
+// Workgroups of the (W, NG) variant one compute unit holds at once, cached
+// (relaxed atomics: concurrent first calls store the same value).
 int resident_per_cu(int w, int ng) {
-  static int cache[2][5] = {{0}};
+  static std::atomic<int> cache[2][5];
   const int wi = w == 4 ? 1 : 0;
   int ni = 0;
   while ((1 << ni) < ng) ++ni;
-  if (cache[wi][ni] > 0) return cache[wi][ni];
+  const int c = cache[wi][ni].load(std::memory_order_relaxed);
+  if (c > 0) return c;
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
           &per_cu, reinterpret_cast<const void*>(pick_kernel(w, ng)), NT, 0) != hipSuccess)
     per_cu = 1;
   if (per_cu < 1) per_cu = 1;
-  cache[wi][ni] = per_cu;
+  cache[wi][ni].store(per_cu, std::memory_order_relaxed);
   return per_cu;
 }
 
