@@ -22,5 +22,5 @@ than itself).
 from .attention import tree_attention, ancestors, path_to_root  # noqa: F401
 from .accept import (AcceptResult, accept_tree, accept_rule, residual,  # noqa: F401
                      target_distribution, sample_inverse_cdf, TIE_BAND, SAMPLE_BAND)
-from .commit import kv_commit  # noqa: F401
+from .commit import kv_commit, kv_commit_from_buffer  # noqa: F401
 from .validate import validate_tree, ERR_TREE, ERR_TOKEN, ERR_NONFINITE, ERR_CAPACITY  # noqa: F401

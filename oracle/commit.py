@@ -1,8 +1,10 @@
 """KV commit of the accepted path (plain copies).
 
 Parity: pinned (tests/test_oracle_commit.py) by the bookkeeping invariants of
-page "推测解码与 EAGLE-3", section "KV cache 回滚" and build step 4, and the
-page's batched-rollback exercise worked out by hand under tests/golden/.
+page "推测解码与 EAGLE-3", section "KV cache 回滚" and build step 4, the
+page's batched-rollback exercise worked out by hand under tests/golden/, and
+(for the scratch-buffer form) its agreement with the in-place form on the same
+tree rows.
 
 The verify pass has written the K/V of every tree node into cache rows
 prefix_len + i.  Rollback is either a physical cache with a logical length
@@ -32,4 +34,27 @@ def kv_commit(k, v, prefix_len, path, accept_len):
     for i in range(int(accept_len) + 1):
         k2[:, L + i] = k[:, L + int(path[i])]
         v2[:, L + i] = v[:, L + int(path[i])]
+    return k2, v2, L + int(accept_len) + 1
+
+
+def kv_commit_from_buffer(k, v, k_tree, v_tree, prefix_len, path, accept_len):
+    """The other rollback form of section "KV cache 回滚": the verify pass wrote
+    the tree's K/V to a scratch buffer, and acceptance commits the root and the
+    accepted drafts into the cache.
+
+    k, v: [Hkv][L_cap][d] cache of one sequence; k_tree, v_tree: [Hkv][n][d]
+    scratch rows of its tree.  Cache row prefix_len + i receives scratch row
+    path[i] for i = 0..a (the root included: the cache never held it).
+    Returns (k', v', new_len); a sequence with accept_len < 0 is unchanged.
+    """
+    k = np.asarray(k)
+    v = np.asarray(v)
+    if accept_len < 0:
+        return k.copy(), v.copy(), int(prefix_len)
+    L = int(prefix_len)
+    k2 = k.copy()
+    v2 = v.copy()
+    for i in range(int(accept_len) + 1):
+        k2[:, L + i] = np.asarray(k_tree)[:, int(path[i])]
+        v2[:, L + i] = np.asarray(v_tree)[:, int(path[i])]
     return k2, v2, L + int(accept_len) + 1

@@ -86,3 +86,47 @@ def test_batched_rollback_exercise():
         assert new_len == seq["new_len"]
         moved = sum(int(not np.array_equal(k2[:, L + i], k[:, L + i])) for i in range(n))
         assert moved == seq["rows_moved"]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_commit_from_buffer_matches_in_place(seed):
+    """The scratch-buffer form and the in-place form of the rollback section
+    commit the same rows when the scratch rows equal the cache's tree rows;
+    rows the scratch form never touches stay as they were."""
+    rng = np.random.default_rng(100 + seed)
+    depth = int(rng.integers(1, 4))
+    parents = tree_shape(int(rng.integers(depth, 10 * depth)), depth, rng)
+    n = len(parents)
+    path = oracle.path_to_root(parents, int(rng.integers(0, n)))
+    a = len(path) - 1
+    hkv, d, L = 2, 4, int(rng.integers(0, 20))
+    cap = L + n + 3
+    k = rng.normal(size=(hkv, cap, d))
+    v = rng.normal(size=(hkv, cap, d))
+    k_tree, v_tree = k[:, L:L + n].copy(), v[:, L:L + n].copy()
+    ki, vi, li = oracle.kv_commit(k, v, L, path, a)
+    # the scratch form starts from a cache whose tree rows hold stale data
+    stale_k, stale_v = k.copy(), v.copy()
+    stale_k[:, L:] = -7.0
+    stale_v[:, L:] = -7.0
+    kb, vb, lb = oracle.kv_commit_from_buffer(stale_k, stale_v, k_tree, v_tree, L, path, a)
+    assert lb == li == L + a + 1
+    np.testing.assert_array_equal(kb[:, :L + a + 1], ki[:, :L + a + 1])
+    np.testing.assert_array_equal(vb[:, :L + a + 1], vi[:, :L + a + 1])
+    assert np.all(kb[:, L + a + 1:] == -7.0) and np.all(vb[:, L + a + 1:] == -7.0)
+
+
+def test_commit_from_buffer_chain_and_failure():
+    # a chain accepts its first a drafts in order; a failed walk changes nothing
+    hkv, d, L, n = 1, 2, 5, 4
+    k = np.zeros((hkv, L + n, d))
+    v = np.zeros((hkv, L + n, d))
+    kt = np.arange(n * d, dtype=float).reshape(1, n, d)
+    vt = -kt
+    k2, v2, ln = oracle.kv_commit_from_buffer(k, v, kt, vt, L, [0, 1, 2], 2)
+    assert ln == L + 3
+    np.testing.assert_array_equal(k2[0, L:L + 3], kt[0, :3])
+    np.testing.assert_array_equal(v2[0, L:L + 3], vt[0, :3])
+    assert np.all(k2[0, L + 3:] == 0)
+    k3, v3, l3 = oracle.kv_commit_from_buffer(k, v, kt, vt, L, [], -1)
+    assert l3 == L and np.all(k3 == k) and np.all(v3 == v)
