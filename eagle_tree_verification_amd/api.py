@@ -60,6 +60,8 @@ def load():
     lib.spec_accept_tree_workspace_size.restype = Z
     lib.spec_kv_commit.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P]
     lib.spec_kv_commit.restype = I
+    lib.spec_kv_commit_layers.argtypes = [P, P, P, P, I, P, P, P, I, I, I, I, I, I, I, P, P]
+    lib.spec_kv_commit_layers.restype = I
     lib.spec_status_string.argtypes = [I]
     lib.spec_status_string.restype = ctypes.c_char_p
     lib.spec_abi_version.argtypes = []
@@ -208,3 +210,60 @@ def kv_commit(k_cache, v_cache, prefix_len, path, accept_len, max_depth, *, dev_
                             _ptr(accept_len), B, Hkv, d, L_cap, int(max_depth), dt,
                             _ptr(dev_error), _stream(stream))
     _check("spec_kv_commit", st)
+
+
+def _pointer_table(tensors, name, like=None):
+    """Device array of the tensors' data pointers (one small host-to-device
+    copy; the tensors must outlive the stream work that reads it)."""
+    tensors = list(tensors)
+    if not tensors:
+        raise ValueError(f"{name}: no layers")
+    ref = like if like is not None else tensors[0]
+    for t in tensors:
+        _dev(t, name, ref.dtype)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name}: every layer must have shape {tuple(ref.shape)}")
+    ptrs = torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64)
+    return ptrs.to(ref.device, non_blocking=False)
+
+
+def kv_commit_layers(k_layers, v_layers, prefix_len, path, accept_len, max_depth, *,
+                     k_tree=None, v_tree=None, dev_error=None, stream=None):
+    """Commit the accepted paths of every layer in one call.
+
+    k_layers, v_layers: sequences of per-layer caches [B][Hkv][L_cap][d].
+    k_tree, v_tree: None (tree K/V already in the caches, committed in place)
+    or sequences of per-layer scratch rows [B][Hkv][n_max][d].
+    prefix_len advances once.  Returns the pointer tables, which must stay
+    alive until the stream work completes.
+    """
+    lib = load()
+    k_layers, v_layers = list(k_layers), list(v_layers)
+    if len(v_layers) != len(k_layers):
+        raise ValueError("k_layers and v_layers differ in length")
+    B, Hkv, L_cap, d = k_layers[0].shape
+    dt = _kv_dtype(k_layers[0])
+    kt = _pointer_table(k_layers, "k_layers")
+    vt = _pointer_table(v_layers, "v_layers", like=k_layers[0])
+    n_max = 0
+    tk = tv = None
+    if (k_tree is None) != (v_tree is None):
+        raise ValueError("give both k_tree and v_tree, or neither")
+    if k_tree is not None:
+        k_tree, v_tree = list(k_tree), list(v_tree)
+        if len(k_tree) != len(k_layers) or len(v_tree) != len(k_layers):
+            raise ValueError("one scratch buffer per layer")
+        Bt, Ht, n_max, dt_ = k_tree[0].shape
+        if (Bt, Ht, dt_) != (B, Hkv, d):
+            raise ValueError("scratch rows must be [B][Hkv][n_max][head_dim]")
+        tk = _pointer_table(k_tree, "k_tree", like=k_tree[0])
+        tv = _pointer_table(v_tree, "v_tree", like=k_tree[0])
+        if k_tree[0].dtype != k_layers[0].dtype:
+            raise ValueError("scratch rows and caches must share a dtype")
+    for t, nm in ((prefix_len, "prefix_len"), (path, "path"), (accept_len, "accept_len")):
+        _dev(t, nm, torch.int32)
+    st = lib.spec_kv_commit_layers(_ptr(kt), _ptr(vt), _ptr(tk), _ptr(tv), len(k_layers),
+                                   _ptr(prefix_len), _ptr(path), _ptr(accept_len), B, n_max, Hkv,
+                                   d, L_cap, int(max_depth), dt, _ptr(dev_error), _stream(stream))
+    _check("spec_kv_commit_layers", st)
+    return (kt, vt, tk, tv)

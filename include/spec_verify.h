@@ -217,6 +217,42 @@ spec_status_t spec_kv_commit(
     int32_t B, int32_t Hkv, int32_t head_dim, int32_t L_cap, int32_t max_depth,
     int32_t dtype, int32_t* dev_error, void* stream);
 
+/*
+ * spec_kv_commit_layers -- spec_kv_commit for num_layers layers in one call,
+ * in either rollback form of [LESSON] "KV cache 回滚":
+ *   - in place (k_tree == NULL): the verify pass wrote tree node j's K/V of
+ *     every layer into cache row prefix_len[b] + j; for every layer, cache
+ *     row prefix_len[b] + i receives row prefix_len[b] + path[b][i]
+ *     (spec_kv_commit, layer by layer);
+ *   - scratch buffer (k_tree, v_tree given): the verify pass wrote the tree's
+ *     K/V of layer l into k_tree[l], v_tree[l]; cache row prefix_len[b] + i
+ *     receives scratch row path[b][i] for i = 0..a, the root included.
+ * Then prefix_len[b] advances by a + 1, once.  Sequences with accept_len < 0
+ * are untouched.  Not idempotent: call once per step, after spec_accept_tree
+ * (and instead of spec_kv_commit).
+ *
+ *   k_layers, v_layers  device array [num_layers] of device pointers, each to
+ *                       a [B][Hkv][L_cap][head_dim] cache of dtype (in/out)
+ *   k_tree, v_tree      NULL for the in-place form, or device arrays
+ *                       [num_layers] of device pointers, each to
+ *                       [B][Hkv][n_max][head_dim] scratch rows of dtype
+ *   num_layers          >= 1
+ *   n_max               scratch rows per sequence (scratch form; otherwise
+ *                       ignored)
+ *   prefix_len, path, accept_len, B, Hkv, head_dim, L_cap, max_depth, dtype
+ *                       as for spec_kv_commit
+ * The pointer arrays are read by the kernels: they must stay valid until the
+ * stream work completes.
+ * Device errors: as spec_kv_commit; in the scratch form also SPEC_DEVERR_TREE
+ * for a path entry >= n_max.  A failed sequence is left untouched in every
+ * layer.
+ */
+spec_status_t spec_kv_commit_layers(
+    void* const* k_layers, void* const* v_layers, const void* const* k_tree,
+    const void* const* v_tree, int32_t num_layers, int32_t* prefix_len, const int32_t* path,
+    const int32_t* accept_len, int32_t B, int32_t n_max, int32_t Hkv, int32_t head_dim,
+    int32_t L_cap, int32_t max_depth, int32_t dtype, int32_t* dev_error, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* spec_status_string(spec_status_t status);
 

@@ -19,7 +19,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = api.declared_functions()
     assert set(names) == {"spec_verify_tree_attn", "spec_verify_tree_attn_workspace_size",
                           "spec_accept_tree", "spec_accept_tree_workspace_size", "spec_kv_commit",
-                          "spec_status_string", "spec_abi_version"}
+                          "spec_kv_commit_layers", "spec_status_string", "spec_abi_version"}
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -77,4 +77,23 @@ def test_commit_host_checks(lib):
     bad = list(args); bad[8] = 0           # L_cap
     assert f(*bad) == SPEC_E_SHAPE
     bad = list(args); bad[10] = 3          # dtype
+    assert f(*bad) == SPEC_E_DTYPE
+
+
+def test_commit_layers_host_checks(lib):
+    P = _buf()
+    f = lib.spec_kv_commit_layers
+    # k_layers, v_layers, k_tree, v_tree, num_layers, prefix_len, path, accept_len,
+    # B, n_max, Hkv, head_dim, L_cap, max_depth, dtype, dev_error, stream
+    args = [P, P, None, None, 4, P, P, P, 2, 0, 4, 16, 64, 5, 0, None, None]
+    assert f(*([None] + args[1:])) == SPEC_E_NULL
+    bad = list(args); bad[2] = P           # k_tree without v_tree
+    assert f(*bad) == SPEC_E_NULL
+    bad = list(args); bad[4] = 0           # no layers
+    assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[2], bad[3] = P, P  # scratch form needs n_max in [1, 64]
+    assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[13] = 64         # max_depth
+    assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[14] = 3          # dtype
     assert f(*bad) == SPEC_E_DTYPE

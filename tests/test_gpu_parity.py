@@ -13,8 +13,9 @@ import pytest
 import torch
 
 from eagle_tree_verification_amd.workloads import make_workload, small_cases, to_device
-from gpu_helpers import (compare_accept, compare_attention, compare_commit, kv_host, run_gpu_step,
-                         say)
+import oracle
+from gpu_helpers import (compare_accept, compare_attention, compare_commit, kv_host, oracle_accept,
+                         run_gpu_step, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -165,3 +166,102 @@ def test_accept_wait_bound_reports_sync(hip_lib, monkeypatch):
     host["ties"] = np.zeros(0, dtype=api.TIE_DTYPE)
     host["final_dist"] = None
     compare_accept(w, host)
+
+
+def _layer_setup(nl, seed):
+    """A ragged batch, its oracle walk, and nl per-layer caches and scratch
+    buffers (random storage patterns: the commit copies bytes)."""
+    import torch
+    w = make_workload(4, batch=6, prefix=(0, 150), vocab=2053, drafts=[60, 1, 0, 17, 33, 8],
+                      T=1.0, seed=seed, prefix_lens=[0, 1, 63, 64, 150, 97])
+    D = w.max_depth
+    path = np.full((w.B, D + 1), -1, dtype=np.int32)
+    acc = np.full(w.B, -1, dtype=np.int32)
+    for b in range(w.B):
+        r = oracle_accept(w, b)
+        acc[b] = r.accept_len
+        path[b, : r.accept_len + 1] = r.path
+    rng = np.random.default_rng(seed)
+    shape_c = w.k_cache.shape
+    shape_t = (w.B, w.Hkv, w.n_max, w.d)
+    kc = [rng.integers(0, 1 << 16, size=shape_c, dtype=np.uint16) for _ in range(nl)]
+    vc = [rng.integers(0, 1 << 16, size=shape_c, dtype=np.uint16) for _ in range(nl)]
+    kt = [rng.integers(0, 1 << 16, size=shape_t, dtype=np.uint16) for _ in range(nl)]
+    vt = [rng.integers(0, 1 << 16, size=shape_t, dtype=np.uint16) for _ in range(nl)]
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return w, path, acc, kc, vc, kt, vt, dev
+
+
+@pytest.mark.parametrize("scratch", [False, True], ids=["in-place", "scratch"])
+def test_commit_layers_parity(hip_lib, scratch):
+    import torch
+    from eagle_tree_verification_amd import api
+    nl = 5
+    w, path, acc, kc, vc, kt, vt, dev = _layer_setup(nl, 31)
+    say(f"[gpu] commit_layers {'scratch' if scratch else 'in-place'}: layers={nl} "
+        f"accept_len={acc.tolist()}")
+    kd, vd = [dev(a) for a in kc], [dev(a) for a in vc]
+    td = ([dev(a) for a in kt], [dev(a) for a in vt]) if scratch else (None, None)
+    plen = torch.from_numpy(w.prefix_len.copy()).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    api.kv_commit_layers(kd, vd, plen, torch.from_numpy(path).cuda(), torch.from_numpy(acc).cuda(),
+                         w.max_depth, k_tree=td[0], v_tree=td[1], dev_error=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    np.testing.assert_array_equal(plen.cpu().numpy(), w.prefix_len + acc + 1)
+    for l in range(nl):
+        kg = kd[l].view(torch.int16).cpu().numpy().view(np.uint16)
+        vg = vd[l].view(torch.int16).cpu().numpy().view(np.uint16)
+        for b in range(w.B):
+            a, L = int(acc[b]), int(w.prefix_len[b])
+            if scratch:
+                k2, v2, _ = oracle.kv_commit_from_buffer(kc[l][b], vc[l][b], kt[l][b], vt[l][b], L,
+                                                         path[b, : a + 1], a)
+            else:
+                k2, v2, _ = oracle.kv_commit(kc[l][b], vc[l][b], L, path[b, : a + 1], a)
+            np.testing.assert_array_equal(kg[b], k2)
+            np.testing.assert_array_equal(vg[b], v2)
+
+
+def test_commit_layers_bad_path_and_forms_agree(hip_lib):
+    import torch
+    from eagle_tree_verification_amd import api
+    nl = 3
+    w, path, acc, kc, vc, kt, vt, dev = _layer_setup(nl, 47)
+    b_bad = int(np.argmax(acc))
+    assert acc[b_bad] >= 1
+    bad = path.copy()
+    bad[b_bad, 1] = bad[b_bad, 0]  # not increasing
+    say(f"[gpu] commit_layers: corrupted path of sequence {b_bad}; scratch form on cache rows")
+    # scratch rows taken from the caches' own tree rows: both forms must agree
+    for l in range(nl):
+        for b in range(w.B):
+            L, n = int(w.prefix_len[b]), int(w.n_nodes[b])
+            kt[l][b, :, :n] = kc[l][b, :, L:L + n]
+            vt[l][b, :, :n] = vc[l][b, :, L:L + n]
+    outs = []
+    for use_scratch in (False, True):
+        kd, vd = [dev(a) for a in kc], [dev(a) for a in vc]
+        td = ([dev(a) for a in kt], [dev(a) for a in vt]) if use_scratch else (None, None)
+        plen = torch.from_numpy(w.prefix_len.copy()).cuda()
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        api.kv_commit_layers(kd, vd, plen, torch.from_numpy(bad).cuda(),
+                             torch.from_numpy(acc).cuda(), w.max_depth, k_tree=td[0],
+                             v_tree=td[1], dev_error=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) & api.DEVERR_TREE
+        lens = plen.cpu().numpy()
+        assert lens[b_bad] == w.prefix_len[b_bad]
+        ok = np.arange(w.B) != b_bad
+        np.testing.assert_array_equal(lens[ok], (w.prefix_len + acc + 1)[ok])
+        got = [(k.view(torch.int16).cpu().numpy(), v.view(torch.int16).cpu().numpy())
+               for k, v in zip(kd, vd)]
+        for l in range(nl):  # the failed sequence is untouched in every layer
+            np.testing.assert_array_equal(got[l][0][b_bad].view(np.uint16), kc[l][b_bad])
+            np.testing.assert_array_equal(got[l][1][b_bad].view(np.uint16), vc[l][b_bad])
+        outs.append((got, lens))
+    for l in range(nl):
+        for b in range(w.B):
+            rows = int(w.prefix_len[b]) + int(acc[b]) + 1
+            np.testing.assert_array_equal(outs[0][0][l][0][b][:, :rows], outs[1][0][l][0][b][:, :rows])
+            np.testing.assert_array_equal(outs[0][0][l][1][b][:, :rows], outs[1][0][l][1][b][:, :rows])
