@@ -141,6 +141,64 @@ def cpu_baseline(w, budget_s=12.0):
                       f"{dt:.1f} s on {cores} host threads"}
 
 
+def commit_layers_bench(w, dev, outs, plen0, layers, reps=20):
+    """The all-layer commit on this step's accepted paths, over `layers`
+    caches of the workload's shape, in place and from scratch rows.  Cache
+    contents are left as allocated: the commit moves bytes."""
+    import torch
+
+    from eagle_tree_verification_amd import api
+
+    kv_t = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+    s = 2 if w.kv_dtype == "bf16" else 4
+    shape = (w.B, w.Hkv, w.L_cap, w.d)
+    kl = [torch.empty(shape, dtype=kv_t, device="cuda") for _ in range(layers)]
+    vl = [torch.empty(shape, dtype=kv_t, device="cuda") for _ in range(layers)]
+    tshape = (w.B, w.Hkv, w.n_max, w.d)
+    kt = [torch.empty(tshape, dtype=kv_t, device="cuda") for _ in range(layers)]
+    vt = [torch.empty(tshape, dtype=kv_t, device="cuda") for _ in range(layers)]
+    acc = outs["accept_len"].cpu().numpy()
+    path = outs["path"].cpu().numpy()
+    row = w.Hkv * w.d * s * 2 * layers                    # K and V of one cache row, all layers
+    moved = sum(int(acc[b]) for b in range(w.B)
+                if acc[b] > 0 and any(int(path[b, i]) != i for i in range(acc[b] + 1)))
+    res = {"layers": layers}
+    for form, tree in (("in_place", (None, None)), ("scratch", (kt, vt))):
+        pl = plen0.clone()
+
+        def call():
+            pl.copy_(plen0)
+            return api.kv_commit_layers(kl, vl, pl, outs["path"], outs["accept_len"], w.max_depth,
+                                        k_tree=tree[0], v_tree=tree[1])
+        call()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            pl.copy_(plen0)
+            keep = api._pointer_table(kl, "k_layers"), api._pointer_table(vl, "v_layers")
+            tk = (api._pointer_table(kt, "k_tree"), api._pointer_table(vt, "v_tree")) \
+                if tree[0] is not None else (None, None)
+            torch.cuda.synchronize()
+            e0.record()
+            st = api.load().spec_kv_commit_layers(
+                api._ptr(keep[0]), api._ptr(keep[1]), api._ptr(tk[0]), api._ptr(tk[1]), layers,
+                api._ptr(pl), api._ptr(outs["path"]), api._ptr(outs["accept_len"]), w.B,
+                w.n_max if tree[0] is not None else 0, w.Hkv, w.d, w.L_cap, w.max_depth,
+                api.SPEC_BF16 if w.kv_dtype == "bf16" else api.SPEC_F32, None,
+                api._stream(None))
+            e1.record()
+            torch.cuda.synchronize()
+            if st != 0:
+                raise RuntimeError(f"spec_kv_commit_layers status {st}")
+            ms.append(e0.elapsed_time(e1))
+        t = float(np.median(ms))
+        nbytes = 2 * row * (moved if form == "in_place" else int((acc + 1).sum()))
+        res[form] = {"ms": round(t, 4), "algorithmic_bytes": nbytes,
+                     "GBps": round(nbytes / (t * 1e-3) / 1e9, 1)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,6 +206,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--commit-layers", type=int, default=32,
+                    help="also time spec_kv_commit_layers over this many layers (0: skip)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -273,6 +333,8 @@ def main():
         "ms_per_step_wall_incl_length_restore": round(wall / args.steps * 1e3, 4),
         "roofline": roof,
     }
+    if args.commit_layers > 0:
+        rec["commit_layers"] = commit_layers_bench(w, dev, outs, plen0, args.commit_layers)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)
