@@ -62,6 +62,12 @@ def load():
     lib.spec_kv_commit.restype = I
     lib.spec_kv_commit_layers.argtypes = [P, P, P, P, I, P, P, P, I, I, I, I, I, I, I, P, P]
     lib.spec_kv_commit_layers.restype = I
+    lib.spec_tree_state_size.argtypes = [I, I, I]
+    lib.spec_tree_state_size.restype = Z
+    lib.spec_tree_expand.argtypes = [P, I, P, I, I, I, I, I, P, Z, P, P, P, P]
+    lib.spec_tree_expand.restype = I
+    lib.spec_tree_finalize.argtypes = [P, Z, I, I, I, I, P, P, I, P, P, P, P, P, P, P, P, P, P]
+    lib.spec_tree_finalize.restype = I
     lib.spec_status_string.argtypes = [I]
     lib.spec_status_string.restype = ctypes.c_char_p
     lib.spec_abi_version.argtypes = []
@@ -267,3 +273,73 @@ def kv_commit_layers(k_layers, v_layers, prefix_len, path, accept_len, max_depth
                                    d, L_cap, int(max_depth), dt, _ptr(dev_error), _stream(stream))
     _check("spec_kv_commit_layers", st)
     return (kt, vt, tk, tv)
+
+
+def tree_state_size(B, top_k, depth):
+    return int(load().spec_tree_state_size(B, top_k, depth))
+
+
+def tree_state(B, top_k, depth, device):
+    """A state buffer for one tree per sequence (uninitialised device bytes)."""
+    n = tree_state_size(B, top_k, depth)
+    if n == 0:
+        raise ValueError("tree sizes out of range")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def tree_expand(draft_logits, state, level, top_k, depth, *, d2t=None, expanded_tokens=None,
+                expanded_ids=None, dev_error=None, stream=None):
+    """Grow level `level` (1-based) of every sequence's tree.
+
+    draft_logits: [B][R][Vd] float32 or bfloat16 (R = 1 at level 1, top_k
+    after).  Returns (expanded_tokens, expanded_ids), each [B][top_k] int32.
+    """
+    lib = load()
+    B, R, Vd = draft_logits.shape
+    dt = _kv_dtype(_dev(draft_logits, "draft_logits"))
+    if R != (1 if level == 1 else top_k):
+        raise ValueError(f"level {level} takes {1 if level == 1 else top_k} draft rows, got {R}")
+    _dev(state, "state", torch.uint8)
+    if d2t is not None:
+        _dev(d2t, "d2t", torch.int32)
+    dev = draft_logits.device
+    if expanded_tokens is None:
+        expanded_tokens = torch.empty((B, top_k), dtype=torch.int32, device=dev)
+    if expanded_ids is None:
+        expanded_ids = torch.empty((B, top_k), dtype=torch.int32, device=dev)
+    st = lib.spec_tree_expand(_ptr(draft_logits), dt, _ptr(d2t), B, Vd, int(top_k), int(depth),
+                              int(level), _ptr(state), state.numel(), _ptr(expanded_tokens),
+                              _ptr(expanded_ids), _ptr(dev_error), _stream(stream))
+    _check("spec_tree_expand", st)
+    return expanded_tokens, expanded_ids
+
+
+def tree_finalize(state, B, top_k, depth, total_tokens, n_max, *, root_token=None,
+                  prefix_len=None, dev_error=None, outputs=None, stream=None):
+    """Rerank and emit the trees; returns a dict of device tensors (tokens,
+    parents, n_nodes, depth, positions, anc_mask (int64 bit patterns),
+    draft_row, value)."""
+    lib = load()
+    _dev(state, "state", torch.uint8)
+    for t, nm in ((root_token, "root_token"), (prefix_len, "prefix_len")):
+        if t is not None:
+            _dev(t, nm, torch.int32)
+    dev = state.device
+    o = dict(outputs or {})
+    shapes = {"tokens": torch.int32, "parents": torch.int32, "depth": torch.int32,
+              "positions": torch.int32, "anc_mask": torch.int64, "draft_row": torch.int32,
+              "value": torch.float32}
+    for key, dtype in shapes.items():
+        if o.get(key) is None:
+            o[key] = torch.empty((B, n_max), dtype=dtype, device=dev)
+        _dev(o[key], key, dtype)
+    if o.get("n_nodes") is None:
+        o["n_nodes"] = torch.empty((B,), dtype=torch.int32, device=dev)
+    st = lib.spec_tree_finalize(_ptr(state), state.numel(), B, int(top_k), int(depth),
+                                int(total_tokens), _ptr(root_token), _ptr(prefix_len), int(n_max),
+                                _ptr(o["tokens"]), _ptr(o["parents"]), _ptr(o["n_nodes"]),
+                                _ptr(o["depth"]), _ptr(o["positions"]), _ptr(o["anc_mask"]),
+                                _ptr(o["draft_row"]), _ptr(o["value"]), _ptr(dev_error),
+                                _stream(stream))
+    _check("spec_tree_finalize", st)
+    return o

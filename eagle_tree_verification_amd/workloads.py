@@ -433,6 +433,63 @@ def small_cases():
     }
 
 
+@dataclass
+class TreeInputs:
+    """Draft outputs for building trees level by level (inputs only).
+
+    levels[l] holds the draft logits of level l + 1: [B][1][Vd] for the root
+    row, [B][top_k][Vd] afterwards (row r standing for the r-th node expanded
+    at the level before).  `store[l]` is the same in storage form (float32, or
+    bf16 bits as uint16); `levels[l]` is its exact float32 value.
+    """
+    B: int
+    top_k: int
+    depth: int
+    Vd: int
+    total_tokens: int
+    dtype: str
+    levels: list
+    store: list
+    d2t: Optional[np.ndarray]
+    root_token: np.ndarray
+    prefix_len: np.ndarray
+
+
+def make_tree_inputs(B, top_k, depth, Vd, total_tokens, *, dtype="f32", seed=0,
+                     logit_std=3.0, target_vocab=None, threads=None):
+    """Seeded draft logits ~ N(0, logit_std) for a tree of `depth` levels.
+
+    target_vocab: if given, d2t maps the Vd draft ids onto a sorted random
+    subset of range(target_vocab) (draft id i -> token i + d2t[i]), the shape
+    of an EAGLE-3 head with its own smaller vocabulary (page "EAGLE-1/2/3
+    拆解", section "代码里能直接读到的三处改动": 32000 draft ids into 128256).
+    """
+    ss = np.random.SeedSequence([2000, seed])
+    kids = ss.spawn(depth + 1)
+    aux = np.random.Generator(np.random.Philox(kids[depth]))
+
+    def one(lv):
+        rg = np.random.Generator(np.random.Philox(kids[lv]))
+        R = 1 if lv == 0 else top_k
+        x = rg.standard_normal(size=(B, R, Vd), dtype=np.float32) * np.float32(logit_std)
+        st = _to_storage(x, dtype)
+        val = bf16_bits_to_f32(st) if dtype == "bf16" else st
+        return val, st
+
+    workers = max(1, min(depth, threads or len(os.sched_getaffinity(0)), 16))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        out = list(ex.map(one, range(depth)))
+    d2t = None
+    if target_vocab is not None:
+        ids = np.sort(aux.choice(int(target_vocab), size=Vd, replace=False))
+        d2t = (ids - np.arange(Vd)).astype(np.int32)
+    root = aux.integers(0, target_vocab or Vd, size=B).astype(np.int32)
+    prefix = aux.integers(0, 4096, size=B).astype(np.int32)
+    return TreeInputs(B=B, top_k=top_k, depth=depth, Vd=Vd, total_tokens=total_tokens,
+                      dtype=dtype, levels=[o[0] for o in out], store=[o[1] for o in out],
+                      d2t=d2t, root_token=root, prefix_len=prefix)
+
+
 def to_device(w: Workload, device="cuda"):
     """Copy a workload's arrays into device tensors (dict keyed like the fields)."""
     import torch

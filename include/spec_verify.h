@@ -58,6 +58,8 @@ extern "C" {
 
 #define SPEC_ABI_VERSION 1
 #define SPEC_MAX_NODES 64
+#define SPEC_TREE_MAX_TOP_K 16  /* children per expanded node (tree construction) */
+#define SPEC_TREE_MAX_DEPTH 16  /* levels of a constructed tree                   */
 
 typedef int32_t spec_status_t;
 
@@ -252,6 +254,101 @@ spec_status_t spec_kv_commit_layers(
     const void* const* v_tree, int32_t num_layers, int32_t* prefix_len, const int32_t* path,
     const int32_t* accept_len, int32_t B, int32_t n_max, int32_t Hkv, int32_t head_dim,
     int32_t L_cap, int32_t max_depth, int32_t dtype, int32_t* dev_error, void* stream);
+
+/*
+ * Draft-tree construction (EAGLE-2), the step before verification
+ * ([GUIDE] "一个可核对的经验性质": a node's value is the product of the
+ * draft's confidences on its root path; the section on EAGLE-2's two stages:
+ * Expansion runs the draft, level by level, only on the top_k most valuable
+ * nodes of the level before, and Reranking sends the total_tokens most
+ * valuable nodes of the whole tree to verification; the paragraph on the
+ * papers' settings: 60/50/48 drafts, depth 6 (8 for EAGLE-3), 10 expanded
+ * per level; section "代码里能直接读到的三处改动": an EAGLE-3 draft head
+ * ranks its own vocabulary and draft id i is target token i + d2t[i]).
+ *
+ * Values are sums of float32 log-probabilities (log of the product of
+ * confidences); confidences are the draft's softmax probabilities.  The
+ * pool of one sequence holds, per level, the top_k children of each
+ * expanded node: level 1 has the root's top_k children (all expanded), level
+ * l >= 2 the top_k * top_k children of level l-1's expanded nodes, of which
+ * the top_k are expanded.  Pool order is (level, draft row, child rank);
+ * equal logits go to the lower draft id, equal values to the lower pool
+ * index.  Pool ids: level 1 holds 0..top_k-1, level l >= 2 holds
+ * top_k + (l-2)*top_k^2 + r*top_k + j for child rank j of draft row r.
+ *
+ * One tree per call sequence: spec_tree_expand for level 1, 2, ..., then
+ * spec_tree_finalize, all on one stream with one state buffer.
+ *
+ * spec_tree_state_size -- bytes of the state buffer (device memory owned by
+ *   the caller; 0 for arguments out of range).  It needs no initialisation:
+ *   a level-1 call starts a new tree on it.  It holds the pool between
+ *   calls, so trees in flight need one each.
+ */
+size_t spec_tree_state_size(int32_t B, int32_t top_k, int32_t depth);
+
+/*
+ * spec_tree_expand -- grow level `level` (1-based) of every sequence's tree.
+ *
+ *   draft_logits  [B][R][Vd], dtype SPEC_F32 or SPEC_BF16: R = 1 at level 1
+ *                 (the draft's output at the root), R = top_k afterwards, row
+ *                 r being the draft's output at the r-th node the previous
+ *                 call returned in expanded_ids
+ *   d2t           NULL, or [Vd] int32 offsets: a child's token is
+ *                 id + d2t[id] (not range-checked here)
+ *   B, Vd         1 <= B <= 65535; top_k <= Vd <= 16384 * min(64, 256/top_k)
+ *   top_k, depth  1 <= top_k <= SPEC_TREE_MAX_TOP_K,
+ *                 1 <= level <= depth <= SPEC_TREE_MAX_DEPTH (depth sizes
+ *                 the state and must be the same in every call on it)
+ *   state         >= spec_tree_state_size(B, top_k, depth) bytes
+ *   expanded_tokens (out) [B][top_k] int32: tokens of the nodes chosen for
+ *                 expansion, most valuable first (-1 for a failed sequence)
+ *   expanded_ids  (out, nullable) [B][top_k] int32: their pool ids; the
+ *                 parent of pool id p at level l >= 2 is the node of draft
+ *                 row (p - top_k - (l-2)*top_k^2) / top_k of that level
+ * Device errors: SPEC_DEVERR_NONFINITE (a NaN or +inf logit, or a row with
+ * no finite logit), SPEC_DEVERR_TREE (level l >= 2 called when level l-1 was
+ * not the last one grown on this state).  The sequence is then failed until
+ * its next level-1 call: later levels return -1 tokens, finalize gives it
+ * n_nodes = 0.
+ */
+spec_status_t spec_tree_expand(const void* draft_logits, int32_t dtype, const int32_t* d2t,
+                               int32_t B, int32_t Vd, int32_t top_k, int32_t depth,
+                               int32_t level, void* state, size_t state_bytes,
+                               int32_t* expanded_tokens, int32_t* expanded_ids,
+                               int32_t* dev_error, void* stream);
+
+/*
+ * spec_tree_finalize -- rerank: the total_tokens most valuable pool nodes
+ * (nodes of value -inf excluded) follow the root, node 0, in pool order, so
+ * parents precede children; the result is a tree in the format of
+ * spec_verify_tree_attn and spec_accept_tree.
+ *
+ *   total_tokens  drafts to keep, 1 <= total_tokens < SPEC_MAX_NODES
+ *   root_token    (nullable) [B] int32: written to tokens[b][0] (else -1)
+ *   prefix_len    (nullable) [B] int32: positions = prefix_len + depth
+ *                 (else depth)
+ *   n_max         row stride of the outputs, total_tokens < n_max <= 64
+ *   tokens, parents (out) [B][n_max] int32; parents[b][0] = -1
+ *   n_nodes       (out) [B] int32: 1 + drafts kept (0 for a failed sequence)
+ *   node_depth, positions, draft_row (out, nullable) [B][n_max] int32;
+ *                 draft_row is the expansion row whose draft output holds the
+ *                 node's children: 0 for the root, 1 + (l-1)*top_k + r for
+ *                 the r-th node expanded at level l < levels grown, -1 for a
+ *                 node without children
+ *   anc_mask      (out, nullable) [B][n_max] uint64: bit i of row j set iff i
+ *                 is j or an ancestor of j
+ *   value         (out, nullable) [B][n_max] float32: sum of log-probabilities
+ * Rows >= n_nodes[b] are not written.
+ * The state must have had a level-1 call since it was allocated.
+ * Device errors: SPEC_DEVERR_TREE (state not in a valid grown state).
+ */
+spec_status_t spec_tree_finalize(const void* state, size_t state_bytes, int32_t B,
+                                 int32_t top_k, int32_t depth, int32_t total_tokens,
+                                 const int32_t* root_token, const int32_t* prefix_len,
+                                 int32_t n_max, int32_t* tokens, int32_t* parents,
+                                 int32_t* n_nodes, int32_t* node_depth, int32_t* positions,
+                                 uint64_t* anc_mask, int32_t* draft_row, float* value,
+                                 int32_t* dev_error, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* spec_status_string(spec_status_t status);

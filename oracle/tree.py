@@ -67,8 +67,9 @@ def top_children(z, k):
     """The k most probable draft ids of row z, best first; ties to the lower
     id (reading T2).  Sorting by logit equals sorting by probability."""
     z = np.asarray(z, dtype=np.float64)
-    order = sorted(range(len(z)), key=lambda i: (-z[i], i))
-    return order[:k]
+    # lexsort: last key is primary -> by -z, then by id
+    order = np.lexsort((np.arange(len(z)), -z))
+    return [int(i) for i in order[:k]]
 
 
 class TreeBuilder:

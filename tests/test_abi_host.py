@@ -19,7 +19,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = api.declared_functions()
     assert set(names) == {"spec_verify_tree_attn", "spec_verify_tree_attn_workspace_size",
                           "spec_accept_tree", "spec_accept_tree_workspace_size", "spec_kv_commit",
-                          "spec_kv_commit_layers", "spec_status_string", "spec_abi_version"}
+                          "spec_kv_commit_layers", "spec_status_string", "spec_abi_version",
+                          "spec_tree_state_size", "spec_tree_expand", "spec_tree_finalize"}
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -97,3 +98,47 @@ def test_commit_layers_host_checks(lib):
     assert f(*bad) == SPEC_E_SHAPE
     bad = list(args); bad[14] = 3          # dtype
     assert f(*bad) == SPEC_E_DTYPE
+
+
+def test_tree_host_checks(lib):
+    P = _buf()
+    assert lib.spec_tree_state_size(0, 10, 8) == 0
+    assert lib.spec_tree_state_size(4, 17, 8) == 0
+    assert lib.spec_tree_state_size(4, 10, 17) == 0
+    nbytes = lib.spec_tree_state_size(4, 10, 8)
+    assert nbytes > 4 * (10 + 7 * 100) * 12
+    f = lib.spec_tree_expand
+    # draft_logits, dtype, d2t, B, Vd, top_k, depth, level, state, state_bytes,
+    # expanded_tokens, expanded_ids, dev_error, stream
+    args = [P, 0, None, 4, 1000, 10, 8, 2, P, nbytes, P, None, None, None]
+    assert f(*([None] + args[1:])) == SPEC_E_NULL
+    bad = list(args); bad[10] = None       # expanded_tokens
+    assert f(*bad) == SPEC_E_NULL
+    bad = list(args); bad[4] = 9           # Vd < top_k
+    assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[4] = 16384 * 25 + 1  # more splits than the state holds
+    assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[7] = 9           # level > depth
+    assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[7] = 0
+    assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[5] = 17
+    assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[1] = 2           # dtype
+    assert f(*bad) == SPEC_E_DTYPE
+    bad = list(args); bad[9] = nbytes - 1
+    assert f(*bad) == -5                   # SPEC_E_WORKSPACE
+    g = lib.spec_tree_finalize
+    # state, state_bytes, B, top_k, depth, total_tokens, root_token, prefix_len,
+    # n_max, tokens, parents, n_nodes, node_depth, positions, anc_mask,
+    # draft_row, value, dev_error, stream
+    args = [P, nbytes, 4, 10, 8, 60, None, None, 64, P, P, P] + [None] * 7
+    assert g(*([None] + args[1:])) == SPEC_E_NULL
+    bad = list(args); bad[8] = 60          # n_max must exceed total_tokens
+    assert g(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[5] = 64          # total_tokens < 64
+    assert g(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[5] = 0
+    assert g(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[1] = 100
+    assert g(*bad) == -5
