@@ -199,6 +199,70 @@ def commit_layers_bench(w, dev, outs, plen0, layers, reps=20):
     return res
 
 
+def tree_build_bench(B, top_k, depth, Vd, total, reps=20):
+    """EAGLE-2 tree construction at the workload's batch, tree budget and
+    vocabulary: `depth` calls of spec_tree_expand on seeded N(0, 3) draft
+    logits (a separate buffer per level) and one spec_tree_finalize, timed
+    with HIP events on the launch stream; per dtype of the draft logits."""
+    import torch
+
+    from eagle_tree_verification_amd import api
+
+    res = {"batch": B, "top_k": top_k, "depth": depth, "draft_vocab": Vd, "drafts": total}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    for name, tdt, s in (("bf16", torch.bfloat16, 2), ("f32", torch.float32, 4)):
+        levels = [(torch.randn((B, 1 if lv == 0 else top_k, Vd), generator=gen, device="cuda")
+                   * 3.0).to(tdt) for lv in range(depth)]
+        state = api.tree_state(B, top_k, depth, "cuda")
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        et = torch.empty((B, top_k), dtype=torch.int32, device="cuda")
+        ei = torch.empty((B, top_k), dtype=torch.int32, device="cuda")
+        n_max = total + 1
+        outs = {key: torch.empty((B, n_max), dtype=dt_, device="cuda")
+                for key, dt_ in (("tokens", torch.int32), ("parents", torch.int32),
+                                 ("depth", torch.int32), ("positions", torch.int32),
+                                 ("anc_mask", torch.int64), ("draft_row", torch.int32),
+                                 ("value", torch.float32))}
+        outs["n_nodes"] = torch.empty(B, dtype=torch.int32, device="cuda")
+
+        def build(ev=None):
+            for lv in range(depth):
+                api.tree_expand(levels[lv], state, lv + 1, top_k, depth, expanded_tokens=et,
+                                expanded_ids=ei, dev_error=err)
+                if ev:
+                    ev[lv + 1].record()
+            api.tree_finalize(state, B, top_k, depth, total, n_max, dev_error=err, outputs=outs)
+
+        build()
+        torch.cuda.synchronize()
+        tot, lev = [], []
+        for _ in range(reps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(depth + 2)]
+            ev[0].record()
+            build(ev)
+            ev[depth + 1].record()
+            torch.cuda.synchronize()
+            tot.append(ev[0].elapsed_time(ev[depth + 1]))
+            lev.append([ev[i].elapsed_time(ev[i + 1]) for i in range(1, depth)])
+        if int(err.item()) != 0:
+            raise RuntimeError(f"tree construction device error bits {int(err.item())}")
+        if (outs["n_nodes"] != total + 1).any():
+            raise RuntimeError("tree construction emitted a short tree")
+        t = float(np.median(tot))
+        t_lv = float(np.median(np.asarray(lev)))             # one full level (rows = top_k)
+        nbytes = B * Vd * s * (1 + (depth - 1) * top_k)       # every draft logit read once
+        lv_bytes = B * top_k * Vd * s
+        res[name] = {"ms": round(t, 4), "algorithmic_bytes": nbytes,
+                     "GBps": round(nbytes / (t * 1e-3) / 1e9, 1),
+                     "level_ms": round(t_lv, 4),
+                     "level_GBps": round(lv_bytes / (t_lv * 1e-3) / 1e9, 1),
+                     "level_frac_hbm_peak": round(lv_bytes / (t_lv * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        del levels, state
+        torch.cuda.synchronize()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,6 +272,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--commit-layers", type=int, default=32,
                     help="also time spec_kv_commit_layers over this many layers (0: skip)")
+    ap.add_argument("--no-tree-build", action="store_true",
+                    help="skip timing the EAGLE-2 tree construction")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -335,6 +401,8 @@ def main():
     }
     if args.commit_layers > 0:
         rec["commit_layers"] = commit_layers_bench(w, dev, outs, plen0, args.commit_layers)
+    if not args.no_tree_build:
+        rec["tree_build"] = tree_build_bench(w.B, 10, cfg.depth, w.V, cfg.drafts)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

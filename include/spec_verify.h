@@ -295,7 +295,7 @@ size_t spec_tree_state_size(int32_t B, int32_t top_k, int32_t depth);
  *                 call returned in expanded_ids
  *   d2t           NULL, or [Vd] int32 offsets: a child's token is
  *                 id + d2t[id] (not range-checked here)
- *   B, Vd         1 <= B <= 65535; top_k <= Vd <= 16384 * min(64, 256/top_k)
+ *   B, Vd         1 <= B <= 65535; top_k <= Vd <= 2^24
  *   top_k, depth  1 <= top_k <= SPEC_TREE_MAX_TOP_K,
  *                 1 <= level <= depth <= SPEC_TREE_MAX_DEPTH (depth sizes
  *                 the state and must be the same in every call on it)

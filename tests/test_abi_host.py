@@ -116,7 +116,7 @@ def test_tree_host_checks(lib):
     assert f(*bad) == SPEC_E_NULL
     bad = list(args); bad[4] = 9           # Vd < top_k
     assert f(*bad) == SPEC_E_SHAPE
-    bad = list(args); bad[4] = 16384 * 25 + 1  # more splits than the state holds
+    bad = list(args); bad[4] = (1 << 24) + 1  # vocabulary limit
     assert f(*bad) == SPEC_E_SHAPE
     bad = list(args); bad[7] = 9           # level > depth
     assert f(*bad) == SPEC_E_SHAPE
