@@ -199,6 +199,107 @@ def commit_layers_bench(w, dev, outs, plen0, layers, reps=20):
     return res
 
 
+def model_verify_bench(w, dev, outs, plen0, layers, ws_attn, ws_acc, reps=10):
+    """One verify step of a whole `layers`-layer model's tree part: per layer,
+    the tree's K/V written into that layer's cache with rotated keys
+    (spec_tree_kv_write) and the rotated-query tree attention over it
+    (spec_verify_tree_attn_rope); then the acceptance walk and the all-layer
+    commit.  Each layer has its own seeded cache, queries and new K/V (so no
+    layer finds another's data in cache).  Frequencies: base 500000 with the
+    lower half of the planes slowed 8x (a rescaled schedule)."""
+    import torch
+
+    from eagle_tree_verification_amd import api
+
+    kv_t = torch.bfloat16 if w.kv_dtype == "bf16" else torch.float32
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(777)
+    shape = (w.B, w.Hkv, w.L_cap, w.d)
+    kl = [torch.randn(shape, generator=gen, device="cuda").to(kv_t) for _ in range(layers)]
+    vl = [torch.randn(shape, generator=gen, device="cuda").to(kv_t) for _ in range(layers)]
+    ql = [torch.randn((w.B, w.n_max, w.Hq, w.d), generator=gen, device="cuda").to(kv_t)
+          for _ in range(layers)]
+    kn = [torch.randn((w.B, w.n_max, w.Hkv, w.d), generator=gen, device="cuda").to(kv_t)
+          for _ in range(layers)]
+    vn = [torch.randn((w.B, w.n_max, w.Hkv, w.d), generator=gen, device="cuda").to(kv_t)
+          for _ in range(layers)]
+    f = 500000.0 ** (-np.arange(w.d // 2) * 2.0 / w.d)
+    f[w.d // 4:] /= 8.0
+    inv_freq = torch.tensor(f, dtype=torch.float32, device="cuda")
+    out = torch.empty((w.B, w.n_max, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pl = plen0.clone()
+
+    def step(ev=None):
+        pl.copy_(plen0)
+        if ev:
+            ev[0].record()
+        for l in range(layers):
+            api.tree_kv_write(kn[l], vn[l], kl[l], vl[l], pl, dev["n_nodes"], dev["parents"],
+                              inv_freq=inv_freq, dev_error=err)
+            api.verify_tree_attn(ql[l], kl[l], vl[l], pl, dev["n_nodes"], dev["parents"], out=out,
+                                 workspace=ws_attn, dev_error=err, inv_freq=inv_freq)
+        if ev:
+            ev[1].record()
+        api.accept_tree(dev["tokens"], dev["parents"], dev["n_nodes"], dev["draft_p"],
+                        dev["logits"], w.T, dev["u_accept"], dev["u_sample"], w.max_depth,
+                        workspace=ws_acc, dev_error=err, outputs=outs)
+        if ev:
+            ev[2].record()
+        st = lib.spec_kv_commit_layers(
+            api._ptr(ktab), api._ptr(vtab), None, None, layers, api._ptr(pl),
+            api._ptr(outs["path"]), api._ptr(outs["accept_len"]), w.B, 0, w.Hkv, w.d, w.L_cap,
+            w.max_depth, api.SPEC_BF16 if w.kv_dtype == "bf16" else api.SPEC_F32,
+            api._ptr(err), api._stream(None))
+        if st != 0:
+            raise RuntimeError(f"spec_kv_commit_layers status {st}")
+        if ev:
+            ev[3].record()
+
+    lib = api.load()
+    ktab = api._pointer_table(kl, "k_layers")   # built once, outside the timed steps
+    vtab = api._pointer_table(vl, "v_layers")
+    step()
+    torch.cuda.synchronize()
+    rows = []
+    for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        step(ev)
+        torch.cuda.synchronize()
+        rows.append([ev[0].elapsed_time(ev[3]), ev[0].elapsed_time(ev[1]),
+                     ev[1].elapsed_time(ev[2]), ev[2].elapsed_time(ev[3])])
+    # the two per-layer calls alone (layer 0), for the breakdown
+    part = []
+    for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        api.tree_kv_write(kn[0], vn[0], kl[0], vl[0], pl, dev["n_nodes"], dev["parents"],
+                          inv_freq=inv_freq, dev_error=err)
+        ev[1].record()
+        api.verify_tree_attn(ql[0], kl[0], vl[0], pl, dev["n_nodes"], dev["parents"], out=out,
+                             workspace=ws_attn, dev_error=err, inv_freq=inv_freq)
+        ev[2].record()
+        torch.cuda.synchronize()
+        part.append([ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])])
+    t_kvw, t_attn = (float(x) for x in np.median(np.asarray(part), axis=0))
+    if int(err.item()) != 0:
+        raise RuntimeError(f"model verify device error bits {int(err.item())}")
+    t, t_layers, t_acc, t_com = (float(x) for x in np.median(np.asarray(rows), axis=0))
+    verified = w.verified_tokens
+    committed = int((outs["accept_len"].cpu().numpy() + 1).sum())
+    res = {"layers": layers, "rope": "half, base 500000, lower planes / 8",
+           "ms": round(t, 4), "layers_ms": round(t_layers, 4),
+           "per_layer_ms": round(t_layers / layers, 4),
+           "kv_write_ms": round(t_kvw, 4), "attn_rope_ms": round(t_attn, 4),
+           "accept_ms": round(t_acc, 4),
+           "commit_layers_ms": round(t_com, 4),
+           "verified_tokens_per_s": round(verified / (t * 1e-3), 1),
+           "committed_tokens_per_s": round(committed / (t * 1e-3), 1)}
+    del kl, vl, ql, kn, vn, ktab, vtab
+    torch.cuda.synchronize()
+    return res
+
+
 def tree_build_bench(B, top_k, depth, Vd, total, reps=20):
     """EAGLE-2 tree construction at the workload's batch, tree budget and
     vocabulary: `depth` calls of spec_tree_expand on seeded N(0, 3) draft
@@ -272,6 +373,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--commit-layers", type=int, default=32,
                     help="also time spec_kv_commit_layers over this many layers (0: skip)")
+    ap.add_argument("--model-layers", type=int, default=32,
+                    help="also time a whole model's verify step over this many layers, with "
+                         "rotary embedding (0: skip)")
     ap.add_argument("--no-tree-build", action="store_true",
                     help="skip timing the EAGLE-2 tree construction")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -401,6 +505,9 @@ def main():
     }
     if args.commit_layers > 0:
         rec["commit_layers"] = commit_layers_bench(w, dev, outs, plen0, args.commit_layers)
+    if args.model_layers > 0:
+        rec["model_verify"] = model_verify_bench(w, dev, outs, plen0, args.model_layers, ws_attn,
+                                                 ws_acc)
     if not args.no_tree_build:
         rec["tree_build"] = tree_build_bench(w.B, 10, cfg.depth, w.V, cfg.drafts)
     if not args.no_cpu_baseline:

@@ -62,6 +62,11 @@ def load():
     lib.spec_kv_commit.restype = I
     lib.spec_kv_commit_layers.argtypes = [P, P, P, P, I, P, P, P, I, I, I, I, I, I, I, P, P]
     lib.spec_kv_commit_layers.restype = I
+    lib.spec_verify_tree_attn_rope.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, I, P,
+                                               P, Z, P, P]
+    lib.spec_verify_tree_attn_rope.restype = I
+    lib.spec_tree_kv_write.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, I, P, P]
+    lib.spec_tree_kv_write.restype = I
     lib.spec_tree_state_size.argtypes = [I, I, I]
     lib.spec_tree_state_size.restype = Z
     lib.spec_tree_expand.argtypes = [P, I, P, I, I, I, I, I, P, Z, P, P, P, P]
@@ -125,9 +130,16 @@ def _workspace(nbytes, device, workspace):
     return workspace, workspace.numel() * workspace.element_size()
 
 
+ROPE_STYLES = {"half": 1, "interleaved": 2}
+
+
 def verify_tree_attn(q, k_cache, v_cache, prefix_len, n_nodes, parents, *, scale=None, out=None,
-                     workspace=None, dev_error=None, stream=None):
-    """Tree-masked attention; returns out [B][n_max][Hq][d] float32."""
+                     workspace=None, dev_error=None, stream=None, inv_freq=None,
+                     rope_style="half"):
+    """Tree-masked attention; returns out [B][n_max][Hq][d] float32.
+
+    With inv_freq ([d/2] float32 device tensor) the queries are rotated in
+    the kernel (spec_verify_tree_attn_rope)."""
     lib = load()
     B, n_max, Hq, d = q.shape
     _, Hkv, L_cap, _ = k_cache.shape
@@ -143,12 +155,44 @@ def verify_tree_attn(q, k_cache, v_cache, prefix_len, n_nodes, parents, *, scale
         scale = 1.0 / float(np.sqrt(d))
     ws, wsb = _workspace(verify_tree_attn_workspace_size(B, n_max, Hq, Hkv, d, L_cap, dt),
                          q.device, workspace)
-    st = lib.spec_verify_tree_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(prefix_len),
-                                   _ptr(n_nodes), _ptr(parents), B, n_max, Hq, Hkv, d, L_cap,
-                                   float(scale), dt, _ptr(out), _ptr(ws), wsb, _ptr(dev_error),
-                                   _stream(stream))
-    _check("spec_verify_tree_attn", st)
+    if inv_freq is None:
+        st = lib.spec_verify_tree_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(prefix_len),
+                                       _ptr(n_nodes), _ptr(parents), B, n_max, Hq, Hkv, d, L_cap,
+                                       float(scale), dt, _ptr(out), _ptr(ws), wsb,
+                                       _ptr(dev_error), _stream(stream))
+        _check("spec_verify_tree_attn", st)
+        return out
+    _dev(inv_freq, "inv_freq", torch.float32)
+    st = lib.spec_verify_tree_attn_rope(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(prefix_len),
+                                        _ptr(n_nodes), _ptr(parents), B, n_max, Hq, Hkv, d,
+                                        L_cap, float(scale), dt, _ptr(inv_freq),
+                                        ROPE_STYLES[rope_style], _ptr(out), _ptr(ws), wsb,
+                                        _ptr(dev_error), _stream(stream))
+    _check("spec_verify_tree_attn_rope", st)
     return out
+
+
+def tree_kv_write(k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, parents, *, inv_freq=None,
+                  rope_style="half", dev_error=None, stream=None):
+    """Write the tree's K (rotated when inv_freq is given) and V into the cache
+    rows prefix_len + j.  k_new, v_new: [B][n_max][Hkv][d]."""
+    lib = load()
+    B, Hkv, L_cap, d = k_cache.shape
+    n_max = k_new.shape[1]
+    dt = _kv_dtype(k_cache)
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, nm, k_cache.dtype)
+    if tuple(k_new.shape) != (B, n_max, Hkv, d) or tuple(v_new.shape) != (B, n_max, Hkv, d):
+        raise ValueError("k_new, v_new must be [B][n_max][Hkv][head_dim]")
+    for t, nm in ((prefix_len, "prefix_len"), (n_nodes, "n_nodes"), (parents, "parents")):
+        _dev(t, nm, torch.int32)
+    if inv_freq is not None:
+        _dev(inv_freq, "inv_freq", torch.float32)
+    st = lib.spec_tree_kv_write(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(prefix_len), _ptr(n_nodes), _ptr(parents), B, n_max, Hkv, d,
+                                L_cap, dt, _ptr(inv_freq), ROPE_STYLES[rope_style],
+                                _ptr(dev_error), _stream(stream))
+    _check("spec_tree_kv_write", st)
 
 
 def accept_tree(tokens, parents, n_nodes, draft_p, logits, temperature, u_accept, u_sample,

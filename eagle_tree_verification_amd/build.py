@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libspecverify.so")
-SOURCES = ["abi.hip", "attention.hip", "accept.hip", "commit.hip", "tree.hip"]
+SOURCES = ["abi.hip", "attention.hip", "accept.hip", "commit.hip", "tree.hip", "rope.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -71,7 +71,8 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ prefix_len, const int32_t* __restrict__ n_nodes,
     const int32_t* __restrict__ parents, int n_max, int Hq, int Hkv, int d, int L_cap,
-    float c, float* __restrict__ out, int32_t* dev_error) {
+    float c, const float* __restrict__ inv_freq, int rope, float* __restrict__ out,
+    int32_t* dev_error) {
   __shared__ uint64_t anc[64];
   __shared__ int flag;
   __shared__ int rows[64];
@@ -106,6 +107,20 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
   const T* qrow = q + (((size_t)b * n_max + i) * Hq + h) * d;
   for (int k = lane; k < d; k += 64) qs[k] = load_as_f32(qrow + k);
   __syncthreads();
+  if (rope) {  // rotate the query at prefix_len + depth(i), in float32
+    const int pos = L + __popcll(a) - 1;
+    const int half = d / 2;
+    for (int t = lane; t < half; t += 64) {
+      const int ia = rope == kRopeInterleaved ? 2 * t : t;
+      const int ib = rope == kRopeInterleaved ? 2 * t + 1 : t + half;
+      float cs, sn;
+      rope_cs(pos, inv_freq[t], &cs, &sn);
+      const float x = qs[ia], y = qs[ib];
+      qs[ia] = x * cs - y * sn;
+      qs[ib] = y * cs + x * sn;
+    }
+    __syncthreads();
+  }
 
   const T* kb = kc + ((size_t)b * Hkv + g) * (size_t)L_cap * d;
   const T* vb = vc + ((size_t)b * Hkv + g) * (size_t)L_cap * d;
@@ -172,6 +187,8 @@ struct MfmaArgs {
   int units;   // B * Hkv * S_max
   int sort;    // map units to sequences longest prefix first
   float c;     // scale * log2(e)
+  const float* inv_freq;  // rotary frequencies [HD/2], or null
+  int rope;               // 0: none; kRopeHalf or kRopeInterleaved
   float* out;
   float* part_o;     // [B*Hkv][RB*RPW][S_max][HD]
   float2* part_ml;   // [B*Hkv][RB*RPW][S_max]  (running max, running sum)
@@ -267,6 +284,36 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
       qf[nb][ks] = valid ? *reinterpret_cast<const bf16x8_t*>(qp + ks * 16) : bf16x8_t{};
+    if (a.rope && valid) {
+      // Rotary embedding of the query at prefix_len + depth(i), rounded back
+      // to bf16.  The lane holds dims 16*ks + 8*lh + e: the pair (t, t + 64)
+      // of the half layout is (qf[ks][e], qf[ks + 4][e]); the pair (2t, 2t+1)
+      // of the interleaved layout is (qf[ks][e], qf[ks][e + 1]).
+      const int pos = L + __popcll(anc_r[nb]) - 1;
+      if (a.rope == kRopeHalf) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float cs, sn;
+            rope_cs(pos, a.inv_freq[16 * ks + 8 * lh + e], &cs, &sn);
+            const float x = (float)qf[nb][ks][e], y = (float)qf[nb][ks + 4][e];
+            qf[nb][ks][e] = (__bf16)(x * cs - y * sn);
+            qf[nb][ks + 4][e] = (__bf16)(y * cs + x * sn);
+          }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            float cs, sn;
+            rope_cs(pos, a.inv_freq[(16 * ks + 8 * lh + e) >> 1], &cs, &sn);
+            const float x = (float)qf[nb][ks][e], y = (float)qf[nb][ks][e + 1];
+            qf[nb][ks][e] = (__bf16)(x * cs - y * sn);
+            qf[nb][ks][e + 1] = (__bf16)(y * cs + x * sn);
+          }
+      }
+    }
   }
 
   f32x16_t o[NB][4];
@@ -597,11 +644,14 @@ extern "C" size_t spec_verify_tree_attn_workspace_size(int32_t B, int32_t n_max,
   return make_plan(B, n_max, Hq, Hkv, head_dim, L_cap, dtype).ws;
 }
 
-extern "C" spec_status_t spec_verify_tree_attn(
-    const void* q, const void* k_cache, const void* v_cache, const int32_t* prefix_len,
-    const int32_t* n_nodes, const int32_t* parents, int32_t B, int32_t n_max, int32_t Hq,
-    int32_t Hkv, int32_t head_dim, int32_t L_cap, float scale, int32_t dtype, float* out,
-    void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream) {
+namespace {
+spec_status_t launch_attn(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* prefix_len, const int32_t* n_nodes,
+                          const int32_t* parents, int32_t B, int32_t n_max, int32_t Hq,
+                          int32_t Hkv, int32_t head_dim, int32_t L_cap, float scale,
+                          int32_t dtype, const float* inv_freq, int rope, float* out,
+                          void* workspace, size_t workspace_bytes, int32_t* dev_error,
+                          void* stream) {
   spec_status_t st = check_args(q, k_cache, v_cache, prefix_len, n_nodes, parents, B, n_max, Hq,
                                 Hkv, head_dim, L_cap, scale, dtype, out);
   if (st != SPEC_OK) return st;
@@ -614,12 +664,12 @@ extern "C" spec_status_t spec_verify_tree_attn(
       hipLaunchKernelGGL(attn_valu_kernel<float>, grid, dim3(64), 0, strm,
                          static_cast<const float*>(q), static_cast<const float*>(k_cache),
                          static_cast<const float*>(v_cache), prefix_len, n_nodes, parents, n_max,
-                         Hq, Hkv, head_dim, L_cap, c, out, dev_error);
+                         Hq, Hkv, head_dim, L_cap, c, inv_freq, rope, out, dev_error);
     } else {
       hipLaunchKernelGGL(attn_valu_kernel<uint16_t>, grid, dim3(64), 0, strm,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                          static_cast<const uint16_t*>(v_cache), prefix_len, n_nodes, parents, n_max,
-                         Hq, Hkv, head_dim, L_cap, c, out, dev_error);
+                         Hq, Hkv, head_dim, L_cap, c, inv_freq, rope, out, dev_error);
     }
     SPEC_HIP_TRY(hipGetLastError());
     return SPEC_OK;
@@ -636,6 +686,8 @@ extern "C" spec_status_t spec_verify_tree_attn(
   a.B = B; a.n_max = n_max; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.L_cap = L_cap;
   a.RB = p.rb; a.S_max = p.S_max; a.chunk = p.chunk; a.units = p.units; a.sort = p.sort;
   a.c = c;
+  a.inv_freq = inv_freq;
+  a.rope = rope;
   a.out = out;
   a.dev_error = dev_error;
   a.part_o = nullptr;
@@ -664,4 +716,28 @@ extern "C" spec_status_t spec_verify_tree_attn(
     SPEC_HIP_TRY(hipGetLastError());
   }
   return SPEC_OK;
+}
+}  // namespace
+
+extern "C" spec_status_t spec_verify_tree_attn(
+    const void* q, const void* k_cache, const void* v_cache, const int32_t* prefix_len,
+    const int32_t* n_nodes, const int32_t* parents, int32_t B, int32_t n_max, int32_t Hq,
+    int32_t Hkv, int32_t head_dim, int32_t L_cap, float scale, int32_t dtype, float* out,
+    void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream) {
+  return launch_attn(q, k_cache, v_cache, prefix_len, n_nodes, parents, B, n_max, Hq, Hkv,
+                     head_dim, L_cap, scale, dtype, nullptr, 0, out, workspace, workspace_bytes,
+                     dev_error, stream);
+}
+
+extern "C" spec_status_t spec_verify_tree_attn_rope(
+    const void* q, const void* k_cache, const void* v_cache, const int32_t* prefix_len,
+    const int32_t* n_nodes, const int32_t* parents, int32_t B, int32_t n_max, int32_t Hq,
+    int32_t Hkv, int32_t head_dim, int32_t L_cap, float scale, int32_t dtype,
+    const float* inv_freq, int32_t rope_style, float* out, void* workspace,
+    size_t workspace_bytes, int32_t* dev_error, void* stream) {
+  if (!inv_freq) return SPEC_E_NULL;
+  if (rope_style != kRopeHalf && rope_style != kRopeInterleaved) return SPEC_E_VALUE;
+  return launch_attn(q, k_cache, v_cache, prefix_len, n_nodes, parents, B, n_max, Hq, Hkv,
+                     head_dim, L_cap, scale, dtype, inv_freq, rope_style, out, workspace,
+                     workspace_bytes, dev_error, stream);
 }

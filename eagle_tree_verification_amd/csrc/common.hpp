@@ -40,6 +40,23 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Rotary embedding: cosine and sine of pos * f.  The angle is formed and
+// reduced to [-1/2, 1/2] revolutions in float64, so a position in the
+// millions keeps float32 accuracy; the hardware sine and cosine
+// (v_sin_f32 / v_cos_f32, which take revolutions) finish it.
+__device__ __forceinline__ void rope_cs(int pos, float f, float* c, float* s) {
+  constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
+  double r = (double)pos * (double)f * kInvTwoPi;
+  r -= rint(r);
+  const float rf = (float)r;
+  *s = __builtin_amdgcn_sinf(rf);
+  *c = __builtin_amdgcn_cosf(rf);
+}
+
+// Rotary pair layouts: 1 = dimension i with i + d/2, 2 = dimension 2i with 2i + 1.
+constexpr int kRopeHalf = 1;
+constexpr int kRopeInterleaved = 2;
+
 __device__ __forceinline__ void report(int32_t* dev_error, int bits) {
   if (dev_error) atomicOr(dev_error, bits);
 }

@@ -133,6 +133,59 @@ size_t spec_verify_tree_attn_workspace_size(
     int32_t dtype);
 
 /*
+ * spec_verify_tree_attn_rope -- spec_verify_tree_attn with the rotary
+ * position embedding of the queries fused in: q holds the queries before
+ * rotation, and query row (b, i) is rotated at position prefix_len[b] +
+ * depth(i) before the contraction (the draft candidates of one level share a
+ * position: [GUIDE], the init_tree passage, where a level's position ids
+ * start as zeros).  The rotation is the published rotary embedding: plane t
+ * of the head dimension turns by pos * inv_freq[t].  The cache holds keys
+ * already rotated (spec_tree_kv_write writes the tree's rows that way).
+ *
+ *   inv_freq    [head_dim/2] float32 device array (any frequency schedule,
+ *               e.g. base^(-2t/head_dim) or a rescaled one)
+ *   rope_style  1: plane t pairs dimensions t and t + head_dim/2 (the
+ *               LLaMA-family layout); 2: dimensions 2t and 2t + 1
+ * On the matrix-core path the rotated query is rounded to bf16, as a query
+ * rotated by the caller would be; on the vector path it stays float32.
+ * Other arguments, outputs and errors as spec_verify_tree_attn; a NULL
+ * inv_freq is SPEC_E_NULL and another rope_style SPEC_E_VALUE.
+ */
+spec_status_t spec_verify_tree_attn_rope(
+    const void* q, const void* k_cache, const void* v_cache, const int32_t* prefix_len,
+    const int32_t* n_nodes, const int32_t* parents, int32_t B, int32_t n_max, int32_t Hq,
+    int32_t Hkv, int32_t head_dim, int32_t L_cap, float scale, int32_t dtype,
+    const float* inv_freq, int32_t rope_style, float* out, void* workspace,
+    size_t workspace_bytes, int32_t* dev_error, void* stream);
+
+/*
+ * spec_tree_kv_write -- the verify pass's write of the tree's keys and values
+ * into the cache, keys rotated ([LESSON] "KV cache 回滚": the verify pass
+ * extends the cache by the tree's rows; positions as for
+ * spec_verify_tree_attn_rope).  For every sequence b and node j <
+ * n_nodes[b], cache row prefix_len[b] + j of every KV head receives
+ * k_new[b][j][h] rotated at position prefix_len[b] + depth(j) (unrotated if
+ * inv_freq is NULL) and v_new[b][j][h].  Other cache rows are not touched.
+ *
+ *   k_new, v_new      [B][n_max][Hkv][head_dim], dtype (must not overlap the
+ *                     cache)
+ *   k_cache, v_cache  [B][Hkv][L_cap][head_dim], dtype (in/out)
+ *   prefix_len, n_nodes, parents   as for spec_verify_tree_attn
+ *   head_dim          even, <= 1024
+ *   inv_freq, rope_style           as for spec_verify_tree_attn_rope, or
+ *                     inv_freq NULL (rope_style ignored)
+ * bf16 results are rounded to nearest even.
+ * Device errors: SPEC_DEVERR_TREE, SPEC_DEVERR_CAPACITY (the sequence is not
+ * written).
+ */
+spec_status_t spec_tree_kv_write(const void* k_new, const void* v_new, void* k_cache,
+                                 void* v_cache, const int32_t* prefix_len,
+                                 const int32_t* n_nodes, const int32_t* parents, int32_t B,
+                                 int32_t n_max, int32_t Hkv, int32_t head_dim, int32_t L_cap,
+                                 int32_t dtype, const float* inv_freq, int32_t rope_style,
+                                 int32_t* dev_error, void* stream);
+
+/*
  * spec_accept_tree -- the acceptance walk ([LESSON] "不变量：Leviathan 拒绝
  * 采样" and build steps 1-3; [GUIDE] prefix property of tree acceptance).
  *

@@ -20,7 +20,8 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(names) == {"spec_verify_tree_attn", "spec_verify_tree_attn_workspace_size",
                           "spec_accept_tree", "spec_accept_tree_workspace_size", "spec_kv_commit",
                           "spec_kv_commit_layers", "spec_status_string", "spec_abi_version",
-                          "spec_tree_state_size", "spec_tree_expand", "spec_tree_finalize"}
+                          "spec_tree_state_size", "spec_tree_expand", "spec_tree_finalize",
+                          "spec_verify_tree_attn_rope", "spec_tree_kv_write"}
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -142,3 +143,30 @@ def test_tree_host_checks(lib):
     assert g(*bad) == SPEC_E_SHAPE
     bad = list(args); bad[1] = 100
     assert g(*bad) == -5
+
+
+def test_rope_host_checks(lib):
+    P = _buf()
+    f = lib.spec_verify_tree_attn_rope
+    # q, k, v, prefix_len, n_nodes, parents, B, n_max, Hq, Hkv, d, L_cap, scale, dtype,
+    # inv_freq, rope_style, out, workspace, ws_bytes, dev_error, stream
+    args = [P] * 6 + [1, 6, 4, 4, 16, 64, 0.25, 0, P, 1, P, None, 0, None, None]
+    bad = list(args); bad[14] = None       # inv_freq
+    assert f(*bad) == SPEC_E_NULL
+    bad = list(args); bad[15] = 3          # rope_style
+    assert f(*bad) == SPEC_E_VALUE
+    bad = list(args); bad[7] = 65
+    assert f(*bad) == SPEC_E_SHAPE
+    g = lib.spec_tree_kv_write
+    # k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, parents, B, n_max, Hkv, d,
+    # L_cap, dtype, inv_freq, rope_style, dev_error, stream
+    args = [P] * 7 + [2, 6, 4, 16, 64, 0, P, 1, None, None]
+    assert g(*([None] + args[1:])) == SPEC_E_NULL
+    bad = list(args); bad[10] = 15         # odd head_dim
+    assert g(*bad) == SPEC_E_DTYPE
+    bad = list(args); bad[11] = 5          # L_cap < n_max
+    assert g(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[14] = 0          # rope_style with inv_freq
+    assert g(*bad) == SPEC_E_VALUE
+    bad = list(args); bad[12] = 2
+    assert g(*bad) == SPEC_E_DTYPE

@@ -1,0 +1,204 @@
+"""GPU parity of the rotary position embedding of tree nodes:
+spec_tree_kv_write (keys rotated into the cache) and spec_verify_tree_attn_rope
+(queries rotated inside the attention kernel), against the oracle
+(oracle/rope.py with oracle/attention.py).
+
+Keys written to a bf16 cache must equal the oracle's float64 rotation within
+one bf16 rounding (2^-8 relative) plus 2e-6; an f32 cache within 2e-6 (the
+angle is reduced in float64, the hardware sine and cosine err by about 1e-7).
+Attention outputs: 2e-2 absolute for bf16, 1e-5 for f32, the verify path's
+bars.  Rows outside the tree's rows stay bit-identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import rope as orope
+from eagle_tree_verification_amd.workloads import (make_workload, small_cases, storage_to_f64,
+                                                   to_device, _to_storage)
+from gpu_helpers import ATOL, SENTINEL, say
+
+pytestmark = pytest.mark.gpu
+
+
+def inv_freq(d, base, scale_low=1.0):
+    """A frequency schedule: base^(-2t/d), the lower half optionally divided
+    by scale_low (a rescaled schedule, as long-context models use)."""
+    f = base ** (-np.arange(d // 2) * 2.0 / d)
+    f[d // 4:] /= scale_low
+    return f.astype(np.float32)
+
+
+def _kv_new(w, seed):
+    rng = np.random.default_rng(seed)
+    shape = (w.B, w.n_max, w.Hkv, w.d)
+    kn = rng.standard_normal(size=shape, dtype=np.float32)
+    vn = rng.standard_normal(size=shape, dtype=np.float32)
+    return _to_storage(kn, w.kv_dtype), _to_storage(vn, w.kv_dtype)
+
+
+def _dev(arr, kv_dtype):
+    t = torch.from_numpy(np.ascontiguousarray(arr))
+    if kv_dtype == "bf16":
+        return t.view(torch.int16).to("cuda").view(torch.bfloat16)
+    return t.to("cuda")
+
+
+def _host(t, kv_dtype):
+    if kv_dtype == "bf16":
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def _key_tol(kv_dtype, ref):
+    return (2.0 ** -8) * np.abs(ref) + 2e-6 if kv_dtype == "bf16" else 2e-6
+
+
+CASES = ["c1-t1", "c2-mini", "c3-mini-t1", "c4-mini", "c5-mini"]
+
+
+@pytest.mark.parametrize("style", ["half", "interleaved"])
+@pytest.mark.parametrize("name", CASES)
+def test_rope_write_and_attention(hip_lib, name, style):
+    api = hip_lib
+    w = make_workload(poison=True, **small_cases()[name])
+    f = inv_freq(w.d, 500000.0 if w.kv_dtype == "bf16" else 10000.0, scale_low=8.0)
+    say(f"[gpu] rope {name} {style}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} {w.kv_dtype} "
+        f"L={w.prefix_len.tolist()} n={w.n_nodes.tolist()}")
+    kn, vn = _kv_new(w, 99)
+    dev = to_device(w)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fdev = torch.from_numpy(f).to("cuda")
+    api.tree_kv_write(_dev(kn, w.kv_dtype), _dev(vn, w.kv_dtype), dev["k_cache"], dev["v_cache"],
+                      dev["prefix_len"], dev["n_nodes"], dev["parents"], inv_freq=fdev,
+                      rope_style=style, dev_error=err)
+    out = torch.full((w.B, w.n_max, w.Hq, w.d), SENTINEL, dtype=torch.float32, device="cuda")
+    api.verify_tree_attn(dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"],
+                         dev["n_nodes"], dev["parents"], out=out, dev_error=err, inv_freq=fdev,
+                         rope_style=style)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    kc = _host(dev["k_cache"], w.kv_dtype)
+    vc = _host(dev["v_cache"], w.kv_dtype)
+    attn = out.cpu().numpy()
+    worst_k = worst_a = 0.0
+    for b in range(w.B):
+        n, L = int(w.n_nodes[b]), int(w.prefix_len[b])
+        par = w.parents[b, :n]
+        k0 = storage_to_f64(w.k_cache[b], w.kv_dtype)
+        v0 = storage_to_f64(w.v_cache[b], w.kv_dtype)
+        k2, v2 = orope.tree_kv_write(k0, v0, storage_to_f64(kn[b], w.kv_dtype),
+                                     storage_to_f64(vn[b], w.kv_dtype), L, par, n, f, style)
+        # the tree's rows: rotated keys, copied values; every other row unchanged
+        got_k = storage_to_f64(kc[b], w.kv_dtype)
+        dk = np.abs(got_k[:, L:L + n] - k2[:, L:L + n])
+        worst_k = max(worst_k, float(dk.max()))
+        assert np.all(dk <= _key_tol(w.kv_dtype, k2[:, L:L + n]))
+        np.testing.assert_array_equal(kc[b][:, :L], w.k_cache[b][:, :L])
+        np.testing.assert_array_equal(kc[b][:, L + n:], w.k_cache[b][:, L + n:])
+        np.testing.assert_array_equal(vc[b][:, :L], w.v_cache[b][:, :L])
+        np.testing.assert_array_equal(vc[b][:, L:L + n], np.transpose(vn[b][:n], (1, 0, 2)))
+        # attention over the written cache with the rotated queries
+        pos = orope.node_positions(par, n, L)
+        q = orope.rope_rotate(w.q_f64(b), pos[:, None], f, style)
+        ref = oracle.tree_attention(q, got_k[:, :L + n], storage_to_f64(vc[b][:, :L + n], w.kv_dtype),
+                                    L, par, scale=w.scale)
+        d = np.abs(attn[b, :n].astype(np.float64) - ref).max()
+        worst_a = max(worst_a, float(d))
+        assert d <= ATOL[w.kv_dtype], (b, d)
+        assert np.all(attn[b, n:] == SENTINEL)
+    say(f"[gpu]   max|key diff|={worst_k:.3g} max|attn diff|={worst_a:.3g}")
+
+
+def test_rope_position_zero_and_unrotated_write(hip_lib):
+    """Without frequencies the write is a plain copy; with frequencies all
+    zero (position-independent angle 0) the rotated entry point equals the
+    plain one bit for bit."""
+    api = hip_lib
+    w = make_workload(poison=True, **small_cases()["c4-mini"])
+    kn, vn = _kv_new(w, 7)
+    dev = to_device(w)
+    api.tree_kv_write(_dev(kn, w.kv_dtype), _dev(vn, w.kv_dtype), dev["k_cache"], dev["v_cache"],
+                      dev["prefix_len"], dev["n_nodes"], dev["parents"])
+    torch.cuda.synchronize()
+    kc = _host(dev["k_cache"], w.kv_dtype)
+    for b in range(w.B):
+        n, L = int(w.n_nodes[b]), int(w.prefix_len[b])
+        np.testing.assert_array_equal(kc[b][:, L:L + n], np.transpose(kn[b][:n], (1, 0, 2)))
+    zero = torch.zeros(w.d // 2, dtype=torch.float32, device="cuda")
+    a = api.verify_tree_attn(dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"],
+                             dev["n_nodes"], dev["parents"])
+    b_ = api.verify_tree_attn(dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"],
+                              dev["n_nodes"], dev["parents"], inv_freq=zero)
+    torch.cuda.synchronize()
+    for b in range(w.B):
+        n = int(w.n_nodes[b])
+        assert torch.equal(a[b, :n], b_[b, :n])
+
+
+def test_rope_write_errors(hip_lib):
+    api = hip_lib
+    w = make_workload(poison=True, **small_cases()["c4-mini"])
+    kn, vn = _kv_new(w, 3)
+    dev = to_device(w)
+    par = dev["parents"].clone()
+    par[1, 2] = 5                     # parent after its child
+    plen = dev["prefix_len"].clone()
+    plen[3] = w.L_cap - 1             # tree does not fit
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    before = _host(dev["k_cache"], w.kv_dtype).copy()
+    f = torch.from_numpy(inv_freq(w.d, 10000.0)).to("cuda")
+    api.tree_kv_write(_dev(kn, w.kv_dtype), _dev(vn, w.kv_dtype), dev["k_cache"], dev["v_cache"],
+                      plen, dev["n_nodes"], par, inv_freq=f, dev_error=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == api.DEVERR_TREE | api.DEVERR_CAPACITY
+    after = _host(dev["k_cache"], w.kv_dtype)
+    np.testing.assert_array_equal(after[1], before[1])
+    np.testing.assert_array_equal(after[3], before[3])
+    assert not np.array_equal(after[0], before[0])
+
+
+@pytest.mark.timeout(900)
+def test_rope_full_size_serving(hip_lib):
+    """Batch 64 (config 4 shape) with the rotated path, sampled against the
+    oracle: the longest and shortest prefix and a random sequence, root,
+    last and random nodes, edge and random heads."""
+    api = hip_lib
+    w = make_workload(4)
+    f = inv_freq(w.d, 500000.0, scale_low=8.0)
+    kn, vn = _kv_new(w, 4)
+    dev = to_device(w)
+    fdev = torch.from_numpy(f).to("cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    api.tree_kv_write(_dev(kn, w.kv_dtype), _dev(vn, w.kv_dtype), dev["k_cache"], dev["v_cache"],
+                      dev["prefix_len"], dev["n_nodes"], dev["parents"], inv_freq=fdev,
+                      dev_error=err)
+    out = torch.full((w.B, w.n_max, w.Hq, w.d), SENTINEL, dtype=torch.float32, device="cuda")
+    api.verify_tree_attn(dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"],
+                         dev["n_nodes"], dev["parents"], out=out, dev_error=err, inv_freq=fdev)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    attn = out.cpu().numpy()
+    assert np.isfinite(attn[:, 0]).all()
+    rng = np.random.default_rng(0)
+    seqs = sorted({int(np.argmax(w.prefix_len)), int(np.argmin(w.prefix_len)),
+                   int(rng.integers(w.B))})
+    for b in seqs:
+        n, L = int(w.n_nodes[b]), int(w.prefix_len[b])
+        par = w.parents[b, :n]
+        kc_b = storage_to_f64(_host(dev["k_cache"][b:b + 1], w.kv_dtype)[0][:, :L + n], "bf16")
+        vc_b = storage_to_f64(_host(dev["v_cache"][b:b + 1], w.kv_dtype)[0][:, :L + n], "bf16")
+        nodes = sorted({0, n - 1, int(rng.integers(n))})
+        heads = sorted({0, w.Hq - 1, int(rng.integers(w.Hq))})
+        pos = orope.node_positions(par, n, L)
+        q = orope.rope_rotate(w.q_f64(b), pos[:, None], f, "half")
+        ref = oracle.tree_attention(q, kc_b, vc_b, L, par, scale=w.scale, nodes=nodes, heads=heads)
+        for i in nodes:
+            for h in heads:
+                d = np.abs(attn[b, i, h].astype(np.float64) - ref[i, h]).max()
+                assert d <= ATOL["bf16"], (b, i, h, d)
+        k2, _ = orope.tree_kv_write(np.zeros((w.Hkv, L + n, w.d)), np.zeros((w.Hkv, L + n, w.d)),
+                                    storage_to_f64(kn[b], "bf16"), storage_to_f64(vn[b], "bf16"),
+                                    L, par, n, f, "half")
+        assert np.all(np.abs(kc_b[:, L:] - k2[:, L:]) <= _key_tol("bf16", k2[:, L:]))
