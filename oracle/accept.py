@@ -105,6 +105,27 @@ class AcceptResult:
     error: int = 0
 
 
+def draft_p_to_target(p_draft, d2t, V):
+    """A draft distribution over the draft head's own vocabulary, moved onto
+    the target vocabulary.
+
+    Page "EAGLE-1/2/3 拆解", section "代码里能直接读到的三处改动": an EAGLE-3
+    draft head ranks its own (smaller) vocabulary and draft id i stands for
+    target token i + d2t[i].  So p(i + d2t[i]) = p_draft(i), and p is 0 on
+    target tokens no draft id maps to (a child with such a token has draft
+    probability 0, which the rule accepts).  p_draft: [..., Vd].  Returns None
+    when the map is not one-to-one into [0, V) (reported as ERR_TOKEN).
+    """
+    d2t = np.asarray(d2t, dtype=np.int64)
+    tgt = np.arange(len(d2t)) + d2t
+    if (tgt < 0).any() or (tgt >= V).any() or len(np.unique(tgt)) != len(tgt):
+        return None
+    p_draft = np.asarray(p_draft, dtype=np.float64)
+    out = np.zeros(p_draft.shape[:-1] + (V,))
+    out[..., tgt] = p_draft
+    return out
+
+
 def _fail(err):
     return AcceptResult(-1, [], [], None, [], False, err)
 

@@ -441,3 +441,38 @@ def test_invalid_inputs_are_flagged():
     p2 = p.copy(); p2[0] = 0.5 / (V - 1); p2[0, 1] = 0.5  # ratio 0.25 at the root's child
     r = oracle.accept_tree([0, 1, 2], [-1, 0, 1], 3, p2, bad, 1.0, [0, HI, HI], z, 4)
     assert r.error == 0 and r.accept_len == 0
+
+
+# ----------------------------------------------------------------------------
+# draft head with its own vocabulary (d2t map)
+# ----------------------------------------------------------------------------
+def test_draft_vocab_map_by_hand():
+    # draft ids 0, 1, 2 stand for target tokens 0 + 0, 1 + 1, 2 + 2
+    p = oracle.draft_p_to_target([0.5, 0.3, 0.2], [0, 1, 2], 6)
+    np.testing.assert_array_equal(p, [0.5, 0.0, 0.3, 0.0, 0.2, 0.0])
+    # draft id 0 -> target 3, draft id 1 -> target 0, per row
+    rows = oracle.draft_p_to_target([[0.1, 0.9], [0.6, 0.4]], [3, -1], 4)
+    np.testing.assert_array_equal(rows, [[0.9, 0.0, 0.0, 0.1], [0.4, 0.0, 0.0, 0.6]])
+    assert oracle.draft_p_to_target([0.5, 0.5], [1, 0], 4) is None      # both map to 1
+    assert oracle.draft_p_to_target([0.5, 0.5], [0, 3], 4) is None      # 1 + 3 = 4 >= V
+    assert oracle.draft_p_to_target([0.5, 0.5], [-1, 0], 4) is None     # 0 - 1 < 0
+
+
+@pytest.mark.parametrize("K", [1, 2, 3])
+def test_enumeration_with_a_draft_vocabulary(K):
+    """Drafts come from a 3-id draft vocabulary mapped into 5 target tokens
+    (two tokens can never be drafted): the first emitted token is still
+    exactly q, at every tree width."""
+    V, Vd = 5, 3
+    d2t = [0, 1, 1]            # draft ids 0, 1, 2 -> targets 0, 2, 3
+    rng = np.random.default_rng(40 + K)
+    table = {}
+
+    def pd(ctx):
+        if ctx not in table:
+            table[ctx] = rng.dirichlet(np.full(Vd, 0.8))
+        return oracle.draft_p_to_target(table[ctx], d2t, V)
+
+    qf, _ = _dists(V, 300 + K)
+    P1, _ = _tree_marginals(V, [-1] + [0] * K, qf, pd)
+    np.testing.assert_allclose(P1, qf(()), rtol=0, atol=1e-12)
