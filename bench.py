@@ -199,6 +199,66 @@ def commit_layers_bench(w, dev, outs, plen0, layers, reps=20):
     return res
 
 
+def accept_variants_bench(w, dev, reps=20):
+    """The walk's input variants at the workload's shape: per-sequence
+    temperatures (seeded from {0, 0.8, 1, 1.5}), and draft rows over a
+    32000-id draft vocabulary mapped into the target one (EAGLE-3's shape:
+    a sorted seeded subset, rows restricted and renormalised, children
+    redrawn from their parent's draft row).  Each is timed with the plain
+    call on the same inputs beside it."""
+    import torch
+
+    from eagle_tree_verification_amd import api
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(99)
+    temps = torch.tensor([0.0, 0.8, 1.0, 1.5], device="cuda")[
+        torch.randint(0, 4, (w.B,), generator=gen, device="cuda")]
+    Vd = min(32000, w.V)
+    ids = torch.sort(torch.randperm(w.V, generator=gen, device="cuda")[:Vd]).values
+    d2t = (ids - torch.arange(Vd, device="cuda")).to(torch.int32)
+    pd = dev["draft_p"][:, :, ids]
+    pd = (pd / pd.sum(-1, keepdim=True).clamp_min(1e-30)).contiguous()
+    par = dev["parents"].long().clamp_min(0)
+    rows = torch.gather(pd, 1, par[:, :, None].expand(-1, -1, Vd)).reshape(-1, Vd)
+    draw = torch.multinomial(rows.nan_to_num(0.0).clamp_min(0) + 1e-30, 1, generator=gen)
+    tokens = dev["tokens"].clone()
+    child = torch.arange(w.n_max, device="cuda")[None, :] >= 1
+    tokens = torch.where(child, ids[draw.reshape(w.B, w.n_max)].to(torch.int32), tokens)
+    full = torch.zeros_like(dev["draft_p"])
+    full[:, :, ids] = pd
+    ws = torch.empty(api.accept_tree_ex_workspace_size(w.B, w.n_max, w.V, Vd), dtype=torch.uint8,
+                     device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return round(float(np.median(ms)), 4)
+
+    def walk(draft_p, toks, **kw):
+        return lambda: api.accept_tree(toks, dev["parents"], dev["n_nodes"], draft_p,
+                                       dev["logits"], w.T, dev["u_accept"], dev["u_sample"],
+                                       w.max_depth, workspace=ws, dev_error=err, **kw)
+    res = {"draft_vocab": Vd,
+           "scalar_T_ms": timed(walk(dev["draft_p"], dev["tokens"])),
+           "per_seq_T_ms": timed(walk(dev["draft_p"], dev["tokens"], temperatures=temps)),
+           "expanded_rows_ms": timed(walk(full, tokens)),
+           "draft_vocab_ms": timed(walk(pd, tokens, d2t=d2t))}
+    if int(err.item()) != 0:
+        raise RuntimeError(f"walk variants device error bits {int(err.item())}")
+    del full, pd, rows
+    return res
+
+
 def model_verify_bench(w, dev, outs, plen0, layers, ws_attn, ws_acc, reps=10):
     """One verify step of a whole `layers`-layer model's tree part: per layer,
     the tree's K/V written into that layer's cache with rotated keys
@@ -376,6 +436,8 @@ def main():
     ap.add_argument("--model-layers", type=int, default=32,
                     help="also time a whole model's verify step over this many layers, with "
                          "rotary embedding (0: skip)")
+    ap.add_argument("--no-walk-variants", action="store_true",
+                    help="skip timing the walk with per-sequence temperatures and a draft vocabulary")
     ap.add_argument("--no-tree-build", action="store_true",
                     help="skip timing the EAGLE-2 tree construction")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -505,6 +567,8 @@ def main():
     }
     if args.commit_layers > 0:
         rec["commit_layers"] = commit_layers_bench(w, dev, outs, plen0, args.commit_layers)
+    if not args.no_walk_variants:
+        rec["walk_variants"] = accept_variants_bench(w, dev)
     if args.model_layers > 0:
         rec["model_verify"] = model_verify_bench(w, dev, outs, plen0, args.model_layers, ws_attn,
                                                  ws_acc)

@@ -58,6 +58,11 @@ def load():
     lib.spec_accept_tree.restype = I
     lib.spec_accept_tree_workspace_size.argtypes = [I, I, I]
     lib.spec_accept_tree_workspace_size.restype = Z
+    lib.spec_accept_tree_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, P, P, I, P, P, P, P, P, P,
+                                        P, P, I, P, P, Z, P, P]
+    lib.spec_accept_tree_ex.restype = I
+    lib.spec_accept_tree_ex_workspace_size.argtypes = [I, I, I, I]
+    lib.spec_accept_tree_ex_workspace_size.restype = Z
     lib.spec_kv_commit.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P]
     lib.spec_kv_commit.restype = I
     lib.spec_kv_commit_layers.argtypes = [P, P, P, P, I, P, P, P, I, I, I, I, I, I, I, P, P]
@@ -197,15 +202,24 @@ def tree_kv_write(k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, parents, 
 
 def accept_tree(tokens, parents, n_nodes, draft_p, logits, temperature, u_accept, u_sample,
                 max_depth, *, final_dist=False, tie_cap=0, workspace=None, dev_error=None,
-                outputs=None, stream=None):
+                outputs=None, stream=None, temperatures=None, d2t=None):
     """Acceptance walk; returns a dict of device tensors.
 
     Keys: accept_len [B], path [B][max_depth+1], out_tokens [B][max_depth+1],
     n_out [B], final_dist [B][V] or None, tie_log (uint8 bytes of tie_cap
     spec_tie_t records) or None, tie_count [1] or None.
+
+    temperatures ([B] float32 device tensor) gives each sequence its own
+    temperature; d2t ([Vd] int32 device tensor) means draft_p rows hold the
+    draft vocabulary's Vd entries (spec_accept_tree_ex).
     """
     lib = load()
     B, n_max, V = logits.shape
+    Vd = 0 if d2t is None else int(d2t.numel())
+    if temperatures is not None or d2t is not None:
+        return _accept_tree_ex(lib, tokens, parents, n_nodes, draft_p, logits, temperature,
+                               u_accept, u_sample, max_depth, final_dist, tie_cap, workspace,
+                               dev_error, outputs, stream, temperatures, d2t, B, n_max, V, Vd)
     dev = logits.device
     for t, nm in ((tokens, "tokens"), (parents, "parents"), (n_nodes, "n_nodes")):
         _dev(t, nm, torch.int32)
@@ -232,6 +246,50 @@ def accept_tree(tokens, parents, n_nodes, draft_p, logits, temperature, u_accept
                               _ptr(nout), _ptr(fd), _ptr(tlog), int(tie_cap), _ptr(tcount),
                               _ptr(ws), wsb, _ptr(dev_error), _stream(stream))
     _check("spec_accept_tree", st)
+    return {"accept_len": acc, "path": path, "out_tokens": toks, "n_out": nout,
+            "final_dist": fd, "tie_log": tlog, "tie_count": tcount}
+
+
+def accept_tree_ex_workspace_size(B, n_max, V, Vd):
+    return int(load().spec_accept_tree_ex_workspace_size(B, n_max, V, Vd))
+
+
+def _accept_tree_ex(lib, tokens, parents, n_nodes, draft_p, logits, temperature, u_accept,
+                    u_sample, max_depth, final_dist, tie_cap, workspace, dev_error, outputs,
+                    stream, temperatures, d2t, B, n_max, V, Vd):
+    dev = logits.device
+    for t, nm in ((tokens, "tokens"), (parents, "parents"), (n_nodes, "n_nodes")):
+        _dev(t, nm, torch.int32)
+    for t, nm in ((draft_p, "draft_p"), (logits, "logits"), (u_accept, "u_accept"),
+                  (u_sample, "u_sample")):
+        _dev(t, nm, torch.float32)
+    if temperatures is not None:
+        _dev(temperatures, "temperatures", torch.float32)
+    if d2t is not None:
+        _dev(d2t, "d2t", torch.int32)
+    if tuple(draft_p.shape) != (B, n_max, Vd if d2t is not None else V):
+        raise ValueError("draft_p must be [B][n_max][Vd] with d2t, [B][n_max][V] without")
+    o = outputs or {}
+
+    def _out(key, shape):
+        t = o.get(key)
+        return torch.empty(shape, dtype=torch.int32, device=dev) if t is None else _dev(t, key, torch.int32)
+
+    acc = _out("accept_len", (B,))
+    path = _out("path", (B, max_depth + 1))
+    toks = _out("out_tokens", (B, max_depth + 1))
+    nout = _out("n_out", (B,))
+    fd = torch.empty((B, V), dtype=torch.float32, device=dev) if final_dist else None
+    tlog = torch.zeros(max(tie_cap, 1) * TIE_DTYPE.itemsize, dtype=torch.uint8, device=dev) if tie_cap else None
+    tcount = torch.zeros(1, dtype=torch.int32, device=dev) if tie_cap else None
+    ws, wsb = _workspace(accept_tree_ex_workspace_size(B, n_max, V, Vd), dev, workspace)
+    st = lib.spec_accept_tree_ex(_ptr(tokens), _ptr(parents), _ptr(n_nodes), _ptr(draft_p),
+                                 _ptr(logits), B, n_max, V, int(max_depth), float(temperature),
+                                 _ptr(temperatures), _ptr(d2t), Vd, _ptr(u_accept),
+                                 _ptr(u_sample), _ptr(acc), _ptr(path), _ptr(toks), _ptr(nout),
+                                 _ptr(fd), _ptr(tlog), int(tie_cap), _ptr(tcount), _ptr(ws), wsb,
+                                 _ptr(dev_error), _stream(stream))
+    _check("spec_accept_tree_ex", st)
     return {"accept_len": acc, "path": path, "out_tokens": toks, "n_out": nout,
             "final_dist": fd, "tie_log": tlog, "tie_count": tcount}
 

@@ -117,6 +117,10 @@ struct AcceptArgs {
   const float* logits;
   int B, n_max, V, max_depth, greedy;
   double inv_T;
+  const float* temps;       // per-sequence temperatures, or null (inv_T / greedy apply)
+  const int32_t* t2d;       // target -> draft id (-1: none), when p is over a draft vocabulary
+  const int32_t* t2d_bad;   // nonzero when the draft map is not one-to-one into [0, V)
+  int pstride;              // entries per draft_p row (V, or the draft vocabulary size)
   const float* u_accept;
   const float* u_sample;
   int32_t* accept_len;
@@ -370,6 +374,35 @@ __device__ __forceinline__ void load_group(const float* row, int lo, int hi, int
   }
 }
 
+// Group g of a draft row held over a draft vocabulary: target entry i reads
+// p_draft[t2d[i]], or 0 when no draft id maps to i.
+template <int W>
+__device__ __forceinline__ void load_group_mapped(const float* row, const int32_t* t2d, int lo,
+                                                  int hi, int g, float fill, float* x) {
+  const int i = elem_index<W>(lo, g * W);
+  if (W == 4) {
+    if (i < hi) {
+      const int4 t = *reinterpret_cast<const int4*>(t2d + i);
+      x[0] = t.x >= 0 ? row[t.x] : 0.f;
+      x[1] = t.y >= 0 ? row[t.y] : 0.f;
+      x[2] = t.z >= 0 ? row[t.z] : 0.f;
+      x[3] = t.w >= 0 ? row[t.w] : 0.f;
+    } else {
+      x[0] = x[1] = x[2] = x[3] = fill;
+    }
+  } else {
+    const int t = i < hi ? t2d[i] : -1;
+    x[0] = i < hi ? (t >= 0 ? row[t] : 0.f) : fill;
+  }
+}
+
+template <int W, bool MAPPED>
+__device__ __forceinline__ void load_group_p(const float* row, const int32_t* t2d, int lo, int hi,
+                                             int g, float fill, float* x) {
+  if constexpr (MAPPED) load_group_mapped<W>(row, t2d, lo, hi, g, fill, x);
+  else load_group<W>(row, lo, hi, g, fill, x);
+}
+
 template <int W, int BG>
 __device__ __forceinline__ void load_batch(const float* row, int lo, int hi, int g0, float fill,
                                            float (*xv)[W]) {
@@ -381,25 +414,30 @@ __device__ __forceinline__ void load_batch(const float* row, int lo, int hi, int
 // `body(g0, x, y)`, BG groups at a time, with the next batch's loads issued
 // before the current batch is processed.  Groups past the slice read as fill
 // and touch no memory.
-template <int NG, int W, int BG, bool R2, typename F>
+template <int NG, int W, int BG, bool R2, bool MAPPED = false, typename F>
 __device__ __forceinline__ void stream_slice(const float* r1, float f1, const float* r2, float f2,
-                                             int lo, int hi, F body) {
+                                             int lo, int hi, F body,
+                                             const int32_t* t2d = nullptr) {
   float xa[BG][W], xb[BG][W], ya[BG][W], yb[BG][W];
+  auto load2 = [&](int g0, float (*y)[W]) {
+#pragma unroll
+    for (int gb = 0; gb < BG; ++gb) load_group_p<W, MAPPED>(r2, t2d, lo, hi, g0 + gb, f2, y[gb]);
+  };
   load_batch<W, BG>(r1, lo, hi, 0, f1, xa);
-  if (R2) load_batch<W, BG>(r2, lo, hi, 0, f2, ya);
+  if (R2) load2(0, ya);
 #pragma unroll 1
   for (int g0 = 0; g0 < NG; g0 += 2 * BG) {
     load_batch<W, BG>(r1, lo, hi, g0 + BG, f1, xb);
-    if (R2) load_batch<W, BG>(r2, lo, hi, g0 + BG, f2, yb);
+    if (R2) load2(g0 + BG, yb);
     body(g0, xa, ya);
     if (g0 + BG >= NG) break;
     load_batch<W, BG>(r1, lo, hi, g0 + 2 * BG, f1, xa);
-    if (R2) load_batch<W, BG>(r2, lo, hi, g0 + 2 * BG, f2, ya);
+    if (R2) load2(g0 + 2 * BG, ya);
     body(g0 + BG, xb, yb);
   }
 }
 
-template <int NG, int W>
+template <int NG, int W, bool MAPPED>
 __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   // groups loaded together: four in the one-row passes, two when the
   // residual pass streams logits and draft rows side by side
@@ -434,7 +472,18 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   // ---- validation (identical in every workgroup of the sequence) ----------
   const int n = a.n_nodes[b];
   int err = 0;
-  if (n < 1 || n > a.n_max) {
+  bool greedy = a.greedy;
+  double invT = a.inv_T;
+  if (a.temps) {  // this sequence's temperature
+    const float T = a.temps[b];
+    if (!(T >= 0.f) || !isfinite(T)) err = SPEC_DEVERR_NONFINITE;
+    greedy = T == 0.f;
+    invT = greedy ? 0.0 : 1.0 / (double)T;
+  }
+  if (MAPPED && *a.t2d_bad) err = SPEC_DEVERR_TOKEN;
+  if (err) {
+    // a bad temperature or draft map: nothing else is checked
+  } else if (n < 1 || n > a.n_max) {
     err = SPEC_DEVERR_TREE;
   } else {
     int bad_tree = 0, bad_tok = 0;
@@ -472,14 +521,13 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   int gen = 0;
   int v = 0, depth = 0;
   if (tid == 0) s_path[0] = 0;
-  const double invT = a.inv_T;
   const size_t rows_b = (size_t)b * a.n_max;
 
   for (;;) {
     const float* lrow = a.logits + (rows_b + v) * (size_t)a.V;
-    const float* prow = a.draft_p + (rows_b + v) * (size_t)a.V;
+    const float* prow = a.draft_p + (rows_b + v) * (size_t)a.pstride;
 
-    if (a.greedy) {
+    if (greedy) {
       float bv = -INFINITY;
       int bi = 0x7fffffff, nf = 0;
       stream_slice<NG, W, BG1, false>(lrow, -INFINITY, lrow, 0.f, lo, hi,
@@ -544,7 +592,12 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
     float k_p = 0.f, k_l = 0.f, k_u = 0.f, k_us = 0.f;
     if (kid) {
       const int xt = s_tok[tid];
-      k_p = prow[xt];
+      if constexpr (MAPPED) {
+        const int dx = a.t2d[xt];
+        k_p = dx >= 0 ? prow[dx] : 0.f;
+      } else {
+        k_p = prow[xt];
+      }
       k_l = lrow[xt];
       k_u = a.u_accept[rows_b + tid];
     }
@@ -607,7 +660,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       float xv[W], pv[W];
       load_group<W>(lrow, lo, hi, g, -INFINITY, xv);
       if (use_p) {
-        load_group<W>(prow, lo, hi, g, 0.f, pv);
+        load_group_p<W, MAPPED>(prow, a.t2d, lo, hi, g, 0.f, pv);
       } else {
 #pragma unroll
         for (int j = 0; j < W; ++j) pv[j] = 0.f;
@@ -651,7 +704,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       double zp = 0.0;
       int pnf = 0;
       const double CnS = Cn * S;
-      stream_slice<NG, W, BG2, true>(lrow, -INFINITY, prow, 0.f, lo, hi,
+      stream_slice<NG, W, BG2, true, MAPPED>(lrow, -INFINITY, prow, 0.f, lo, hi,
           [&](int, float (*xv)[W], float (*pv)[W]) {
 #pragma unroll
             for (int gb = 0; gb < BG2; ++gb)
@@ -661,7 +714,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
                 const double e = exp_tab(fma((double)xv[gb][j], invT, -M), s_tab);
                 zp += fmax(0.0, e - CnS * (double)pv[gb][j]);
               }
-          });
+          }, a.t2d);
       pnf = block_or(pnf, &s_or);
       zp = block_sum(zp, red);
       if (!exchange(a, bl, part, gen, zp, (double)pnf, xs, &s_or)) {
@@ -838,23 +891,47 @@ uint64_t next_epoch() {
 
 typedef void (*accept_fn)(AcceptArgs);
 
-accept_fn pick_kernel(int w, int ng) {
+template <bool MAPPED>
+accept_fn pick_variant(int w, int ng) {
   if (w == 4) {
     switch (ng) {
-      case 1: return accept_kernel<1, 4>;
-      case 2: return accept_kernel<2, 4>;
-      case 4: return accept_kernel<4, 4>;
-      case 8: return accept_kernel<8, 4>;
-      default: return accept_kernel<16, 4>;
+      case 1: return accept_kernel<1, 4, MAPPED>;
+      case 2: return accept_kernel<2, 4, MAPPED>;
+      case 4: return accept_kernel<4, 4, MAPPED>;
+      case 8: return accept_kernel<8, 4, MAPPED>;
+      default: return accept_kernel<16, 4, MAPPED>;
     }
   }
   switch (ng) {
-    case 1: return accept_kernel<1, 1>;
-    case 2: return accept_kernel<2, 1>;
-    case 4: return accept_kernel<4, 1>;
-    case 8: return accept_kernel<8, 1>;
-    default: return accept_kernel<16, 1>;
+    case 1: return accept_kernel<1, 1, MAPPED>;
+    case 2: return accept_kernel<2, 1, MAPPED>;
+    case 4: return accept_kernel<4, 1, MAPPED>;
+    case 8: return accept_kernel<8, 1, MAPPED>;
+    default: return accept_kernel<16, 1, MAPPED>;
   }
+}
+
+accept_fn pick_kernel(int w, int ng, bool mapped = false) {
+  return mapped ? pick_variant<true>(w, ng) : pick_variant<false>(w, ng);
+}
+
+// Inverse of a draft-vocabulary map: t2d[x] = i where x = i + d2t[i], -1 for
+// target tokens no draft id maps to; *bad set when the map leaves [0, V) or
+// is not one-to-one.  Two launches: fill, then scatter.
+__global__ void t2d_fill_kernel(int32_t* t2d, int V, int32_t* bad) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < V) t2d[i] = -1;
+  if (i == 0) *bad = 0;
+}
+__global__ void t2d_scatter_kernel(const int32_t* d2t, int Vd, int V, int32_t* t2d, int32_t* bad) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= Vd) return;
+  const long x = (long)i + d2t[i];
+  if (x < 0 || x >= V) {
+    atomicOr(bad, 1);
+    return;
+  }
+  if (atomicCAS(t2d + x, -1, i) != -1) atomicOr(bad, 1);
 }
 
 // Groups per thread are capped so the sample scan's [NG][NT] float64 table
@@ -871,19 +948,20 @@ struct AcceptPlan {
 
 // Workgroups of the (W, NG) variant one compute unit holds at once, cached
 // (relaxed atomics: concurrent first calls store the same value).
-int resident_per_cu(int w, int ng) {
-  static std::atomic<int> cache[2][5];
+int resident_per_cu(int w, int ng, bool mapped) {
+  static std::atomic<int> cache[2][2][5];
   const int wi = w == 4 ? 1 : 0;
+  const int mi = mapped ? 1 : 0;
   int ni = 0;
   while ((1 << ni) < ng) ++ni;
-  const int c = cache[wi][ni].load(std::memory_order_relaxed);
+  const int c = cache[mi][wi][ni].load(std::memory_order_relaxed);
   if (c > 0) return c;
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(pick_kernel(w, ng)), NT, 0) != hipSuccess)
+          &per_cu, reinterpret_cast<const void*>(pick_kernel(w, ng, mapped)), NT, 0) != hipSuccess)
     per_cu = 1;
   if (per_cu < 1) per_cu = 1;
-  cache[wi][ni].store(per_cu, std::memory_order_relaxed);
+  cache[mi][wi][ni].store(per_cu, std::memory_order_relaxed);
   return per_cu;
 }
 
@@ -892,7 +970,7 @@ int resident_per_cu(int w, int ng) {
 // are all resident at once, so the whole batch walks in one launch; beyond
 // that (very large batches) the fewest workgroups per
 // sequence, walked in consecutive groups of sequences.
-AcceptPlan make_accept_plan(int B, int V) {
+AcceptPlan make_accept_plan(int B, int V, bool mapped = false) {
   AcceptPlan p;
   p.W = (V % 4) == 0 ? 4 : 1;
   const long per_group = (long)NT * p.W;
@@ -911,7 +989,7 @@ AcceptPlan make_accept_plan(int B, int V) {
     for (int ng = 1; ng <= kMaxNG; ng *= 2) {
       const long kp = (V + per_group * ng - 1) / (per_group * ng);
       if (kp > SPEC_MAX_NODES) continue;
-      if ((long)B * kp <= (long)resident_per_cu(p.W, ng) * cus) {
+      if ((long)B * kp <= (long)resident_per_cu(p.W, ng, mapped) * cus) {
         best_ng = ng;
         break;
       }
@@ -921,6 +999,7 @@ AcceptPlan make_accept_plan(int B, int V) {
   p.chunk = (int)(per_group * best_ng);
   p.KP = (V + p.chunk - 1) / p.chunk;
   p.ws = p.KP > 1 ? (size_t)B * 2 * p.KP * 8 * sizeof(uint64_t) : 256;
+  if (mapped) p.ws = ((p.ws + 255) & ~(size_t)255) + (size_t)V * sizeof(int32_t) + 256;
   return p;
 }
 
@@ -935,23 +1014,33 @@ extern "C" size_t spec_accept_tree_workspace_size(int32_t B, int32_t n_max, int3
   return make_accept_plan(B, V).ws;
 }
 
-extern "C" spec_status_t spec_accept_tree(
+extern "C" size_t spec_accept_tree_ex_workspace_size(int32_t B, int32_t n_max, int32_t V,
+                                                     int32_t Vd) {
+  if (B <= 0 || n_max <= 0 || V <= 0 || Vd < 0 || Vd > V) return 0;
+  (void)n_max;
+  return make_accept_plan(B, V, Vd > 0).ws;
+}
+
+extern "C" spec_status_t spec_accept_tree_ex(
     const int32_t* tokens, const int32_t* parents, const int32_t* n_nodes, const float* draft_p,
     const float* logits, int32_t B, int32_t n_max, int32_t V, int32_t max_depth,
-    float temperature, const float* u_accept, const float* u_sample, int32_t* accept_len,
-    int32_t* path, int32_t* out_tokens, int32_t* n_out, float* final_dist, spec_tie_t* tie_log,
-    int32_t tie_cap, int32_t* tie_count, void* workspace, size_t workspace_bytes,
-    int32_t* dev_error, void* stream) {
+    float temperature, const float* temperatures, const int32_t* d2t, int32_t Vd,
+    const float* u_accept, const float* u_sample, int32_t* accept_len, int32_t* path,
+    int32_t* out_tokens, int32_t* n_out, float* final_dist, spec_tie_t* tie_log, int32_t tie_cap,
+    int32_t* tie_count, void* workspace, size_t workspace_bytes, int32_t* dev_error,
+    void* stream) {
   if (!tokens || !parents || !n_nodes || !draft_p || !logits || !u_accept || !u_sample ||
       !accept_len || !path || !out_tokens || !n_out)
     return SPEC_E_NULL;
+  const bool mapped = d2t != nullptr;
+  if (mapped && (Vd <= 0 || Vd > V)) return SPEC_E_SHAPE;
   if (tie_log && !tie_count) return SPEC_E_NULL;
   if (B <= 0 || n_max <= 0 || n_max > SPEC_MAX_NODES || V <= 0 ||
       V > SPEC_MAX_NODES * NT * kMaxNG * (V % 4 == 0 ? 4 : 1) || max_depth < 0 || max_depth >= SPEC_MAX_NODES ||
       (tie_log && tie_cap < 0))
     return SPEC_E_SHAPE;
-  if (!(temperature >= 0.f) || !isfinite(temperature)) return SPEC_E_VALUE;
-  AcceptPlan p = make_accept_plan(B, V);
+  if (!temperatures && (!(temperature >= 0.f) || !isfinite(temperature))) return SPEC_E_VALUE;
+  AcceptPlan p = make_accept_plan(B, V, mapped);
   if (p.KP > SPEC_MAX_NODES) return SPEC_E_SHAPE;
   if (!workspace || workspace_bytes < p.ws) return SPEC_E_WORKSPACE;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
@@ -961,7 +1050,11 @@ extern "C" spec_status_t spec_accept_tree(
   a.draft_p = draft_p; a.logits = logits;
   a.B = B; a.n_max = n_max; a.V = V; a.max_depth = max_depth;
   a.greedy = temperature == 0.f ? 1 : 0;
-  a.inv_T = a.greedy ? 0.0 : 1.0 / (double)temperature;
+  a.inv_T = a.greedy || temperatures ? 0.0 : 1.0 / (double)temperature;
+  a.temps = temperatures;
+  a.pstride = mapped ? Vd : V;
+  a.t2d = nullptr;
+  a.t2d_bad = nullptr;
   a.u_accept = u_accept; a.u_sample = u_sample;
   a.accept_len = accept_len; a.path = path; a.out_tokens = out_tokens; a.n_out = n_out;
   a.final_dist = final_dist; a.tie_log = tie_log; a.tie_cap = tie_cap; a.tie_count = tie_count;
@@ -973,7 +1066,7 @@ extern "C" spec_status_t spec_accept_tree(
   // bound, which makes every wait give up at once, to drive the failure path
   a.spin_limit = 1 << 22;
   if (const char* env = getenv("SPEC_ACCEPT_SPIN_LIMIT")) a.spin_limit = atoi(env);
-  const accept_fn fn = pick_kernel(p.W, p.NG);
+  const accept_fn fn = pick_kernel(p.W, p.NG, mapped);
   const char* coop_env = getenv("SPEC_ACCEPT_COOPERATIVE");
   const bool cooperative = coop_env && coop_env[0] == '1';
 
@@ -981,13 +1074,26 @@ extern "C" spec_status_t spec_accept_tree(
   // sequence cannot be resident together (their exchanges need that).
   int group = B;
   if (p.KP > 1) {
-    const long resident = (long)resident_per_cu(p.W, p.NG) * device_cu_count();
+    const long resident = (long)resident_per_cu(p.W, p.NG, mapped) * device_cu_count();
     if (resident < p.KP) return SPEC_E_UNSUPPORTED;
     group = (int)(resident / p.KP < B ? resident / p.KP : B);
   }
   if (tie_count) {
     hipLaunchKernelGGL(accept_init_kernel, dim3(1), dim3(64), 0, strm, tie_count);
     SPEC_HIP_TRY(hipGetLastError());
+  }
+  if (mapped) {  // inverse map in the workspace, after the exchange words
+    const size_t off = p.KP > 1 ? (((size_t)B * 2 * p.KP * 8 * sizeof(uint64_t) + 255) & ~(size_t)255)
+                                : 256;
+    int32_t* t2d = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + off);
+    int32_t* bad = t2d + V;
+    hipLaunchKernelGGL(t2d_fill_kernel, dim3((V + 255) / 256), dim3(256), 0, strm, t2d, V, bad);
+    SPEC_HIP_TRY(hipGetLastError());
+    hipLaunchKernelGGL(t2d_scatter_kernel, dim3((Vd + 255) / 256), dim3(256), 0, strm, d2t, Vd, V,
+                       t2d, bad);
+    SPEC_HIP_TRY(hipGetLastError());
+    a.t2d = t2d;
+    a.t2d_bad = bad;
   }
   for (int b0 = 0; b0 < B; b0 += group) {
     const int nb = B - b0 < group ? B - b0 : group;
@@ -1013,4 +1119,17 @@ extern "C" spec_status_t spec_accept_tree(
     }
   }
   return SPEC_OK;
+}
+
+extern "C" spec_status_t spec_accept_tree(
+    const int32_t* tokens, const int32_t* parents, const int32_t* n_nodes, const float* draft_p,
+    const float* logits, int32_t B, int32_t n_max, int32_t V, int32_t max_depth,
+    float temperature, const float* u_accept, const float* u_sample, int32_t* accept_len,
+    int32_t* path, int32_t* out_tokens, int32_t* n_out, float* final_dist, spec_tie_t* tie_log,
+    int32_t tie_cap, int32_t* tie_count, void* workspace, size_t workspace_bytes,
+    int32_t* dev_error, void* stream) {
+  return spec_accept_tree_ex(tokens, parents, n_nodes, draft_p, logits, B, n_max, V, max_depth,
+                             temperature, nullptr, nullptr, 0, u_accept, u_sample, accept_len,
+                             path, out_tokens, n_out, final_dist, tie_log, tie_cap, tie_count,
+                             workspace, workspace_bytes, dev_error, stream);
 }

@@ -251,6 +251,42 @@ spec_status_t spec_accept_tree(
 size_t spec_accept_tree_workspace_size(int32_t B, int32_t n_max, int32_t V);
 
 /*
+ * spec_accept_tree_ex -- spec_accept_tree with two variants of its inputs
+ * ([GUIDE] "一次 eagenerate 调用的完整流转": temperature is a per-call
+ * sampling argument, so a batch of requests carries one per sequence;
+ * [GUIDE] "代码里能直接读到的三处改动": an EAGLE-3 draft head ranks its own
+ * vocabulary and draft id i stands for target token i + d2t[i]).
+ *
+ *   temperatures  NULL (the scalar temperature applies), or [B] float32
+ *                 device array: sequence b uses q = softmax(logits /
+ *                 temperatures[b]), 0 meaning greedy for that sequence; a
+ *                 negative or non-finite entry fails its sequence with
+ *                 SPEC_DEVERR_NONFINITE
+ *   d2t, Vd       NULL (draft_p rows hold V entries), or [Vd] int32 device
+ *                 array with 1 <= Vd <= V: draft_p rows hold Vd entries over
+ *                 the draft vocabulary, and the draft probability of target
+ *                 token x is draft_p[..][i] for the i with i + d2t[i] = x, 0
+ *                 if there is none.  A map that leaves [0, V) or sends two
+ *                 draft ids to one token fails every sequence with
+ *                 SPEC_DEVERR_TOKEN.  Tree tokens stay target ids.
+ *   workspace     >= spec_accept_tree_ex_workspace_size(B, n_max, V, Vd)
+ *                 bytes (Vd = 0 without d2t); with d2t it also holds the
+ *                 inverse map, which the call builds first
+ * Everything else as spec_accept_tree, which is this call with both NULL.
+ */
+spec_status_t spec_accept_tree_ex(
+    const int32_t* tokens, const int32_t* parents, const int32_t* n_nodes,
+    const float* draft_p, const float* logits,
+    int32_t B, int32_t n_max, int32_t V, int32_t max_depth, float temperature,
+    const float* temperatures, const int32_t* d2t, int32_t Vd,
+    const float* u_accept, const float* u_sample,
+    int32_t* accept_len, int32_t* path, int32_t* out_tokens, int32_t* n_out,
+    float* final_dist, spec_tie_t* tie_log, int32_t tie_cap, int32_t* tie_count,
+    void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream);
+
+size_t spec_accept_tree_ex_workspace_size(int32_t B, int32_t n_max, int32_t V, int32_t Vd);
+
+/*
  * spec_kv_commit -- commit the accepted path ([LESSON] "KV cache 回滚" and
  * build step 4).  For every sequence with accept_len[b] = a >= 0 and every
  * KV head: cache row prefix_len[b] + i receives the pre-commit row

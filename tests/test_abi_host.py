@@ -21,7 +21,8 @@ def test_every_declared_symbol_is_exported(lib):
                           "spec_accept_tree", "spec_accept_tree_workspace_size", "spec_kv_commit",
                           "spec_kv_commit_layers", "spec_status_string", "spec_abi_version",
                           "spec_tree_state_size", "spec_tree_expand", "spec_tree_finalize",
-                          "spec_verify_tree_attn_rope", "spec_tree_kv_write"}
+                          "spec_verify_tree_attn_rope", "spec_tree_kv_write",
+                          "spec_accept_tree_ex", "spec_accept_tree_ex_workspace_size"}
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -170,3 +171,25 @@ def test_rope_host_checks(lib):
     assert g(*bad) == SPEC_E_VALUE
     bad = list(args); bad[12] = 2
     assert g(*bad) == SPEC_E_DTYPE
+
+
+def test_accept_ex_host_checks(lib):
+    P = _buf()
+    f = lib.spec_accept_tree_ex
+    # tokens, parents, n_nodes, draft_p, logits, B, n_max, V, max_depth, T, temps, d2t, Vd,
+    # u_accept, u_sample, accept_len, path, out_tokens, n_out, final_dist, tie_log, tie_cap,
+    # tie_count, workspace, ws_bytes, dev_error, stream
+    args = ([P] * 5 + [2, 6, 100, 5, 1.0, None, None, 0] + [P] * 6 +
+            [None, None, 0, None, P, 1 << 20, None, None])
+    assert f(*([None] + args[1:])) == SPEC_E_NULL
+    bad = list(args); bad[9] = -1.0        # scalar temperature checked without the array
+    assert f(*bad) == SPEC_E_VALUE
+    bad = list(args); bad[11] = P; bad[12] = 0     # d2t needs 1 <= Vd <= V
+    assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[11] = P; bad[12] = 101
+    assert f(*bad) == SPEC_E_SHAPE
+    assert lib.spec_accept_tree_ex_workspace_size(4, 8, 1000, 0) == \
+        lib.spec_accept_tree_workspace_size(4, 8, 1000)
+    assert lib.spec_accept_tree_ex_workspace_size(4, 8, 1000, 300) >= \
+        lib.spec_accept_tree_workspace_size(4, 8, 1000) + 4 * 1000
+    assert lib.spec_accept_tree_ex_workspace_size(4, 8, 1000, 1001) == 0

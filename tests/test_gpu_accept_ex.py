@@ -1,0 +1,175 @@
+"""GPU parity of spec_accept_tree_ex: per-sequence temperatures and a draft
+distribution held over an EAGLE-3 draft vocabulary (d2t), against the oracle
+(oracle.accept_tree with each sequence's temperature; oracle.draft_p_to_target
+for the draft vocabulary).
+
+Bars as for spec_accept_tree: accepted lengths, paths and tokens bit-exact
+except sequences with a logged near tie; residual distributions within 1e-5.
+The mapped call is also compared with the unmapped call on the explicitly
+expanded draft rows: same kernel arithmetic, so every output is bit-identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from eagle_tree_verification_amd.workloads import make_workload, small_cases, to_device
+from gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(api, w, dev, draft_p, *, temperatures=None, d2t=None, T=None, tokens=None):
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    res = api.accept_tree(tokens if tokens is not None else dev["tokens"], dev["parents"],
+                          dev["n_nodes"], draft_p, dev["logits"], w.T if T is None else T,
+                          dev["u_accept"], dev["u_sample"], w.max_depth, final_dist=True,
+                          tie_cap=4096, dev_error=err, temperatures=temperatures, d2t=d2t)
+    torch.cuda.synchronize()
+    host = {k: v.cpu().numpy() for k, v in res.items() if isinstance(v, torch.Tensor) and k != "tie_log"}
+    host["ties"] = api.decode_ties(res["tie_log"], res["tie_count"])
+    host["dev_error"] = int(err.item())
+    return host
+
+
+def _compare(w, host, temps, p_rows, tokens, seqs=None):
+    """Oracle per sequence at its own temperature; returns excluded sequences."""
+    gpu_tie = set(int(t["b"]) for t in host["ties"])
+    excluded = []
+    for b in (range(w.B) if seqs is None else seqs):
+        r = oracle.accept_tree(tokens[b], w.parents[b], w.n_nodes[b], p_rows(b), w.logits[b],
+                               float(temps[b]), w.u_accept[b], w.u_sample[b], w.max_depth,
+                               n_max=w.n_max)
+        if r.near_tie or b in gpu_tie:
+            excluded.append(b)
+            continue
+        a = r.accept_len
+        assert host["accept_len"][b] == a, (b, host["accept_len"][b], a)
+        np.testing.assert_array_equal(host["path"][b, : a + 1], r.path)
+        np.testing.assert_array_equal(host["out_tokens"][b, : a + 1], r.out_tokens)
+        np.testing.assert_allclose(host["final_dist"][b], r.final_dist / r.final_dist.sum(),
+                                   rtol=0, atol=1e-5)
+    return excluded
+
+
+@pytest.mark.parametrize("name", ["c4-mini", "c2-mini", "c1-t1"])
+def test_per_sequence_temperatures(hip_lib, name):
+    api = hip_lib
+    w = make_workload(poison=True, **small_cases()[name])
+    rng = np.random.default_rng(17)
+    temps = rng.choice(np.array([0.0, 0.6, 1.0, 1.7, 3.0], np.float32), size=w.B)
+    if w.B >= 2:
+        temps[0], temps[1] = 0.0, 1.0
+    say(f"[gpu] per-sequence temperatures {name}: {temps.tolist()}")
+    dev = to_device(w)
+    host = _run(api, w, dev, dev["draft_p"], temperatures=torch.from_numpy(temps).to("cuda"))
+    assert host["dev_error"] == 0
+    excluded = _compare(w, host, temps, lambda b: w.draft_p[b], w.tokens)
+    say(f"[gpu]   near-tie sequences excluded: {excluded}")
+    assert len(excluded) <= max(1, w.B // 4)
+    # all equal to the call's scalar: bit-identical to the scalar form
+    same = _run(api, w, dev, dev["draft_p"],
+                temperatures=torch.full((w.B,), w.T, dtype=torch.float32, device="cuda"))
+    base = _run(api, w, dev, dev["draft_p"])
+    for k in ("accept_len", "path", "out_tokens", "n_out", "final_dist"):
+        np.testing.assert_array_equal(same[k], base[k], err_msg=k)
+
+
+def test_bad_temperature_fails_only_its_sequence(hip_lib):
+    api = hip_lib
+    w = make_workload(poison=True, **small_cases()["c4-mini"])
+    dev = to_device(w)
+    temps = np.full(w.B, 1.0, np.float32)
+    temps[2] = -0.5
+    temps[3] = np.nan
+    host = _run(api, w, dev, dev["draft_p"], temperatures=torch.from_numpy(temps).to("cuda"))
+    assert host["dev_error"] == api.DEVERR_NONFINITE
+    assert host["accept_len"][2] == -1 and host["accept_len"][3] == -1
+    assert (host["path"][2] == -1).all() and host["n_out"][3] == 0
+    _compare(w, host, temps, lambda b: w.draft_p[b], w.tokens, seqs=[0, 1, 4])
+
+
+def _draft_vocab(w, Vd, seed):
+    """A draft vocabulary of Vd target ids: d2t, draft rows restricted to it
+    and renormalised, and child tokens redrawn from the parent's draft row."""
+    rng = np.random.default_rng(seed)
+    ids = np.sort(rng.choice(w.V, size=Vd, replace=False))
+    d2t = (ids - np.arange(Vd)).astype(np.int32)
+    pd = w.draft_p[:, :, ids].astype(np.float64)
+    pd /= np.where(pd.sum(-1, keepdims=True) > 0, pd.sum(-1, keepdims=True), 1.0)
+    pd = np.ascontiguousarray(pd, dtype=np.float32)
+    tokens = w.tokens.copy()
+    for b in range(w.B):
+        n = int(w.n_nodes[b])
+        for j in range(1, n):
+            row = pd[b, w.parents[b, j]].astype(np.float64)
+            cdf = np.cumsum(row)
+            i = min(int(np.searchsorted(cdf, rng.random() * cdf[-1], side="right")), Vd - 1)
+            tokens[b, j] = ids[i]
+    return d2t, pd, tokens
+
+
+@pytest.mark.parametrize("name,Vd", [("c4-mini", 1201), ("c2-mini", 1500), ("c1-t1", 250)])
+def test_draft_vocabulary(hip_lib, name, Vd):
+    api = hip_lib
+    w = make_workload(poison=True, **small_cases()[name])
+    d2t, pd, tokens = _draft_vocab(w, Vd, 23)
+    say(f"[gpu] draft vocabulary {name}: V={w.V} Vd={Vd} T={w.T}")
+    dev = to_device(w)
+    tok_dev = torch.from_numpy(tokens).to("cuda")
+    host = _run(api, w, dev, torch.from_numpy(pd).to("cuda"), d2t=torch.from_numpy(d2t).to("cuda"),
+                tokens=tok_dev)
+    assert host["dev_error"] == 0
+    temps = np.full(w.B, w.T)
+    excluded = _compare(w, host, temps, lambda b: oracle.draft_p_to_target(pd[b], d2t, w.V), tokens)
+    say(f"[gpu]   near-tie sequences excluded: {excluded}")
+    assert len(excluded) <= max(1, w.B // 4)
+    # the unmapped call on the expanded rows: bit-identical outputs
+    full = np.zeros((w.B, w.n_max, w.V), np.float32)
+    full[:, :, np.arange(Vd) + d2t] = pd
+    base = _run(api, w, dev, torch.from_numpy(full).to("cuda"), tokens=tok_dev)
+    for k in ("accept_len", "path", "out_tokens", "n_out", "final_dist"):
+        np.testing.assert_array_equal(host[k], base[k], err_msg=k)
+
+
+def test_bad_draft_map_fails_every_sequence(hip_lib):
+    api = hip_lib
+    w = make_workload(poison=True, **small_cases()["c4-mini"])
+    d2t, pd, tokens = _draft_vocab(w, 600, 5)
+    d2t_dup = d2t.copy()
+    d2t_dup[7] = d2t[8] + 1          # ids 7 and 8 land on one token
+    dev = to_device(w)
+    for bad in (d2t_dup, np.where(np.arange(600) == 599, w.V, d2t).astype(np.int32)):
+        host = _run(api, w, dev, torch.from_numpy(pd).to("cuda"),
+                    d2t=torch.from_numpy(bad).to("cuda"), tokens=torch.from_numpy(tokens).to("cuda"))
+        assert host["dev_error"] == api.DEVERR_TOKEN
+        assert (host["accept_len"] == -1).all()
+
+
+@pytest.mark.timeout(900)
+def test_draft_vocabulary_full_size(hip_lib):
+    """The EAGLE-3 shape at the serving batch: a 32000-id draft vocabulary in
+    the 128256-id target vocabulary, batch 64, per-sequence temperatures.
+    Every sequence is compared with the unmapped call on expanded rows (bit
+    for bit); a sample of sequences with the oracle."""
+    api = hip_lib
+    w = make_workload(4)
+    d2t, pd, tokens = _draft_vocab(w, 32000, 31)
+    temps = np.random.default_rng(2).choice(np.array([0.0, 0.8, 1.0, 1.5], np.float32), size=w.B)
+    dev = to_device(w)
+    tok_dev = torch.from_numpy(tokens).to("cuda")
+    t_dev = torch.from_numpy(temps).to("cuda")
+    host = _run(api, w, dev, torch.from_numpy(pd).to("cuda"), d2t=torch.from_numpy(d2t).to("cuda"),
+                tokens=tok_dev, temperatures=t_dev)
+    assert host["dev_error"] == 0
+    full = torch.zeros((w.B, w.n_max, w.V), dtype=torch.float32, device="cuda")
+    full[:, :, torch.from_numpy(np.arange(32000) + d2t).long().cuda()] = torch.from_numpy(pd).cuda()
+    base = _run(api, w, dev, full, tokens=tok_dev, temperatures=t_dev)
+    del full
+    for k in ("accept_len", "path", "out_tokens", "n_out", "final_dist"):
+        np.testing.assert_array_equal(host[k], base[k], err_msg=k)
+    sample = sorted(np.random.default_rng(3).choice(w.B, size=6, replace=False).tolist())
+    excluded = _compare(w, host, temps, lambda b: oracle.draft_p_to_target(pd[b], d2t, w.V),
+                        tokens, seqs=sample)
+    say(f"[gpu]   sampled {sample}; near-tie excluded {excluded}")
+    assert len(excluded) <= 2
