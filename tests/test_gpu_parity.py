@@ -53,6 +53,34 @@ def test_ragged_trees_and_temperatures(hip_lib, T):
                    dev["prefix_len"].cpu().numpy())
 
 
+@pytest.mark.parametrize("T", [0.0, 1.0])
+def test_maximum_trees(hip_lib, T):
+    """The largest trees the ABI takes (64 nodes): a 63-deep chain, a root
+    with 63 children, a random depth-8 tree and a binary tree, over prefixes
+    from 0 to 8000 keys (so the attention splits its prefix), at the serving
+    head layout."""
+    from eagle_tree_verification_amd.workloads import tree_shape
+    rng = np.random.default_rng(64)
+    chain = np.arange(-1, 63, dtype=np.int32)
+    star = np.array([-1] + [0] * 63, dtype=np.int32)
+    rand = tree_shape(63, 8, rng).astype(np.int32)
+    binary = np.array([-1] + [(j - 1) // 2 for j in range(1, 64)], dtype=np.int32)
+    pars = [chain, star, rand, binary]
+    w = make_workload(4, batch=4, prefix=(0, 8000), vocab=4099, T=T, poison=True, seed=641,
+                      parents=pars, prefix_lens=[8000, 0, 4097, 1])
+    say(f"[gpu] maximum trees T={T}: n={w.n_nodes.tolist()} depth={w.max_depth} "
+        f"L={w.prefix_len.tolist()}")
+    assert w.n_max == 64 and int(w.n_nodes.max()) == 64
+    dev = to_device(w)
+    host = run_gpu_step(w, dev)
+    assert host["dev_error"] == 0
+    compare_attention(w, host["attn"], nodes_per_seq=12, rng=np.random.default_rng(1))
+    excluded = compare_accept(w, host)
+    assert len(excluded) <= 1
+    compare_commit(w, host, kv_host(dev["k_cache"], w.kv_dtype), kv_host(dev["v_cache"], w.kv_dtype),
+                   dev["prefix_len"].cpu().numpy())
+
+
 @pytest.mark.parametrize("hq,hkv,d,dt", [(4, 4, 16, "f32"), (8, 2, 64, "bf16"), (6, 3, 32, "f32"),
                                          (16, 16, 128, "f32"), (12, 4, 128, "bf16")])
 def test_attention_layouts(hip_lib, hq, hkv, d, dt):
