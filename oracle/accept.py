@@ -5,7 +5,9 @@ first- and second-token marginals on tiny trees (they must equal the
 verifier's distributions), a 50,000-step chi-square test of the first emitted
 token, the closed form for the expected number of emitted tokens of an i.i.d.
 chain, a brute-force greedy check at T = 0, the inverse-CDF definition on
-hand-worked cases, and the special cases the pages fix.
+hand-worked cases, and the special cases the pages fix.  The sampling
+filters are pinned by hand-worked tables, the nucleus size of a geometric
+distribution (closed form), ties, and enumeration with filtered q.
 
 Rule (page "推测解码与 EAGLE-3", section "不变量：Leviathan 拒绝采样" and
 build steps 1-3): a draft token d drawn from the draft distribution p is
@@ -34,6 +36,9 @@ terminal token is that argmax (page "EAGLE-1/2/3 拆解", opening section,
 Temperature = 0 is greedy decoding, and the eagenerate flow section: the
 longest passing prefix plus one corrected token lands each cycle).
 
+Sampling filters.  top_k / top_p restrict every q of the walk (filter_keep);
+the rule itself is unchanged, so the output follows the filtered q.
+
 Near ties.  Decisions whose |u - min(1, ratio)| < TIE_BAND and samples whose
 threshold u * W lies within SAMPLE_BAND * W of an edge of the chosen bucket
 are flagged; a flagged sequence-step is excluded from bit-exact comparison
@@ -50,10 +55,57 @@ TIE_BAND = 1e-6
 SAMPLE_BAND = 1e-9
 
 
-def target_distribution(logit_row, T):
-    """q = softmax(logits / T), float64."""
-    x = np.asarray(logit_row, dtype=np.float64) / float(T)
+def _full_distribution(lr, T):
+    x = lr / float(T)
     e = np.exp(x - x.max())
+    return e / e.sum()
+
+
+def filter_keep(logit_row, T, top_k=0, top_p=0.0):
+    """Tokens kept by the verifier's sampling filters, and the top-p margin.
+
+    Page "EAGLE-1/2/3 拆解", section "一次 eagenerate 调用的完整流转", lists
+    top_p and top_k (both 0, i.e. off, by default) beside temperature as the
+    sampling arguments of the generation call.  Readings (listed in the design
+    notes): both filters act on the verifier's q only (p is the draft's
+    distribution as given) and are computed on the tempered distribution over
+    the whole vocabulary; a token is kept when it passes both.  Top-k keeps
+    every token whose logit is at least the k-th largest (ties at the k-th
+    value all kept); 0 < top_k < V turns it on.  Top-p keeps a token when the
+    mass of the tokens with strictly larger logits is below top_p (so ties are
+    kept or dropped together, and the argmax always stays); 0 < top_p < 1
+    turns it on.
+
+    Returns (keep, margin): margin is the smallest |mass above - top_p| over
+    the tokens the top-k filter keeps (inf with top-p off); a margin under
+    TIE_BAND marks a decision rounding could flip.
+    """
+    lr = np.asarray(logit_row, dtype=np.float64)
+    V = len(lr)
+    keep = np.ones(V, dtype=bool)
+    if 0 < top_k < V:
+        kth = np.sort(lr)[::-1][top_k - 1]
+        keep &= lr >= kth
+    margin = np.inf
+    if 0.0 < top_p < 1.0:
+        q = _full_distribution(lr, T)
+        # distinct logits in descending order; mass of each tie group
+        _, grp = np.unique(-lr, return_inverse=True)
+        gmass = np.bincount(grp, weights=q)
+        above = np.concatenate([[0.0], np.cumsum(gmass)[:-1]])[grp]
+        margin = float(np.min(np.abs(above[keep] - top_p)))
+        keep &= above < top_p
+    return keep, margin
+
+
+def target_distribution(logit_row, T, top_k=0, top_p=0.0):
+    """q = softmax(logits / T) in float64, restricted to the tokens
+    filter_keep keeps and renormalised."""
+    lr = np.asarray(logit_row, dtype=np.float64)
+    e = _full_distribution(lr, T)
+    if (0 < top_k < len(lr)) or (0.0 < top_p < 1.0):
+        keep, _ = filter_keep(lr, T, top_k, top_p)
+        e = np.where(keep, e, 0.0)
     return e / e.sum()
 
 
@@ -131,13 +183,15 @@ def _fail(err):
 
 
 def accept_tree(tokens, parents, n_nodes, draft_p, logits, T, u_accept, u_sample,
-                max_depth, n_max=None):
+                max_depth, n_max=None, top_k=0, top_p=0.0):
     """One sequence's acceptance walk.
 
     tokens/parents/u_accept/u_sample: [n_max]; draft_p/logits: [n_max][V].
     Node 0 is the pending root; row v of draft_p is the distribution the
     children of v were drawn from, row v of logits the verifier's logits
-    after v.
+    after v.  top_k / top_p: the sampling filters of filter_keep, applied to
+    every q of the walk at T > 0 (greedy decoding is unaffected: the argmax
+    always passes both).
     """
     n = int(n_nodes)
     if n_max is None:
@@ -176,7 +230,11 @@ def accept_tree(tokens, parents, n_nodes, draft_p, logits, T, u_accept, u_sample
             v = nxt
             continue
 
-        cur = target_distribution(lrow, T)
+        cur = target_distribution(lrow, T, top_k, top_p)
+        if 0.0 < top_p < 1.0:
+            _, fm = filter_keep(lrow, T, top_k, top_p)
+            near |= fm < TIE_BAND
+            decisions.append((v, -1, "filter", None, top_p, fm, None))
         prow = None
         nxt = None
         for c in children[v]:

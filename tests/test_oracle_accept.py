@@ -71,7 +71,7 @@ def _outcomes(run, n):
     return found
 
 
-def _tree_marginals(V, parents, q_ctx, p_ctx, accept_fn=None):
+def _tree_marginals(V, parents, q_ctx, p_ctx, accept_fn=None, top_k=0, top_p=0.0):
     """First-token marginal and second-token conditionals, exactly.
 
     parents: a tree of depth <= 2.  q_ctx(ctx) / p_ctx(ctx) give the verifier
@@ -102,7 +102,8 @@ def _tree_marginals(V, parents, q_ctx, p_ctx, accept_fn=None):
 
         def run(u):
             return oracle.accept_tree(tok, parents, n, draft, logits, 1.0, u,
-                                      np.zeros(n), max_depth=int(depth.max()))
+                                      np.zeros(n), max_depth=int(depth.max()), top_k=top_k,
+                                      top_p=top_p)
 
         for w, res in _outcomes(run, n):
             w *= w_tok
@@ -476,3 +477,118 @@ def test_enumeration_with_a_draft_vocabulary(K):
     qf, _ = _dists(V, 300 + K)
     P1, _ = _tree_marginals(V, [-1] + [0] * K, qf, pd)
     np.testing.assert_allclose(P1, qf(()), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# top-k processed verifier distribution
+# ----------------------------------------------------------------------------
+def test_top_k_by_hand():
+    lg = np.log(np.array([1.0, 3.0, 2.0, 3.0, 0.5]))   # weights 1, 3, 2, 3, 0.5
+    np.testing.assert_allclose(oracle.target_distribution(lg, 1.0, 2), [0, .5, 0, .5, 0])
+    np.testing.assert_allclose(oracle.target_distribution(lg, 1.0, 3), [0, 3 / 8, 2 / 8, 3 / 8, 0])
+    # k = 1 with a tie at the top keeps both maxima
+    np.testing.assert_allclose(oracle.target_distribution(lg, 1.0, 1), [0, .5, 0, .5, 0])
+    # k >= V and k = 0 leave q alone; temperature applies before the filter
+    full = np.array([1, 3, 2, 3, .5]) / 9.5
+    np.testing.assert_allclose(oracle.target_distribution(lg, 1.0, 5), full)
+    np.testing.assert_allclose(oracle.target_distribution(lg, 1.0, 0), full)
+    w = np.array([1.0, 3.0, 2.0, 3.0, 0.5]) ** 0.5           # T = 2: weights ** (1/2)
+    w[[0, 4]] = 0.0
+    np.testing.assert_allclose(oracle.target_distribution(lg, 2.0, 3), w / w.sum())
+
+
+@pytest.mark.parametrize("V,K,k", [(5, 2, 2), (4, 3, 1), (5, 1, 3)])
+def test_enumeration_with_top_k(V, K, k):
+    """With the verifier's q cut to its top k, the first emitted token follows
+    that cut distribution exactly (the walk stays lossless for any q)."""
+    qf, pf = _dists(V, 500 + 10 * V + K + k)
+    parents = [-1] + [0] * K
+    P1, _ = _tree_marginals(V, parents, qf, pf, top_k=k)
+    q = qf(())
+    keep = q >= np.sort(q)[::-1][k - 1]
+    want = np.where(keep, q, 0.0) / q[keep].sum()
+    np.testing.assert_allclose(P1, want, rtol=0, atol=1e-12)
+
+
+def test_top_p_by_hand():
+    # weights 1, 3, 2, 3, 0.5 (total 9.5): tokens 1 and 3 tie at the top.
+    # Mass strictly above: tokens 1, 3 -> 0; token 2 -> 6/9.5; token 0 ->
+    # 8/9.5; token 4 -> 9/9.5.
+    lg = np.log(np.array([1.0, 3.0, 2.0, 3.0, 0.5]))
+    td = oracle.target_distribution
+    np.testing.assert_allclose(td(lg, 1.0, 0, 0.5), [0, .5, 0, .5, 0])
+    np.testing.assert_allclose(td(lg, 1.0, 0, 0.63), [0, .5, 0, .5, 0])
+    np.testing.assert_allclose(td(lg, 1.0, 0, 0.64), [0, 3 / 8, 2 / 8, 3 / 8, 0])
+    np.testing.assert_allclose(td(lg, 1.0, 0, 0.9), np.array([1, 3, 2, 3, 0]) / 9.0)
+    np.testing.assert_allclose(td(lg, 1.0, 0, 0.95), np.array([1, 3, 2, 3, .5]) / 9.5)
+    # p at or beyond 1, or 0: off
+    for p in (0.0, 1.0, 1.5):
+        np.testing.assert_allclose(td(lg, 1.0, 0, p), np.array([1, 3, 2, 3, .5]) / 9.5)
+    # both filters: a token must pass each (top-k 1 keeps the tied pair)
+    np.testing.assert_allclose(td(lg, 1.0, 1, 0.9), [0, .5, 0, .5, 0])
+    np.testing.assert_allclose(td(lg, 1.0, 4, 0.7), [0, 3 / 8, 2 / 8, 3 / 8, 0])
+    np.testing.assert_allclose(td(lg, 1.0, 3, 0.95), [0, 3 / 8, 2 / 8, 3 / 8, 0])
+    # margins: distance of top_p to the nearest mass-above of a kept-by-top-k token
+    _, m = oracle.filter_keep(lg, 1.0, 0, 0.64)
+    assert m == pytest.approx(0.64 - 6 / 9.5)
+    _, m = oracle.filter_keep(lg, 1.0, 3, 0.95)     # tokens 0 and 4 are out by top-k
+    assert m == pytest.approx(0.95 - 6 / 9.5)
+    assert oracle.filter_keep(lg, 1.0, 2, 0.0)[1] == np.inf
+
+
+@pytest.mark.parametrize("r,V,p,T", [(0.8, 200, 0.9, 1.0), (0.5, 64, 0.5, 1.0),
+                                     (0.95, 1000, 0.7, 2.0), (0.3, 30, 0.99, 0.5)])
+def test_top_p_geometric_closed_form(r, V, p, T):
+    """q_i proportional to r^i (logits i T log r): token i is kept iff
+    (1 - r^i) / (1 - r^V) < p, so the nucleus holds the first
+    ceil(log(1 - p (1 - r^V)) / log r) tokens."""
+    lg = np.arange(V) * T * np.log(r)
+    rng = np.random.default_rng(V)
+    perm = rng.permutation(V)
+    keep, _ = oracle.filter_keep(lg[perm], T, 0, p)
+    want = int(np.ceil(np.log(1 - p * (1 - r ** V)) / np.log(r)))
+    assert keep.sum() == want
+    assert np.all(keep[np.argsort(perm)][:want])
+
+
+def test_filters_keep_ties_together():
+    rng = np.random.default_rng(4)
+    lg = rng.integers(-3, 3, size=500).astype(np.float64)   # 6 values, many ties
+    for k in (1, 7, 100, 499):
+        keep, _ = oracle.filter_keep(lg, 1.0, k, 0.0)
+        kth = np.sort(lg)[::-1][k - 1]
+        np.testing.assert_array_equal(keep, lg >= kth)
+    for p in (0.05, 0.3, 0.6, 0.99):
+        keep, _ = oracle.filter_keep(lg, 0.7, 0, p)
+        # a kept value keeps all its ties; the largest value is always kept
+        for val in np.unique(lg):
+            assert len(set(keep[lg == val])) == 1
+        assert keep[lg == lg.max()].all()
+    # all logits equal: top-p keeps everything (no token has mass above it)
+    keep, _ = oracle.filter_keep(np.zeros(50), 1.0, 0, 0.01)
+    assert keep.all()
+
+
+@pytest.mark.parametrize("V,K,k,p", [(5, 2, 0, 0.5), (4, 3, 0, 0.8), (5, 2, 3, 0.6)])
+def test_enumeration_with_top_p(V, K, k, p):
+    qf, pf = _dists(V, 700 + 10 * V + K)
+    parents = [-1] + [0] * K
+    P1, _ = _tree_marginals(V, parents, qf, pf, top_k=k, top_p=p)
+    want = oracle.target_distribution(np.log(qf(())), 1.0, k, p)
+    assert (want == 0).any()
+    np.testing.assert_allclose(P1, want, rtol=0, atol=1e-12)
+
+
+def test_top_p_boundary_is_a_near_tie():
+    lg = np.log(np.array([1.0, 3.0, 2.0, 3.0, 0.5]))
+    ids = np.array([2, 0], np.int32)          # the root's child carries token 0
+    par = np.array([-1, 0], np.int32)
+    logits = np.stack([lg, lg])
+    dp = np.full((2, 5), 0.2)
+    r = oracle.accept_tree(ids, par, 2, dp, logits, 1.0, [0.0, 0.99], [0.5, 0.5], 1,
+                           top_p=6 / 9.5)
+    assert r.near_tie
+    r = oracle.accept_tree(ids, par, 2, dp, logits, 1.0, [0.0, 0.99], [0.5, 0.5], 1, top_p=0.7)
+    assert not r.near_tie
+    # token 0 is outside the nucleus at 0.7: q(0) = 0, so it is rejected
+    assert r.accept_len == 0 and r.out_tokens[0] in (1, 2, 3)
