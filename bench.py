@@ -204,8 +204,9 @@ def accept_variants_bench(w, dev, reps=20):
     temperatures (seeded from {0, 0.8, 1, 1.5}), and draft rows over a
     32000-id draft vocabulary mapped into the target one (EAGLE-3's shape:
     a sorted seeded subset, rows restricted and renormalised, children
-    redrawn from their parent's draft row).  Each is timed with the plain
-    call on the same inputs beside it."""
+    redrawn from their parent's draft row), and the sampling filters on q
+    (top-k 50, top-p 0.9, both).  Each is timed with the plain call on the
+    same inputs beside it."""
     import torch
 
     from eagle_tree_verification_amd import api
@@ -227,8 +228,10 @@ def accept_variants_bench(w, dev, reps=20):
     tokens = torch.where(child, ids[draw.reshape(w.B, w.n_max)].to(torch.int32), tokens)
     full = torch.zeros_like(dev["draft_p"])
     full[:, :, ids] = pd
-    ws = torch.empty(api.accept_tree_ex_workspace_size(w.B, w.n_max, w.V, Vd), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(api.accept_tree_ex_workspace_size(w.B, w.n_max, w.V, Vd, filters=True),
+                     dtype=torch.uint8, device="cuda")
+    k50 = torch.full((w.B,), 50, dtype=torch.int32, device="cuda")
+    p09 = torch.full((w.B,), 0.9, dtype=torch.float32, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
 
     def timed(fn):
@@ -252,7 +255,10 @@ def accept_variants_bench(w, dev, reps=20):
            "scalar_T_ms": timed(walk(dev["draft_p"], dev["tokens"])),
            "per_seq_T_ms": timed(walk(dev["draft_p"], dev["tokens"], temperatures=temps)),
            "expanded_rows_ms": timed(walk(full, tokens)),
-           "draft_vocab_ms": timed(walk(pd, tokens, d2t=d2t))}
+           "draft_vocab_ms": timed(walk(pd, tokens, d2t=d2t)),
+           "top_k50_ms": timed(walk(dev["draft_p"], dev["tokens"], top_k=k50)),
+           "top_p09_ms": timed(walk(dev["draft_p"], dev["tokens"], top_p=p09)),
+           "top_k50_p09_ms": timed(walk(dev["draft_p"], dev["tokens"], top_k=k50, top_p=p09))}
     if int(err.item()) != 0:
         raise RuntimeError(f"walk variants device error bits {int(err.item())}")
     del full, pd, rows

@@ -58,10 +58,10 @@ def load():
     lib.spec_accept_tree.restype = I
     lib.spec_accept_tree_workspace_size.argtypes = [I, I, I]
     lib.spec_accept_tree_workspace_size.restype = Z
-    lib.spec_accept_tree_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, P, P, I, P, P, P, P, P, P,
-                                        P, P, I, P, P, Z, P, P]
+    lib.spec_accept_tree_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, P, P, P, P, I, P, P, P, P,
+                                        P, P, P, P, I, P, P, Z, P, P]
     lib.spec_accept_tree_ex.restype = I
-    lib.spec_accept_tree_ex_workspace_size.argtypes = [I, I, I, I]
+    lib.spec_accept_tree_ex_workspace_size.argtypes = [I, I, I, I, I]
     lib.spec_accept_tree_ex_workspace_size.restype = Z
     lib.spec_kv_commit.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P]
     lib.spec_kv_commit.restype = I
@@ -202,7 +202,8 @@ def tree_kv_write(k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, parents, 
 
 def accept_tree(tokens, parents, n_nodes, draft_p, logits, temperature, u_accept, u_sample,
                 max_depth, *, final_dist=False, tie_cap=0, workspace=None, dev_error=None,
-                outputs=None, stream=None, temperatures=None, d2t=None):
+                outputs=None, stream=None, temperatures=None, d2t=None, top_k=None,
+                top_p=None):
     """Acceptance walk; returns a dict of device tensors.
 
     Keys: accept_len [B], path [B][max_depth+1], out_tokens [B][max_depth+1],
@@ -211,15 +212,17 @@ def accept_tree(tokens, parents, n_nodes, draft_p, logits, temperature, u_accept
 
     temperatures ([B] float32 device tensor) gives each sequence its own
     temperature; d2t ([Vd] int32 device tensor) means draft_p rows hold the
-    draft vocabulary's Vd entries (spec_accept_tree_ex).
+    draft vocabulary's Vd entries; top_k ([B] int32) and top_p ([B] float32)
+    are per-sequence sampling filters on q (spec_accept_tree_ex).
     """
     lib = load()
     B, n_max, V = logits.shape
     Vd = 0 if d2t is None else int(d2t.numel())
-    if temperatures is not None or d2t is not None:
+    if temperatures is not None or d2t is not None or top_k is not None or top_p is not None:
         return _accept_tree_ex(lib, tokens, parents, n_nodes, draft_p, logits, temperature,
                                u_accept, u_sample, max_depth, final_dist, tie_cap, workspace,
-                               dev_error, outputs, stream, temperatures, d2t, B, n_max, V, Vd)
+                               dev_error, outputs, stream, temperatures, d2t, top_k, top_p, B,
+                               n_max, V, Vd)
     dev = logits.device
     for t, nm in ((tokens, "tokens"), (parents, "parents"), (n_nodes, "n_nodes")):
         _dev(t, nm, torch.int32)
@@ -250,13 +253,13 @@ def accept_tree(tokens, parents, n_nodes, draft_p, logits, temperature, u_accept
             "final_dist": fd, "tie_log": tlog, "tie_count": tcount}
 
 
-def accept_tree_ex_workspace_size(B, n_max, V, Vd):
-    return int(load().spec_accept_tree_ex_workspace_size(B, n_max, V, Vd))
+def accept_tree_ex_workspace_size(B, n_max, V, Vd, filters=False):
+    return int(load().spec_accept_tree_ex_workspace_size(B, n_max, V, Vd, int(bool(filters))))
 
 
 def _accept_tree_ex(lib, tokens, parents, n_nodes, draft_p, logits, temperature, u_accept,
                     u_sample, max_depth, final_dist, tie_cap, workspace, dev_error, outputs,
-                    stream, temperatures, d2t, B, n_max, V, Vd):
+                    stream, temperatures, d2t, top_k, top_p, B, n_max, V, Vd):
     dev = logits.device
     for t, nm in ((tokens, "tokens"), (parents, "parents"), (n_nodes, "n_nodes")):
         _dev(t, nm, torch.int32)
@@ -267,6 +270,10 @@ def _accept_tree_ex(lib, tokens, parents, n_nodes, draft_p, logits, temperature,
         _dev(temperatures, "temperatures", torch.float32)
     if d2t is not None:
         _dev(d2t, "d2t", torch.int32)
+    if top_k is not None:
+        _dev(top_k, "top_k", torch.int32)
+    if top_p is not None:
+        _dev(top_p, "top_p", torch.float32)
     if tuple(draft_p.shape) != (B, n_max, Vd if d2t is not None else V):
         raise ValueError("draft_p must be [B][n_max][Vd] with d2t, [B][n_max][V] without")
     o = outputs or {}
@@ -282,10 +289,12 @@ def _accept_tree_ex(lib, tokens, parents, n_nodes, draft_p, logits, temperature,
     fd = torch.empty((B, V), dtype=torch.float32, device=dev) if final_dist else None
     tlog = torch.zeros(max(tie_cap, 1) * TIE_DTYPE.itemsize, dtype=torch.uint8, device=dev) if tie_cap else None
     tcount = torch.zeros(1, dtype=torch.int32, device=dev) if tie_cap else None
-    ws, wsb = _workspace(accept_tree_ex_workspace_size(B, n_max, V, Vd), dev, workspace)
+    filters = top_k is not None or top_p is not None
+    ws, wsb = _workspace(accept_tree_ex_workspace_size(B, n_max, V, Vd, filters), dev, workspace)
     st = lib.spec_accept_tree_ex(_ptr(tokens), _ptr(parents), _ptr(n_nodes), _ptr(draft_p),
                                  _ptr(logits), B, n_max, V, int(max_depth), float(temperature),
-                                 _ptr(temperatures), _ptr(d2t), Vd, _ptr(u_accept),
+                                 _ptr(temperatures), _ptr(top_k), _ptr(top_p), _ptr(d2t), Vd,
+                                 _ptr(u_accept),
                                  _ptr(u_sample), _ptr(acc), _ptr(path), _ptr(toks), _ptr(nout),
                                  _ptr(fd), _ptr(tlog), int(tie_cap), _ptr(tcount), _ptr(ws), wsb,
                                  _ptr(dev_error), _stream(stream))

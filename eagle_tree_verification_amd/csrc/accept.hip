@@ -16,6 +16,19 @@
 // Temperature 0 is greedy decoding (accept iff the token is the verifier's
 // argmax; emit the argmax).
 //
+// Sampling filters (page "EAGLE-1/2/3 拆解", section "一次 eagenerate 调用的完整
+// 流转": top_k and top_p are sampling arguments beside the temperature).
+// Both restrict q to the tokens whose logit is at least a threshold t that
+// is itself one of the row's logits: top-k's t is the k-th largest logit,
+// top-p's is the largest logit whose tokens at or above it hold at least
+// the mass p of the tempered q; with both, the larger.  The threshold is
+// found by a radix select over an order-preserving 32-bit key of the float
+// logit, 8 bits per round, on per-bucket counts and 2^-47 fixed-point masses
+// of q (integers, so the sums are exact and order-free), each round's
+// histograms combined over the KP workgroups; then one more pass sums
+// exp(z - M) over the kept tokens, and the walk proceeds with every q masked
+// to logit >= t.
+//
 // Shape on the GPU.  The walk is serial along the tree but every step is a
 // reduction over the 32k-128k vocabulary, so a sequence gets KP workgroups,
 // each owning a slice of NT * W * NG entries (thread t reads W consecutive
@@ -135,7 +148,10 @@ struct AcceptArgs {
   int KP;       // workgroups per sequence
   int chunk;    // vocabulary entries per workgroup (NT * W * NG)
   uint64_t* slots;  // [group size][2][KP][8] tagged exchange words
-  uint64_t epoch;   // launch id (40 bits), part of every exchange tag
+  uint64_t epoch;   // launch id (32 bits), part of every exchange tag
+  const int32_t* top_k;   // per-sequence top-k (<= 0 or >= V: off), or null
+  const float* top_p;     // per-sequence top-p (<= 0 or >= 1: off), or null
+  uint64_t* hist;         // [B][2][KP][512] tagged histogram words
   int32_t* dev_error;
   int spin_limit;
 };
@@ -239,6 +255,12 @@ __device__ void block_argmax(float& v, int& i, double* red) {
 __device__ __forceinline__ int block_or(int f, int*) { return __syncthreads_or(f); }
 
 // ---- inter-workgroup exchange ---------------------------------------------
+// Tag of exchange number gen of this launch: 32 bits of launch id, 16 of
+// exchange number (a walk makes well under 2^16 exchanges), 48 bits in all.
+__device__ __forceinline__ uint64_t exchange_tag(const AcceptArgs& a, int gen) {
+  return ((a.epoch & 0xFFFFFFFFull) << 16) | (uint64_t)(gen & 0xffff);
+}
+
 // Publishes this workgroup's two partials and gathers all KP workgroups'
 // partials into xs.  Each partial travels as four 64-bit words of 16 payload
 // bits under a 48-bit tag (launch id, exchange number), written and read with
@@ -260,7 +282,7 @@ __device__ bool exchange(const AcceptArgs& a, int bl, int part, int& gen, double
     __syncthreads();
     return true;
   }
-  const uint64_t tag = ((a.epoch << 8) | (uint64_t)(gen & 0xff)) & 0xFFFFFFFFFFFFull;
+  const uint64_t tag = exchange_tag(a, gen);
   uint64_t* slot = a.slots + ((size_t)bl * 2 + (gen & 1)) * (size_t)a.KP * 8;
   ++gen;
   if (t < 8) {
@@ -437,7 +459,229 @@ __device__ __forceinline__ void stream_slice(const float* r1, float f1, const fl
   }
 }
 
-template <int NG, int W, bool MAPPED>
+// ---- sampling filters -------------------------------------------------------
+static_assert(NT == 256, "one radix bucket per thread");
+// 2^47: fixed-point unit of q.  A slice's bucket then stays below 2^48 (q <= 1
+// up to rounding), the width of its mass field in an exchange word.
+constexpr double kMassOne = 140737488355328.0;
+
+// Order-preserving 32-bit key of a finite float: a larger float has a larger
+// key, and -0 shares the key of +0 (they compare equal).  Finite floats map
+// into [0x00800000, 0xFF7FFFFF].
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t u = x == 0.f ? 0u : __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// A float f with (x >= f) == (order_key(x) >= k) for every finite x, for a
+// key k at or below some finite float's key.
+__device__ __forceinline__ float key_floor_float(uint32_t k) {
+  if (k <= 0x00800000u) return -INFINITY;
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+struct FilterShared {
+  uint64_t wc[NT / 64], wm[NT / 64];  // wave totals of the bucket scan
+  uint64_t sel_C, sel_F, sel_cnt, sel_mass;
+};
+
+// Publishes this workgroup's 256-bucket histogram (h_cnt, h_mass: bucket j at
+// index j * kCopies) and returns
+// the sums over the KP workgroups of bucket jb.  Like exchange(), with no
+// fence: every 64-bit word carries a 32-bit tag (20 bits of launch id, 12 of
+// exchange number) above 32 payload bits, is written and read with
+// device-coherent atomic accesses, and is valid once its tag is current.  A
+// bucket is two words: count (16 bits; a slice holds at most 16384 entries)
+// with mass bits 47..32, then mass bits 31..0.  Each thread issues the loads
+// of kHistBatch workgroups at once before checking tags.  Buffers alternate with
+// the exchange number as in exchange(), whose numbering this shares.
+constexpr int kHistBatch = 4;  // workgroups whose words one thread loads at once
+// Lanes spread their histogram atomics over kCopies copies of every bucket
+// (lane % kCopies; the copies of one bucket are adjacent words, so in
+// different banks), which cuts same-address serialisation when many lanes
+// share a digit; the copies are folded into copy 0 before the exchange.
+constexpr int kCopies = 4;
+
+__device__ bool exchange_hist(const AcceptArgs& a, int bl, int part, int& gen,
+                              const uint32_t* h_cnt, const uint64_t* h_mass, int jb,
+                              uint64_t& cnt, uint64_t& mass, int* s_or) {
+  const int t = threadIdx.x;
+  if (a.KP == 1) {
+    cnt = h_cnt[jb * kCopies];
+    mass = h_mass[jb * kCopies];
+    return true;
+  }
+  const uint64_t tag = (((a.epoch & 0xFFFFFull) << 12) | (uint64_t)(gen & 0xfff)) << 32;
+  uint64_t* data = a.hist + ((size_t)bl * 2 + (gen & 1)) * (size_t)a.KP * 512;
+  ++gen;
+  const uint64_t m = h_mass[t * kCopies];
+  __hip_atomic_store(data + part * 512 + 2 * t,
+                     tag | ((uint64_t)h_cnt[t * kCopies] << 16) | ((m >> 32) & 0xffffull),
+                     __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(data + part * 512 + 2 * t + 1, tag | (m & 0xffffffffull), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  int bad = 0;
+  uint64_t c = 0, ms = 0;
+  for (int k0 = 0; k0 < a.KP; k0 += kHistBatch) {
+    const int nk = a.KP - k0 < kHistBatch ? a.KP - k0 : kHistBatch;
+    uint64_t w[2 * kHistBatch];
+#pragma unroll
+    for (int i = 0; i < 2 * kHistBatch; ++i)
+      w[i] = i / 2 < nk ? __hip_atomic_load(data + (size_t)(k0 + i / 2) * 512 + 2 * jb + (i & 1),
+                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                        : tag;
+#pragma unroll
+    for (int i = 0; i < 2 * kHistBatch; ++i) {
+      int spins = 0;
+      while ((w[i] >> 32) != (tag >> 32)) {
+        if (a.spin_limit < 0 || ++spins > a.spin_limit) {  // a negative bound: test hook
+          bad = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        w[i] = __hip_atomic_load(data + (size_t)(k0 + i / 2) * 512 + 2 * jb + (i & 1),
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * kHistBatch; i += 2)
+      if (i / 2 < nk) {
+        c += (w[i] >> 16) & 0xffffull;
+        ms += ((w[i] & 0xffffull) << 32) | (w[i + 1] & 0xffffffffull);
+      }
+  }
+  cnt = c;
+  mass = ms;
+  return !block_or(bad, s_or);
+}
+
+// The filters' threshold t for the row at lrow (identical in every workgroup
+// of the sequence): thr is a float with (x >= thr) exactly for the kept
+// logits x.  fk: top-k (0 = off); P: top-p in units of 2^-47 (0 = off).
+// Radix select, most significant digit first.  In each round the entries
+// whose key matches the digits chosen so far are counted (and their masses
+// exp(z - M) / S summed in fixed point) per next digit; with C(j) and F(j) the
+// count and mass of all keys at or above bucket j, top-k's threshold lies in
+// the highest bucket with C(j) >= k and top-p's in the highest with
+// F(j) >= P, and the higher of the two is refined next.  It stops when the
+// chosen bucket is one key (four rounds), holds a single entry, or (top-k
+// deciding) holds exactly the entries still needed.  margin: distance of P
+// to the masses above and at the threshold (in units of q), or a large
+// value when top-p cannot flip a kept token.
+template <int NG, int W, int BG>
+__device__ bool filter_threshold(const AcceptArgs& a, int bl, int part, int& gen,
+                                 const float* lrow, int lo, int hi, double invT, double M,
+                                 double S, int fk, uint64_t P, const double* tab,
+                                 uint32_t* h_cnt, uint64_t* h_mass, FilterShared& fs, int* s_or,
+                                 float& thr, double& margin) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int jb = NT - 1 - tid;  // this thread's bucket in the descending scan
+  const int cp = lane % kCopies;
+  const bool use_k = fk > 0, use_p = P > 0;
+  const double fscale = kMassOne / S;
+  const uint64_t band = (uint64_t)(kTieBand * kMassOne);
+  uint32_t prefix = 0;
+  uint64_t above_c = 0, above_m = 0;
+  margin = 1.0;
+  for (int r = 0;; ++r) {
+    const int sh = 24 - 8 * r;
+#pragma unroll
+    for (int c = 0; c < kCopies; ++c) {
+      h_cnt[tid * kCopies + c] = 0;
+      h_mass[tid * kCopies + c] = 0;
+    }
+    __syncthreads();
+    // one entry of the current range into the histogram
+    auto add = [&](float x) {
+      const int dg = (order_key(x) >> sh) & 255;
+      atomicAdd(&h_cnt[dg * kCopies + cp], 1u);
+      if (use_p) {
+        const double e = exp_tab(fma((double)x, invT, -M), tab);
+        atomicAdd((unsigned long long*)&h_mass[dg * kCopies + cp],
+                  (unsigned long long)(e * fscale));
+      }
+    };
+    stream_slice<NG, W, BG, false>(lrow, -INFINITY, lrow, 0.f, lo, hi,
+        [&](int g0, float (*xv)[W], float (*)[W]) {
+#pragma unroll
+          for (int gb = 0; gb < BG; ++gb)
+#pragma unroll
+            for (int j = 0; j < W; ++j)
+              if (elem_index<W>(lo, (g0 + gb) * W + j) < hi &&
+                  (uint32_t)((uint64_t)order_key(xv[gb][j]) >> (sh + 8)) == prefix)
+                add(xv[gb][j]);
+        });
+    __syncthreads();
+    {
+      uint32_t fc = 0;
+      uint64_t fm = 0;
+#pragma unroll
+      for (int c = 0; c < kCopies; ++c) {
+        fc += h_cnt[tid * kCopies + c];
+        fm += h_mass[tid * kCopies + c];
+      }
+      h_cnt[tid * kCopies] = fc;
+      h_mass[tid * kCopies] = fm;
+    }
+    __syncthreads();
+    uint64_t cnt, mass;
+    if (!exchange_hist(a, bl, part, gen, h_cnt, h_mass, jb, cnt, mass, s_or)) return false;
+    // suffix sums over buckets (prefix sums over threads)
+    uint64_t c = cnt, m = mass;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint64_t c2 = __shfl_up(c, o), m2 = __shfl_up(m, o);
+      if (lane >= o) {
+        c += c2;
+        m += m2;
+      }
+    }
+    if (lane == 63) {
+      fs.wc[wv] = c;
+      fs.wm[wv] = m;
+    }
+    __syncthreads();
+    for (int k = 0; k < wv; ++k) {
+      c += fs.wc[k];
+      m += fs.wm[k];
+    }
+    const uint64_t Cj = above_c + c, Fj = above_m + m;
+    const int jk = use_k ? __syncthreads_count(Cj >= (uint64_t)fk) - 1 : -1;
+    const int jp = use_p ? __syncthreads_count(Fj >= P) - 1 : -1;
+    int js = jk > jp ? jk : jp;
+    if (js < 0) js = 0;  // unreachable: the threshold lies in the current range
+    if (jb == js) {
+      fs.sel_C = Cj;
+      fs.sel_F = Fj;
+      fs.sel_cnt = cnt;
+      fs.sel_mass = mass;
+    }
+    __syncthreads();
+    const uint64_t selC = fs.sel_C, selF = fs.sel_F, selc = fs.sel_cnt, selm = fs.sel_mass;
+    prefix = (prefix << 8) | (uint32_t)js;
+    above_c = selC - selc;
+    above_m = selF - selm;
+    const bool done = r == 3 || selc == 1 ||
+                      (use_k && selC == (uint64_t)fk && (!use_p || selF + band <= P));
+    if (done) {
+      thr = key_floor_float(prefix << sh);
+      if (use_p) {
+        // P - (mass above t) > 0 always; (mass at or above t) - P matters
+        // only when top-p chose the bucket
+        double mg = (double)(P - above_m) / kMassOne;
+        if (js == jp) mg = fmin(mg, (double)(selF - P) / kMassOne);
+        margin = mg;
+      }
+      return true;
+    }
+  }
+}
+
+// FILT: the sampling filters are compiled in (the variant used when the call
+// passes top_k or top_p); without it every q is unfiltered.
+template <int NG, int W, bool MAPPED, bool FILT>
 __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   // groups loaded together: four in the one-row passes, two when the
   // residual pass streams logits and draft rows side by side
@@ -450,7 +694,10 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   __shared__ double red[2 * (NT / 64)];
   __shared__ double xs[SPEC_MAX_NODES][2];
   __shared__ double cur_sums[SPEC_MAX_NODES];
-  __shared__ double scan[NG][NT];
+  // also the filters' histograms: [256][kCopies] uint64 masses in rows 0-3,
+  // [256][kCopies] uint32 counts in rows 4-5
+  __shared__ double scan[FILT && NG < 6 ? 6 : (NG < 2 ? 2 : NG)][NT];
+  __shared__ FilterShared fsh;
   __shared__ double gtot[NG];
   __shared__ int s_or, s_hit, s_gsel, s_tsel;
   __shared__ float s_kp[SPEC_MAX_NODES], s_kl[SPEC_MAX_NODES], s_ku[SPEC_MAX_NODES], s_us;
@@ -480,9 +727,20 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
     greedy = T == 0.f;
     invT = greedy ? 0.0 : 1.0 / (double)T;
   }
+  int fk = 0;          // top-k, 0 = off
+  uint64_t fP = 0;     // top-p in units of 2^-47, 0 = off
+  if (FILT && a.top_k) {
+    const int k = a.top_k[b];
+    if (k > 0 && k < a.V) fk = k;
+  }
+  if (FILT && a.top_p) {
+    const float pp = a.top_p[b];
+    if (pp != pp) err = SPEC_DEVERR_NONFINITE;
+    else if (pp > 0.f && pp < 1.f) fP = max((uint64_t)((double)pp * kMassOne), (uint64_t)1);
+  }
   if (MAPPED && *a.t2d_bad) err = SPEC_DEVERR_TOKEN;
   if (err) {
-    // a bad temperature or draft map: nothing else is checked
+    // a bad temperature, top-p or draft map: nothing else is checked
   } else if (n < 1 || n > a.n_max) {
     err = SPEC_DEVERR_TREE;
   } else {
@@ -643,8 +901,41 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       return;
     }
     const double M = wave_max_d(pm);
-    const double pterm = (has && pm != -INFINITY) ? ps * exp_nonpos(pm - M) : 0.0;
-    const double S = wave_sum_d(pterm);
+    double pterm = (has && pm != -INFINITY) ? ps * exp_nonpos(pm - M) : 0.0;
+    double S = wave_sum_d(pterm);
+
+    // ---- sampling filters: threshold, then the kept mass per slice ----------
+    float lcut = -INFINITY;  // q is restricted to logits >= lcut
+    // kept(x): x passes the filters (always, in a variant without them)
+    auto kept = [&](float x) { return !FILT || x >= lcut; };
+    if (FILT && (fk > 0 || fP > 0)) {
+      double fmargin;
+      if (!filter_threshold<NG, W, 1>(a, bl, part, gen, lrow, lo, hi, invT, M, S, fk, fP, s_tab,
+                                        reinterpret_cast<uint32_t*>(&scan[4][0]),
+                                        reinterpret_cast<uint64_t*>(&scan[0][0]), fsh, &s_or, lcut,
+                                        fmargin)) {
+        fail_sync(a, b, writer0);
+        return;
+      }
+      if (writer0 && tid == 0 && fmargin < kTieBand)
+        log_tie(a, b, v, 3, a.top_p[b], fmargin);
+      double ek = 0.0;
+      stream_slice<NG, W, BG2, false>(lrow, -INFINITY, lrow, 0.f, lo, hi,
+          [&](int, float (*xv)[W], float (*)[W]) {
+#pragma unroll
+            for (int gb = 0; gb < BG2; ++gb)
+#pragma unroll
+              for (int j = 0; j < W; ++j)
+                if (kept(xv[gb][j])) ek += exp_tab(fma((double)xv[gb][j], invT, -M), s_tab);
+          });
+      ek = block_sum(ek, red);
+      if (!exchange(a, bl, part, gen, ek, 0.0, xs, &s_or)) {
+        fail_sync(a, b, writer0);
+        return;
+      }
+      pterm = has ? xs[lane][0] : 0.0;
+      S = wave_sum_d(pterm);
+    }
     // slice masses of q (in units of S) for the sample when no child is rejected
     if (tid < a.KP) cur_sums[tid] = pterm;
     if (kid) {
@@ -655,7 +946,8 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
     if (tid == 0) s_us = k_us;
     __syncthreads();
 
-    // r = max(0, exp(z - M) - CS p) for one group of W entries
+    // r = max(0, exp(z - M) - CS p) for one group of W entries (exp(z - M)
+    // taken as 0 below the filters' threshold)
     auto r_group = [&](int g, double CS, bool use_p, double* rv, int* pnf) {
       float xv[W], pv[W];
       load_group<W>(lrow, lo, hi, g, -INFINITY, xv);
@@ -668,7 +960,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
 #pragma unroll
       for (int j = 0; j < W; ++j) {
         *pnf |= !isfinite(pv[j]);
-        const double e = exp_tab(fma((double)xv[j], invT, -M), s_tab);
+        const double e = kept(xv[j]) ? exp_tab(fma((double)xv[j], invT, -M), s_tab) : 0.0;
         rv[j] = fmax(0.0, e - CS * (double)pv[j]);
       }
     };
@@ -689,7 +981,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
         nxt = c;
         break;
       }
-      const double qx = exp_nonpos((double)s_kl[c] * invT - M) / S;
+      const double qx = kept(s_kl[c]) ? exp_nonpos((double)s_kl[c] * invT - M) / S : 0.0;
       const double cur = fmax(0.0, qx - C * px) / Z;
       const double thr = fmin(1.0, cur / px);
       const float uf = s_ku[c];
@@ -711,7 +1003,8 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
 #pragma unroll
               for (int j = 0; j < W; ++j) {
                 pnf |= !isfinite(pv[gb][j]);
-                const double e = exp_tab(fma((double)xv[gb][j], invT, -M), s_tab);
+                const double e =
+                    kept(xv[gb][j]) ? exp_tab(fma((double)xv[gb][j], invT, -M), s_tab) : 0.0;
                 zp += fmax(0.0, e - CnS * (double)pv[gb][j]);
               }
           }, a.t2d);
@@ -873,7 +1166,7 @@ __global__ void accept_init_kernel(int32_t* tie_count) {
   if (threadIdx.x == 0) *tie_count = 0;
 }
 
-// Launch ids for exchange tags: 40 bits, never 0, distinct for 2^40 launches
+// Launch ids for exchange tags: 32 bits, never 0, distinct for 2^32 launches
 // of this process; the start is drawn from the clock and the process id so
 // that words left in reused memory by another process are unlikely to carry a
 // current tag.
@@ -884,35 +1177,36 @@ uint64_t next_epoch() {
     return (t * 0x9E3779B97F4A7C15ull) ^ ((uint64_t)getpid() << 20);
   }();
   for (;;) {
-    const uint64_t e = (start + counter.fetch_add(1, std::memory_order_relaxed)) & 0xFFFFFFFFFFull;
+    const uint64_t e = (start + counter.fetch_add(1, std::memory_order_relaxed)) & 0xFFFFFFFFull;
     if (e != 0) return e;
   }
 }
 
 typedef void (*accept_fn)(AcceptArgs);
 
-template <bool MAPPED>
+template <bool MAPPED, bool FILT>
 accept_fn pick_variant(int w, int ng) {
   if (w == 4) {
     switch (ng) {
-      case 1: return accept_kernel<1, 4, MAPPED>;
-      case 2: return accept_kernel<2, 4, MAPPED>;
-      case 4: return accept_kernel<4, 4, MAPPED>;
-      case 8: return accept_kernel<8, 4, MAPPED>;
-      default: return accept_kernel<16, 4, MAPPED>;
+      case 1: return accept_kernel<1, 4, MAPPED, FILT>;
+      case 2: return accept_kernel<2, 4, MAPPED, FILT>;
+      case 4: return accept_kernel<4, 4, MAPPED, FILT>;
+      case 8: return accept_kernel<8, 4, MAPPED, FILT>;
+      default: return accept_kernel<16, 4, MAPPED, FILT>;
     }
   }
   switch (ng) {
-    case 1: return accept_kernel<1, 1, MAPPED>;
-    case 2: return accept_kernel<2, 1, MAPPED>;
-    case 4: return accept_kernel<4, 1, MAPPED>;
-    case 8: return accept_kernel<8, 1, MAPPED>;
-    default: return accept_kernel<16, 1, MAPPED>;
+    case 1: return accept_kernel<1, 1, MAPPED, FILT>;
+    case 2: return accept_kernel<2, 1, MAPPED, FILT>;
+    case 4: return accept_kernel<4, 1, MAPPED, FILT>;
+    case 8: return accept_kernel<8, 1, MAPPED, FILT>;
+    default: return accept_kernel<16, 1, MAPPED, FILT>;
   }
 }
 
-accept_fn pick_kernel(int w, int ng, bool mapped = false) {
-  return mapped ? pick_variant<true>(w, ng) : pick_variant<false>(w, ng);
+accept_fn pick_kernel(int w, int ng, bool mapped = false, bool filt = false) {
+  if (filt) return mapped ? pick_variant<true, true>(w, ng) : pick_variant<false, true>(w, ng);
+  return mapped ? pick_variant<true, false>(w, ng) : pick_variant<false, false>(w, ng);
 }
 
 // Inverse of a draft-vocabulary map: t2d[x] = i where x = i + d2t[i], -1 for
@@ -943,25 +1237,28 @@ struct AcceptPlan {
   int NG = 1;      // element groups per thread
   int W = 1;       // entries per group: 4 when rows allow 16-byte loads
   int chunk = 0;   // entries per workgroup
-  size_t ws = 0;
+  size_t ws = 0;   // workspace bytes: exchange words | inverse draft map | histograms
+  size_t off_t2d = 0, off_hist = 0;
 };
 
 // Workgroups of the (W, NG) variant one compute unit holds at once, cached
 // (relaxed atomics: concurrent first calls store the same value).
-int resident_per_cu(int w, int ng, bool mapped) {
-  static std::atomic<int> cache[2][2][5];
+int resident_per_cu(int w, int ng, bool mapped, bool filt) {
+  static std::atomic<int> cache[2][2][2][5];
   const int wi = w == 4 ? 1 : 0;
   const int mi = mapped ? 1 : 0;
+  const int fi = filt ? 1 : 0;
   int ni = 0;
   while ((1 << ni) < ng) ++ni;
-  const int c = cache[mi][wi][ni].load(std::memory_order_relaxed);
+  const int c = cache[fi][mi][wi][ni].load(std::memory_order_relaxed);
   if (c > 0) return c;
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(pick_kernel(w, ng, mapped)), NT, 0) != hipSuccess)
+          &per_cu, reinterpret_cast<const void*>(pick_kernel(w, ng, mapped, filt)), NT, 0) !=
+      hipSuccess)
     per_cu = 1;
   if (per_cu < 1) per_cu = 1;
-  cache[mi][wi][ni].store(per_cu, std::memory_order_relaxed);
+  cache[fi][mi][wi][ni].store(per_cu, std::memory_order_relaxed);
   return per_cu;
 }
 
@@ -970,7 +1267,7 @@ int resident_per_cu(int w, int ng, bool mapped) {
 // are all resident at once, so the whole batch walks in one launch; beyond
 // that (very large batches) the fewest workgroups per
 // sequence, walked in consecutive groups of sequences.
-AcceptPlan make_accept_plan(int B, int V, bool mapped = false) {
+AcceptPlan make_accept_plan(int B, int V, bool mapped = false, bool filters = false) {
   AcceptPlan p;
   p.W = (V % 4) == 0 ? 4 : 1;
   const long per_group = (long)NT * p.W;
@@ -989,7 +1286,7 @@ AcceptPlan make_accept_plan(int B, int V, bool mapped = false) {
     for (int ng = 1; ng <= kMaxNG; ng *= 2) {
       const long kp = (V + per_group * ng - 1) / (per_group * ng);
       if (kp > SPEC_MAX_NODES) continue;
-      if ((long)B * kp <= (long)resident_per_cu(p.W, ng, mapped) * cus) {
+      if ((long)B * kp <= (long)resident_per_cu(p.W, ng, mapped, filters) * cus) {
         best_ng = ng;
         break;
       }
@@ -998,8 +1295,16 @@ AcceptPlan make_accept_plan(int B, int V, bool mapped = false) {
   p.NG = best_ng;
   p.chunk = (int)(per_group * best_ng);
   p.KP = (V + p.chunk - 1) / p.chunk;
+  auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
   p.ws = p.KP > 1 ? (size_t)B * 2 * p.KP * 8 * sizeof(uint64_t) : 256;
-  if (mapped) p.ws = ((p.ws + 255) & ~(size_t)255) + (size_t)V * sizeof(int32_t) + 256;
+  if (mapped) {
+    p.off_t2d = align(p.ws);
+    p.ws = p.off_t2d + (size_t)V * sizeof(int32_t) + 256;
+  }
+  if (filters && p.KP > 1) {
+    p.off_hist = align(p.ws);
+    p.ws = p.off_hist + (size_t)B * 2 * p.KP * 512 * sizeof(uint64_t);
+  }
   return p;
 }
 
@@ -1015,20 +1320,20 @@ extern "C" size_t spec_accept_tree_workspace_size(int32_t B, int32_t n_max, int3
 }
 
 extern "C" size_t spec_accept_tree_ex_workspace_size(int32_t B, int32_t n_max, int32_t V,
-                                                     int32_t Vd) {
+                                                     int32_t Vd, int32_t filters) {
   if (B <= 0 || n_max <= 0 || V <= 0 || Vd < 0 || Vd > V) return 0;
   (void)n_max;
-  return make_accept_plan(B, V, Vd > 0).ws;
+  return make_accept_plan(B, V, Vd > 0, filters != 0).ws;
 }
 
 extern "C" spec_status_t spec_accept_tree_ex(
     const int32_t* tokens, const int32_t* parents, const int32_t* n_nodes, const float* draft_p,
     const float* logits, int32_t B, int32_t n_max, int32_t V, int32_t max_depth,
-    float temperature, const float* temperatures, const int32_t* d2t, int32_t Vd,
-    const float* u_accept, const float* u_sample, int32_t* accept_len, int32_t* path,
-    int32_t* out_tokens, int32_t* n_out, float* final_dist, spec_tie_t* tie_log, int32_t tie_cap,
-    int32_t* tie_count, void* workspace, size_t workspace_bytes, int32_t* dev_error,
-    void* stream) {
+    float temperature, const float* temperatures, const int32_t* top_k, const float* top_p,
+    const int32_t* d2t, int32_t Vd, const float* u_accept, const float* u_sample,
+    int32_t* accept_len, int32_t* path, int32_t* out_tokens, int32_t* n_out, float* final_dist,
+    spec_tie_t* tie_log, int32_t tie_cap, int32_t* tie_count, void* workspace,
+    size_t workspace_bytes, int32_t* dev_error, void* stream) {
   if (!tokens || !parents || !n_nodes || !draft_p || !logits || !u_accept || !u_sample ||
       !accept_len || !path || !out_tokens || !n_out)
     return SPEC_E_NULL;
@@ -1040,7 +1345,8 @@ extern "C" spec_status_t spec_accept_tree_ex(
       (tie_log && tie_cap < 0))
     return SPEC_E_SHAPE;
   if (!temperatures && (!(temperature >= 0.f) || !isfinite(temperature))) return SPEC_E_VALUE;
-  AcceptPlan p = make_accept_plan(B, V, mapped);
+  const bool filters = top_k != nullptr || top_p != nullptr;
+  AcceptPlan p = make_accept_plan(B, V, mapped, filters);
   if (p.KP > SPEC_MAX_NODES) return SPEC_E_SHAPE;
   if (!workspace || workspace_bytes < p.ws) return SPEC_E_WORKSPACE;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
@@ -1055,6 +1361,11 @@ extern "C" spec_status_t spec_accept_tree_ex(
   a.pstride = mapped ? Vd : V;
   a.t2d = nullptr;
   a.t2d_bad = nullptr;
+  a.top_k = top_k;
+  a.top_p = top_p;
+  a.hist = filters && p.KP > 1
+               ? reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + p.off_hist)
+               : nullptr;
   a.u_accept = u_accept; a.u_sample = u_sample;
   a.accept_len = accept_len; a.path = path; a.out_tokens = out_tokens; a.n_out = n_out;
   a.final_dist = final_dist; a.tie_log = tie_log; a.tie_cap = tie_cap; a.tie_count = tie_count;
@@ -1066,7 +1377,7 @@ extern "C" spec_status_t spec_accept_tree_ex(
   // bound, which makes every wait give up at once, to drive the failure path
   a.spin_limit = 1 << 22;
   if (const char* env = getenv("SPEC_ACCEPT_SPIN_LIMIT")) a.spin_limit = atoi(env);
-  const accept_fn fn = pick_kernel(p.W, p.NG, mapped);
+  const accept_fn fn = pick_kernel(p.W, p.NG, mapped, filters);
   const char* coop_env = getenv("SPEC_ACCEPT_COOPERATIVE");
   const bool cooperative = coop_env && coop_env[0] == '1';
 
@@ -1074,7 +1385,7 @@ extern "C" spec_status_t spec_accept_tree_ex(
   // sequence cannot be resident together (their exchanges need that).
   int group = B;
   if (p.KP > 1) {
-    const long resident = (long)resident_per_cu(p.W, p.NG, mapped) * device_cu_count();
+    const long resident = (long)resident_per_cu(p.W, p.NG, mapped, filters) * device_cu_count();
     if (resident < p.KP) return SPEC_E_UNSUPPORTED;
     group = (int)(resident / p.KP < B ? resident / p.KP : B);
   }
@@ -1083,9 +1394,7 @@ extern "C" spec_status_t spec_accept_tree_ex(
     SPEC_HIP_TRY(hipGetLastError());
   }
   if (mapped) {  // inverse map in the workspace, after the exchange words
-    const size_t off = p.KP > 1 ? (((size_t)B * 2 * p.KP * 8 * sizeof(uint64_t) + 255) & ~(size_t)255)
-                                : 256;
-    int32_t* t2d = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + off);
+    int32_t* t2d = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + p.off_t2d);
     int32_t* bad = t2d + V;
     hipLaunchKernelGGL(t2d_fill_kernel, dim3((V + 255) / 256), dim3(256), 0, strm, t2d, V, bad);
     SPEC_HIP_TRY(hipGetLastError());
@@ -1129,7 +1438,7 @@ extern "C" spec_status_t spec_accept_tree(
     int32_t tie_cap, int32_t* tie_count, void* workspace, size_t workspace_bytes,
     int32_t* dev_error, void* stream) {
   return spec_accept_tree_ex(tokens, parents, n_nodes, draft_p, logits, B, n_max, V, max_depth,
-                             temperature, nullptr, nullptr, 0, u_accept, u_sample, accept_len,
-                             path, out_tokens, n_out, final_dist, tie_log, tie_cap, tie_count,
-                             workspace, workspace_bytes, dev_error, stream);
+                             temperature, nullptr, nullptr, nullptr, nullptr, 0, u_accept,
+                             u_sample, accept_len, path, out_tokens, n_out, final_dist, tie_log,
+                             tie_cap, tie_count, workspace, workspace_bytes, dev_error, stream);
 }

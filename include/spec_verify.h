@@ -87,15 +87,16 @@ enum {
 
 /* One near-tie record of spec_accept_tree (kind 0: accept test, 1: sample,
  * 2: residual whose mass fell below 1e-12 of the previous one, so rounding
- * may decide whether it is zero). */
+ * may decide whether it is zero, 3: top-p boundary of spec_accept_tree_ex
+ * within 1e-6 of a kept or dropped token's mass above). */
 typedef struct {
   int32_t b;      /* sequence                                             */
-  int32_t node;   /* child tested (kinds 0, 2) or node sampled at (kind 1) */
+  int32_t node;   /* child tested (kinds 0, 2) or node visited (1, 3)     */
   int32_t kind;
-  float u;        /* the uniform used                                     */
+  float u;        /* the uniform used (kind 3: top_p)                     */
   double margin;  /* |u - min(1, ratio)|; distance of u*W to the chosen
-                     bucket's nearer edge divided by W; or new / old
-                     residual mass                                         */
+                     bucket's nearer edge divided by W; new / old
+                     residual mass; or |mass above - top_p|               */
 } spec_tie_t;
 
 /*
@@ -251,17 +252,28 @@ spec_status_t spec_accept_tree(
 size_t spec_accept_tree_workspace_size(int32_t B, int32_t n_max, int32_t V);
 
 /*
- * spec_accept_tree_ex -- spec_accept_tree with two variants of its inputs
- * ([GUIDE] "一次 eagenerate 调用的完整流转": temperature is a per-call
- * sampling argument, so a batch of requests carries one per sequence;
- * [GUIDE] "代码里能直接读到的三处改动": an EAGLE-3 draft head ranks its own
- * vocabulary and draft id i stands for target token i + d2t[i]).
+ * spec_accept_tree_ex -- spec_accept_tree with variants of its inputs
+ * ([GUIDE] "一次 eagenerate 调用的完整流转": temperature, top_p and top_k are
+ * per-call sampling arguments, so a batch of requests carries them per
+ * sequence; [GUIDE] "代码里能直接读到的三处改动": an EAGLE-3 draft head ranks
+ * its own vocabulary and draft id i stands for target token i + d2t[i]).
  *
  *   temperatures  NULL (the scalar temperature applies), or [B] float32
  *                 device array: sequence b uses q = softmax(logits /
  *                 temperatures[b]), 0 meaning greedy for that sequence; a
  *                 negative or non-finite entry fails its sequence with
  *                 SPEC_DEVERR_NONFINITE
+ *   top_k, top_p  NULL, or [B] int32 / float32 device arrays: sampling
+ *                 filters on the verifier's q at T > 0 (greedy decoding is
+ *                 unaffected).  Top-k keeps the tokens whose logit is at
+ *                 least the k-th largest of the row (ties kept together);
+ *                 top-p keeps a token when the tempered q-mass of the tokens
+ *                 with strictly larger logits is below p; a token must pass
+ *                 both, and q is renormalised over the kept tokens before
+ *                 the acceptance tests, residuals and samples.  k <= 0 or
+ *                 k >= V, and p <= 0 or p >= 1, turn a filter off for that
+ *                 sequence; a NaN p fails it with SPEC_DEVERR_NONFINITE.
+ *                 Boundaries within 1e-6 of p are logged (tie kind 3).
  *   d2t, Vd       NULL (draft_p rows hold V entries), or [Vd] int32 device
  *                 array with 1 <= Vd <= V: draft_p rows hold Vd entries over
  *                 the draft vocabulary, and the draft probability of target
@@ -269,22 +281,26 @@ size_t spec_accept_tree_workspace_size(int32_t B, int32_t n_max, int32_t V);
  *                 if there is none.  A map that leaves [0, V) or sends two
  *                 draft ids to one token fails every sequence with
  *                 SPEC_DEVERR_TOKEN.  Tree tokens stay target ids.
- *   workspace     >= spec_accept_tree_ex_workspace_size(B, n_max, V, Vd)
- *                 bytes (Vd = 0 without d2t); with d2t it also holds the
- *                 inverse map, which the call builds first
- * Everything else as spec_accept_tree, which is this call with both NULL.
+ *   workspace     >= spec_accept_tree_ex_workspace_size(B, n_max, V, Vd,
+ *                 filters) bytes (Vd = 0 without d2t; filters nonzero when
+ *                 top_k or top_p is given); with d2t it also holds the
+ *                 inverse map, which the call builds first, and with filters
+ *                 the per-round histograms the workgroups exchange
+ * Everything else as spec_accept_tree, which is this call with all four NULL.
  */
 spec_status_t spec_accept_tree_ex(
     const int32_t* tokens, const int32_t* parents, const int32_t* n_nodes,
     const float* draft_p, const float* logits,
     int32_t B, int32_t n_max, int32_t V, int32_t max_depth, float temperature,
-    const float* temperatures, const int32_t* d2t, int32_t Vd,
+    const float* temperatures, const int32_t* top_k, const float* top_p,
+    const int32_t* d2t, int32_t Vd,
     const float* u_accept, const float* u_sample,
     int32_t* accept_len, int32_t* path, int32_t* out_tokens, int32_t* n_out,
     float* final_dist, spec_tie_t* tie_log, int32_t tie_cap, int32_t* tie_count,
     void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream);
 
-size_t spec_accept_tree_ex_workspace_size(int32_t B, int32_t n_max, int32_t V, int32_t Vd);
+size_t spec_accept_tree_ex_workspace_size(int32_t B, int32_t n_max, int32_t V, int32_t Vd,
+                                          int32_t filters);
 
 /*
  * spec_kv_commit -- commit the accepted path ([LESSON] "KV cache 回滚" and

@@ -7,7 +7,7 @@ import pytest
 
 from eagle_tree_verification_amd import api
 
-SPEC_E_NULL, SPEC_E_SHAPE, SPEC_E_DTYPE, SPEC_E_VALUE = -1, -2, -3, -4
+SPEC_E_NULL, SPEC_E_SHAPE, SPEC_E_DTYPE, SPEC_E_VALUE, SPEC_E_WORKSPACE = -1, -2, -3, -4, -5
 
 
 @pytest.fixture(scope="module")
@@ -176,20 +176,30 @@ def test_rope_host_checks(lib):
 def test_accept_ex_host_checks(lib):
     P = _buf()
     f = lib.spec_accept_tree_ex
-    # tokens, parents, n_nodes, draft_p, logits, B, n_max, V, max_depth, T, temps, d2t, Vd,
-    # u_accept, u_sample, accept_len, path, out_tokens, n_out, final_dist, tie_log, tie_cap,
-    # tie_count, workspace, ws_bytes, dev_error, stream
-    args = ([P] * 5 + [2, 6, 100, 5, 1.0, None, None, 0] + [P] * 6 +
+    # tokens, parents, n_nodes, draft_p, logits, B, n_max, V, max_depth, T, temps, top_k,
+    # top_p, d2t, Vd, u_accept, u_sample, accept_len, path, out_tokens, n_out, final_dist,
+    # tie_log, tie_cap, tie_count, workspace, ws_bytes, dev_error, stream
+    args = ([P] * 5 + [2, 6, 100, 5, 1.0, None, None, None, None, 0] + [P] * 6 +
             [None, None, 0, None, P, 1 << 20, None, None])
     assert f(*([None] + args[1:])) == SPEC_E_NULL
     bad = list(args); bad[9] = -1.0        # scalar temperature checked without the array
     assert f(*bad) == SPEC_E_VALUE
-    bad = list(args); bad[11] = P; bad[12] = 0     # d2t needs 1 <= Vd <= V
+    bad = list(args); bad[13] = P; bad[14] = 0     # d2t needs 1 <= Vd <= V
     assert f(*bad) == SPEC_E_SHAPE
-    bad = list(args); bad[11] = P; bad[12] = 101
+    bad = list(args); bad[13] = P; bad[14] = 101
     assert f(*bad) == SPEC_E_SHAPE
-    assert lib.spec_accept_tree_ex_workspace_size(4, 8, 1000, 0) == \
-        lib.spec_accept_tree_workspace_size(4, 8, 1000)
-    assert lib.spec_accept_tree_ex_workspace_size(4, 8, 1000, 300) >= \
-        lib.spec_accept_tree_workspace_size(4, 8, 1000) + 4 * 1000
-    assert lib.spec_accept_tree_ex_workspace_size(4, 8, 1000, 1001) == 0
+    ws = lib.spec_accept_tree_ex_workspace_size
+    assert ws(4, 8, 1000, 0, 0) == lib.spec_accept_tree_workspace_size(4, 8, 1000)
+    assert ws(4, 8, 1000, 300, 0) >= lib.spec_accept_tree_workspace_size(4, 8, 1000) + 4 * 1000
+    # filters add one histogram buffer pair per sequence when a row spans workgroups
+    V = 128256
+    base, filt = ws(64, 61, V, 0, 0), ws(64, 61, V, 0, 1)
+    assert filt >= base
+    assert ws(64, 61, V, 32000, 1) >= filt + 4 * V
+    # a filtered call with only the unfiltered workspace is refused on the host
+    small = lib.spec_accept_tree_workspace_size(2, 6, V)
+    wide = ws(2, 6, V, 0, 1)
+    if wide > small:
+        bad = list(args); bad[7] = V; bad[11] = P; bad[26] = small
+        assert f(*bad) == SPEC_E_WORKSPACE
+    assert ws(4, 8, 1000, 1001, 0) == 0

@@ -1,7 +1,7 @@
-"""GPU parity of spec_accept_tree_ex: per-sequence temperatures and a draft
-distribution held over an EAGLE-3 draft vocabulary (d2t), against the oracle
-(oracle.accept_tree with each sequence's temperature; oracle.draft_p_to_target
-for the draft vocabulary).
+"""GPU parity of spec_accept_tree_ex: per-sequence temperatures, top-k /
+top-p filters on q, and a draft distribution held over an EAGLE-3 draft
+vocabulary (d2t), against the oracle (oracle.accept_tree with each sequence's
+temperature and filters; oracle.draft_p_to_target for the draft vocabulary).
 
 Bars as for spec_accept_tree: accepted lengths, paths and tokens bit-exact
 except sequences with a logged near tie; residual distributions within 1e-5.
@@ -19,12 +19,14 @@ from gpu_helpers import say
 pytestmark = pytest.mark.gpu
 
 
-def _run(api, w, dev, draft_p, *, temperatures=None, d2t=None, T=None, tokens=None):
+def _run(api, w, dev, draft_p, *, temperatures=None, d2t=None, T=None, tokens=None, top_k=None,
+         top_p=None, logits=None):
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     res = api.accept_tree(tokens if tokens is not None else dev["tokens"], dev["parents"],
-                          dev["n_nodes"], draft_p, dev["logits"], w.T if T is None else T,
-                          dev["u_accept"], dev["u_sample"], w.max_depth, final_dist=True,
-                          tie_cap=4096, dev_error=err, temperatures=temperatures, d2t=d2t)
+                          dev["n_nodes"], draft_p, dev["logits"] if logits is None else logits,
+                          w.T if T is None else T, dev["u_accept"], dev["u_sample"], w.max_depth,
+                          final_dist=True, tie_cap=4096, dev_error=err, temperatures=temperatures,
+                          d2t=d2t, top_k=top_k, top_p=top_p)
     torch.cuda.synchronize()
     host = {k: v.cpu().numpy() for k, v in res.items() if isinstance(v, torch.Tensor) and k != "tie_log"}
     host["ties"] = api.decode_ties(res["tie_log"], res["tie_count"])
@@ -32,14 +34,17 @@ def _run(api, w, dev, draft_p, *, temperatures=None, d2t=None, T=None, tokens=No
     return host
 
 
-def _compare(w, host, temps, p_rows, tokens, seqs=None):
-    """Oracle per sequence at its own temperature; returns excluded sequences."""
+def _compare(w, host, temps, p_rows, tokens, seqs=None, top_k=None, top_p=None, logits=None):
+    """Oracle per sequence at its own temperature and filters; returns the
+    excluded (near-tie) sequences."""
     gpu_tie = set(int(t["b"]) for t in host["ties"])
+    logits = w.logits if logits is None else logits
     excluded = []
     for b in (range(w.B) if seqs is None else seqs):
-        r = oracle.accept_tree(tokens[b], w.parents[b], w.n_nodes[b], p_rows(b), w.logits[b],
+        r = oracle.accept_tree(tokens[b], w.parents[b], w.n_nodes[b], p_rows(b), logits[b],
                                float(temps[b]), w.u_accept[b], w.u_sample[b], w.max_depth,
-                               n_max=w.n_max)
+                               n_max=w.n_max, top_k=0 if top_k is None else int(top_k[b]),
+                               top_p=0.0 if top_p is None else float(top_p[b]))
         if r.near_tie or b in gpu_tie:
             excluded.append(b)
             continue
@@ -171,5 +176,131 @@ def test_draft_vocabulary_full_size(hip_lib):
     sample = sorted(np.random.default_rng(3).choice(w.B, size=6, replace=False).tolist())
     excluded = _compare(w, host, temps, lambda b: oracle.draft_p_to_target(pd[b], d2t, w.V),
                         tokens, seqs=sample)
+    say(f"[gpu]   sampled {sample}; near-tie excluded {excluded}")
+    assert len(excluded) <= 2
+
+
+# ----------------------------------------------------------------------------
+# top-k / top-p filters on q
+# ----------------------------------------------------------------------------
+K_CHOICES = np.array([0, 1, 2, 7, 40, 1000, -3], np.int32)
+P_CHOICES = np.array([0.0, 0.3, 0.6, 0.8, 0.9, 1e-30, 1.0], np.float32)
+
+
+def _filters(B, V, seed):
+    rng = np.random.default_rng(seed)
+    k = rng.choice(np.append(K_CHOICES, [V - 1, V, V + 5]).astype(np.int32), size=B)
+    p = rng.choice(P_CHOICES, size=B)
+    return k.astype(np.int32), p.astype(np.float32)
+
+
+FILTER_CASES = {
+    # name: (make_workload kwargs, logit rounding step or None)
+    "c1-kp1": (dict(cfg=1, T=1.0), None),                                   # V 1000: one workgroup
+    "c4-w1": (dict(cfg=4, batch=12, prefix=(1, 64), vocab=5003), None),     # ragged V, KP > 1
+    "c4-w4": (dict(cfg=4, batch=16, prefix=(1, 64), vocab=20000), None),    # 16-byte loads, KP > 1
+    "c4-ties": (dict(cfg=4, batch=16, prefix=(1, 64), vocab=20000), 0.25),  # many equal logits
+    "c3-t07": (dict(cfg=3, batch=8, prefix=(1, 64), vocab=3001, T=0.7), None),
+}
+
+
+@pytest.mark.parametrize("name", list(FILTER_CASES))
+def test_sampling_filters(hip_lib, name):
+    api = hip_lib
+    kw, step = FILTER_CASES[name]
+    w = make_workload(poison=True, **kw)
+    logits = w.logits if step is None else (np.round(w.logits / step) * step).astype(np.float32)
+    k, p = _filters(w.B, w.V, 41 + w.V)
+    k[0], p[0] = 2, 0.0           # top-k alone
+    p[1 % w.B], k[1 % w.B] = 0.9, 0   # top-p alone
+    temps = np.full(w.B, w.T, np.float32)
+    say(f"[gpu] filters {name}: B={w.B} V={w.V} T={w.T} k={k.tolist()} p={p.tolist()}")
+    dev = to_device(w)
+    lg = torch.from_numpy(logits).to("cuda")
+    host = _run(api, w, dev, dev["draft_p"], logits=lg, top_k=torch.from_numpy(k).to("cuda"),
+                top_p=torch.from_numpy(p).to("cuda"))
+    assert host["dev_error"] == 0
+    excluded = _compare(w, host, temps, lambda b: w.draft_p[b], w.tokens, top_k=k, top_p=p,
+                        logits=logits)
+    say(f"[gpu]   near-tie sequences excluded: {excluded}; "
+        f"top-p boundary logs {sum(int(t['kind']) == 3 for t in host['ties'])}")
+    assert len(excluded) <= max(1, w.B // 4)
+    # a filtered final distribution is zero outside the kept set
+    for b in range(w.B):
+        if b in excluded or host["accept_len"][b] < 0:
+            continue
+        v = int(host["path"][b, host["accept_len"][b]])
+        keep, _ = oracle.filter_keep(logits[b, v], float(w.T), int(k[b]), float(p[b]))
+        assert np.all(host["final_dist"][b][~keep] == 0.0), b
+
+
+def test_filters_off_are_bit_identical(hip_lib):
+    """k <= 0 or k >= V and p <= 0 or p >= 1 turn the filters off: outputs
+    bit-identical to the unfiltered call (same kernels, threshold -inf)."""
+    api = hip_lib
+    w = make_workload(poison=True, cfg=4, batch=8, prefix=(1, 64), vocab=20000)
+    dev = to_device(w)
+    base = _run(api, w, dev, dev["draft_p"])
+    k = np.array([0, -1, w.V, w.V + 9, 0, 0, -7, w.V], np.int32)
+    p = np.array([0.0, 1.0, 0.0, 2.5, -0.5, 1.0, 0.0, 0.0], np.float32)
+    off = _run(api, w, dev, dev["draft_p"], top_k=torch.from_numpy(k).to("cuda"),
+               top_p=torch.from_numpy(p).to("cuda"))
+    for key in ("accept_len", "path", "out_tokens", "n_out", "final_dist"):
+        np.testing.assert_array_equal(off[key], base[key], err_msg=key)
+
+
+def test_filters_at_greedy_and_with_a_nan_top_p(hip_lib):
+    api = hip_lib
+    w = make_workload(poison=True, cfg=4, batch=6, prefix=(1, 64), vocab=5003)
+    dev = to_device(w)
+    temps = np.array([0.0, 0.0, 1.0, 1.0, 0.8, 1.2], np.float32)
+    k = np.array([1, 3, 5, 0, 2, 9], np.int32)
+    p = np.array([0.1, 0.5, 0.7, np.nan, 0.9, 0.2], np.float32)
+    host = _run(api, w, dev, dev["draft_p"], temperatures=torch.from_numpy(temps).to("cuda"),
+                top_k=torch.from_numpy(k).to("cuda"), top_p=torch.from_numpy(p).to("cuda"))
+    assert host["dev_error"] == api.DEVERR_NONFINITE
+    assert host["accept_len"][3] == -1 and host["n_out"][3] == 0
+    # greedy sequences ignore the filters: same as greedy without them
+    plain = _run(api, w, dev, dev["draft_p"], temperatures=torch.from_numpy(temps).to("cuda"))
+    for b in (0, 1):
+        for key in ("accept_len", "path", "out_tokens"):
+            np.testing.assert_array_equal(host[key][b], plain[key][b], err_msg=key)
+    _compare(w, host, temps, lambda b: w.draft_p[b], w.tokens, seqs=[0, 1, 2, 4, 5], top_k=k,
+             top_p=p)
+
+
+def test_filters_with_a_draft_vocabulary(hip_lib):
+    api = hip_lib
+    w = make_workload(poison=True, cfg=4, batch=10, prefix=(1, 64), vocab=20000)
+    d2t, pd, tokens = _draft_vocab(w, 6000, 77)
+    k, p = _filters(w.B, w.V, 5)
+    dev = to_device(w)
+    host = _run(api, w, dev, torch.from_numpy(pd).to("cuda"), d2t=torch.from_numpy(d2t).to("cuda"),
+                tokens=torch.from_numpy(tokens).to("cuda"), top_k=torch.from_numpy(k).to("cuda"),
+                top_p=torch.from_numpy(p).to("cuda"))
+    assert host["dev_error"] == 0
+    excluded = _compare(w, host, np.full(w.B, w.T), lambda b: oracle.draft_p_to_target(pd[b], d2t, w.V),
+                        tokens, top_k=k, top_p=p)
+    assert len(excluded) <= max(1, w.B // 4)
+
+
+@pytest.mark.timeout(900)
+def test_filters_full_size(hip_lib):
+    """Batch 64 over the 128256-token vocabulary with a per-sequence mix of
+    top-k, top-p and temperature, a sample of sequences against the oracle."""
+    api = hip_lib
+    w = make_workload(4)
+    k, p = _filters(w.B, w.V, 9)
+    k[:4] = [50, 0, 1, 20]
+    p[:4] = [0.0, 0.95, 0.0, 0.8]
+    temps = np.random.default_rng(8).choice(np.array([0.6, 1.0, 1.3], np.float32), size=w.B)
+    dev = to_device(w)
+    host = _run(api, w, dev, dev["draft_p"], temperatures=torch.from_numpy(temps).to("cuda"),
+                top_k=torch.from_numpy(k).to("cuda"), top_p=torch.from_numpy(p).to("cuda"))
+    assert host["dev_error"] == 0
+    sample = sorted(set([0, 1, 2, 3]) | set(np.random.default_rng(4).choice(w.B, size=4,
+                                                                           replace=False).tolist()))
+    excluded = _compare(w, host, temps, lambda b: w.draft_p[b], w.tokens, seqs=sample, top_k=k,
+                        top_p=p)
     say(f"[gpu]   sampled {sample}; near-tie excluded {excluded}")
     assert len(excluded) <= 2
