@@ -4,8 +4,9 @@ Plain, slow, float64 NumPy reference of the three steps of the verify path:
 tree-masked attention (`attention`), the Leviathan acceptance walk down the
 draft tree (`accept`) and the KV commit (`commit`), plus the step before it,
 EAGLE-2's construction of the draft tree from draft probabilities (`tree`),
-and the rotary position embedding of tree nodes with the write of their K/V
-into the cache (`rope`).  Every function cites the
+the rotary position embedding of tree nodes with the write of their K/V
+into the cache (`rope`), and the logical view of a cache held in blocks
+through a block table (`paged`).  Every function cites the
 passage of the pages it follows.  Pages cited throughout:
 
   * "推测解码与 EAGLE-3" -- a lesson on speculative decoding and EAGLE-3
@@ -29,4 +30,5 @@ from .accept import (AcceptResult, accept_tree, accept_rule, residual,  # noqa: 
 from .commit import kv_commit, kv_commit_from_buffer  # noqa: F401
 from .tree import TreeBuilder, build_tree  # noqa: F401
 from .rope import rope_rotate, node_positions, tree_kv_write  # noqa: F401
+from . import paged  # noqa: F401
 from .validate import validate_tree, ERR_TREE, ERR_TOKEN, ERR_NONFINITE, ERR_CAPACITY  # noqa: F401
