@@ -430,6 +430,55 @@ def tree_build_bench(B, top_k, depth, Vd, total, reps=20):
     return res
 
 
+def paged_bench(w, dev, ws_attn, block_size=16, reps=20):
+    """Tree attention over a paged cache: the workload's K/V scattered to a
+    shuffled pool of block_size-row blocks (plus spare blocks), timed against
+    the contiguous call on the same logical contents, interleaved."""
+    import torch
+    from eagle_tree_verification_amd import api
+
+    if w.L_cap % block_size:
+        return {"skipped": f"L_cap {w.L_cap} not a multiple of {block_size}"}
+    mb = w.L_cap // block_size
+    spare = 64
+    gen = torch.Generator(device="cuda").manual_seed(6)
+    perm = torch.randperm(w.B * mb + spare, generator=gen, device="cuda")
+    table = perm[: w.B * mb].reshape(w.B, mb).to(torch.int32).contiguous()
+
+    def to_pool(c):
+        blocks = c.reshape(w.B, w.Hkv, mb, block_size, w.d).permute(0, 2, 1, 3, 4)
+        pool = torch.zeros((w.B * mb + spare, w.Hkv, block_size, w.d), dtype=c.dtype, device="cuda")
+        pool[table.reshape(-1).long()] = blocks.reshape(w.B * mb, w.Hkv, block_size, w.d)
+        return pool
+
+    kp, vp = to_pool(dev["k_cache"]), to_pool(dev["v_cache"])
+    out_c = torch.empty((w.B, w.n_max, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    out_p = torch.empty_like(out_c)
+    fc = lambda: api.verify_tree_attn(dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"],
+                                      dev["n_nodes"], dev["parents"], out=out_c, workspace=ws_attn)
+    fp = lambda: api.verify_tree_attn_paged(dev["q"], kp, vp, table, dev["prefix_len"],
+                                            dev["n_nodes"], dev["parents"], out=out_p,
+                                            workspace=ws_attn)
+    fc(); fp()
+    torch.cuda.synchronize()
+    tc, tp = [], []
+    for _ in range(reps):
+        for fn, acc in ((fc, tc), (fp, tp)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            acc.append(e0.elapsed_time(e1))
+    same = all(torch.equal(out_c[b, : int(w.n_nodes[b])], out_p[b, : int(w.n_nodes[b])])
+               for b in range(w.B))
+    res = {"block_size": block_size, "pool_blocks": int(w.B * mb + spare),
+           "contiguous_attn_ms": round(float(np.median(tc)), 4),
+           "paged_attn_ms": round(float(np.median(tp)), 4), "bit_identical": bool(same)}
+    del kp, vp
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -446,6 +495,8 @@ def main():
                     help="skip timing the walk with per-sequence temperatures and a draft vocabulary")
     ap.add_argument("--no-tree-build", action="store_true",
                     help="skip timing the EAGLE-2 tree construction")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip timing tree attention over a paged (block-table) cache")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -580,6 +631,8 @@ def main():
                                                  ws_acc)
     if not args.no_tree_build:
         rec["tree_build"] = tree_build_bench(w.B, 10, cfg.depth, w.V, cfg.drafts)
+    if not args.no_paged:
+        rec["paged"] = paged_bench(w, dev, ws_attn)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

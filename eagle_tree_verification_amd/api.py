@@ -78,6 +78,15 @@ def load():
     lib.spec_tree_expand.restype = I
     lib.spec_tree_finalize.argtypes = [P, Z, I, I, I, I, P, P, I, P, P, P, P, P, P, P, P, P, P]
     lib.spec_tree_finalize.restype = I
+    lib.spec_verify_tree_attn_paged.argtypes = [P, P, P, P, I, I, I, P, P, P, I, I, I, I, I, F, I,
+                                                P, I, P, P, Z, P, P]
+    lib.spec_verify_tree_attn_paged.restype = I
+    lib.spec_tree_kv_write_paged.argtypes = [P, P, P, P, P, I, I, I, P, P, P, I, I, I, I, I, P, I,
+                                             P, P]
+    lib.spec_tree_kv_write_paged.restype = I
+    lib.spec_kv_commit_layers_paged.argtypes = [P, P, P, P, I, P, I, I, I, P, P, P, I, I, I, I, I,
+                                                I, P, P]
+    lib.spec_kv_commit_layers_paged.restype = I
     lib.spec_status_string.argtypes = [I]
     lib.spec_status_string.restype = ctypes.c_char_p
     lib.spec_abi_version.argtypes = []
@@ -454,3 +463,110 @@ def tree_finalize(state, B, top_k, depth, total_tokens, n_max, *, root_token=Non
                                 _stream(stream))
     _check("spec_tree_finalize", st)
     return o
+
+
+# ----------------------------------------------------------------------------
+# Paged caches: per layer a pool [num_blocks][Hkv][block_size][d] and a
+# [B][max_blocks] int32 block table (logical row r of sequence b is row
+# r % block_size of block block_table[b][r // block_size]).
+# ----------------------------------------------------------------------------
+def _paged_geometry(k_pool, block_table):
+    num_blocks, Hkv, block_size, d = k_pool.shape
+    _dev(block_table, "block_table", torch.int32)
+    B, max_blocks = block_table.shape
+    return B, num_blocks, Hkv, block_size, d, max_blocks
+
+
+def verify_tree_attn_paged(q, k_pool, v_pool, block_table, prefix_len, n_nodes, parents, *,
+                           scale=None, out=None, workspace=None, dev_error=None, stream=None,
+                           inv_freq=None, rope_style="half"):
+    """verify_tree_attn on a paged cache; returns out [B][n_max][Hq][d] float32."""
+    lib = load()
+    B, n_max, Hq, d = q.shape
+    Bt, num_blocks, Hkv, bs, d_, max_blocks = _paged_geometry(k_pool, block_table)
+    if Bt != B or d_ != d or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("pools must be [num_blocks][Hkv][block_size][d], table [B][max_blocks]")
+    dt = _kv_dtype(k_pool)
+    for t, nm in ((q, "q"), (k_pool, "k_pool"), (v_pool, "v_pool")):
+        _dev(t, nm, k_pool.dtype)
+    for t, nm in ((prefix_len, "prefix_len"), (n_nodes, "n_nodes"), (parents, "parents")):
+        _dev(t, nm, torch.int32)
+    if inv_freq is not None:
+        _dev(inv_freq, "inv_freq", torch.float32)
+    if out is None:
+        out = torch.empty((B, n_max, Hq, d), dtype=torch.float32, device=q.device)
+    _dev(out, "out", torch.float32)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(d))
+    ws, wsb = _workspace(verify_tree_attn_workspace_size(B, n_max, Hq, Hkv, d, max_blocks * bs, dt),
+                         q.device, workspace)
+    st = lib.spec_verify_tree_attn_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                         max_blocks, bs, num_blocks, _ptr(prefix_len),
+                                         _ptr(n_nodes), _ptr(parents), B, n_max, Hq, Hkv, d,
+                                         float(scale), dt, _ptr(inv_freq),
+                                         ROPE_STYLES[rope_style], _ptr(out), _ptr(ws), wsb,
+                                         _ptr(dev_error), _stream(stream))
+    _check("spec_verify_tree_attn_paged", st)
+    return out
+
+
+def tree_kv_write_paged(k_new, v_new, k_pool, v_pool, block_table, prefix_len, n_nodes, parents,
+                        *, inv_freq=None, rope_style="half", dev_error=None, stream=None):
+    """tree_kv_write into a paged cache."""
+    lib = load()
+    B, n_max, Hkv, d = k_new.shape
+    Bt, num_blocks, Hp, bs, d_, max_blocks = _paged_geometry(k_pool, block_table)
+    if (Bt, Hp, d_) != (B, Hkv, d) or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("k_new [B][n_max][Hkv][d] must match the pools and table")
+    dt = _kv_dtype(k_pool)
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new"), (k_pool, "k_pool"), (v_pool, "v_pool")):
+        _dev(t, nm, k_pool.dtype)
+    for t, nm in ((prefix_len, "prefix_len"), (n_nodes, "n_nodes"), (parents, "parents")):
+        _dev(t, nm, torch.int32)
+    if inv_freq is not None:
+        _dev(inv_freq, "inv_freq", torch.float32)
+    st = lib.spec_tree_kv_write_paged(_ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool),
+                                      _ptr(block_table), max_blocks, bs, num_blocks,
+                                      _ptr(prefix_len), _ptr(n_nodes), _ptr(parents), B, n_max,
+                                      Hkv, d, dt, _ptr(inv_freq), ROPE_STYLES[rope_style],
+                                      _ptr(dev_error), _stream(stream))
+    _check("spec_tree_kv_write_paged", st)
+
+
+def kv_commit_layers_paged(k_pools, v_pools, block_table, prefix_len, path, accept_len, max_depth,
+                           *, k_tree=None, v_tree=None, dev_error=None, stream=None):
+    """kv_commit_layers on per-layer pools sharing one block table.  Returns
+    the pointer tables, which must stay alive until the stream work
+    completes."""
+    lib = load()
+    k_pools, v_pools = list(k_pools), list(v_pools)
+    if len(v_pools) != len(k_pools):
+        raise ValueError("k_pools and v_pools differ in length")
+    B, num_blocks, Hkv, bs, d, max_blocks = _paged_geometry(k_pools[0], block_table)
+    dt = _kv_dtype(k_pools[0])
+    kt = _pointer_table(k_pools, "k_pools")
+    vt = _pointer_table(v_pools, "v_pools", like=k_pools[0])
+    n_max = 0
+    tk = tv = None
+    if (k_tree is None) != (v_tree is None):
+        raise ValueError("give both k_tree and v_tree, or neither")
+    if k_tree is not None:
+        k_tree, v_tree = list(k_tree), list(v_tree)
+        if len(k_tree) != len(k_pools) or len(v_tree) != len(k_pools):
+            raise ValueError("one scratch buffer per layer")
+        Bt, Ht, n_max, dt_ = k_tree[0].shape
+        if (Bt, Ht, dt_) != (B, Hkv, d):
+            raise ValueError("scratch rows must be [B][Hkv][n_max][head_dim]")
+        if k_tree[0].dtype != k_pools[0].dtype:
+            raise ValueError("scratch rows and pools must share a dtype")
+        tk = _pointer_table(k_tree, "k_tree", like=k_tree[0])
+        tv = _pointer_table(v_tree, "v_tree", like=k_tree[0])
+    for t, nm in ((prefix_len, "prefix_len"), (path, "path"), (accept_len, "accept_len")):
+        _dev(t, nm, torch.int32)
+    st = lib.spec_kv_commit_layers_paged(_ptr(kt), _ptr(vt), _ptr(tk), _ptr(tv), len(k_pools),
+                                         _ptr(block_table), max_blocks, bs, num_blocks,
+                                         _ptr(prefix_len), _ptr(path), _ptr(accept_len), B, n_max,
+                                         Hkv, d, int(max_depth), dt, _ptr(dev_error),
+                                         _stream(stream))
+    _check("spec_kv_commit_layers_paged", st)
+    return (kt, vt, tk, tv)

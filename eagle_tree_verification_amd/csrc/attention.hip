@@ -70,7 +70,7 @@ template <typename T>
 __global__ __launch_bounds__(64) void attn_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ prefix_len, const int32_t* __restrict__ n_nodes,
-    const int32_t* __restrict__ parents, int n_max, int Hq, int Hkv, int d, int L_cap,
+    const int32_t* __restrict__ parents, int n_max, int Hq, int Hkv, int d, KvRows kv,
     float c, const float* __restrict__ inv_freq, int rope, float* __restrict__ out,
     int32_t* dev_error) {
   __shared__ uint64_t anc[64];
@@ -88,12 +88,16 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
     if (reporter) report(dev_error, SPEC_DEVERR_TREE);
     return;
   }
-  if (L < 0 || (int64_t)L + n > L_cap) {
+  if (L < 0 || (int64_t)L + n > kv.L_cap) {
     if (reporter) report(dev_error, SPEC_DEVERR_CAPACITY);
     return;
   }
   if (!build_ancestors(parents + (size_t)b * n_max, n, anc, &flag)) {
     if (reporter) report(dev_error, SPEC_DEVERR_TREE);
+    return;
+  }
+  if (!kv.blocks_ok(b, 0, L + n)) {
+    if (reporter) report(dev_error, SPEC_DEVERR_CAPACITY);
     return;
   }
   if (i >= n) return;
@@ -122,8 +126,6 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
     __syncthreads();
   }
 
-  const T* kb = kc + ((size_t)b * Hkv + g) * (size_t)L_cap * d;
-  const T* vb = vc + ((size_t)b * Hkv + g) * (size_t)L_cap * d;
   const int total = L + npath;
   float m = -INFINITY, l = 0.f, acc0 = 0.f, acc1 = 0.f;
   for (int c0 = 0; c0 < total; c0 += 64) {
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
     const int row = valid ? (t < L ? t : rows[t - L]) : 0;
     float s = -INFINITY;
     if (valid) {
-      const T* kr = kb + (size_t)row * d;
+      const T* kr = kc + kv.offset(b, g, row, d);
       float dot = 0.f;
       for (int k = 0; k < d; ++k) dot = fmaf(qs[k], load_as_f32(kr + k), dot);
       s = dot * c;
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
     for (int kk = 0; kk < cnt; ++kk) {
       const float w = __shfl(p, kk);
       const int r = __shfl(row, kk);
-      const T* vr = vb + (size_t)r * d;
+      const T* vr = vc + kv.offset(b, g, r, d);
       if (lane < d) acc0 = fmaf(w, load_as_f32(vr + lane), acc0);
       if (lane + 64 < d) acc1 = fmaf(w, load_as_f32(vr + lane + 64), acc1);
     }
@@ -181,6 +183,7 @@ struct MfmaArgs {
   const int32_t* n_nodes;
   const int32_t* parents;
   int B, n_max, Hq, Hkv, G, L_cap;
+  KvRows kv;   // where cache rows live (contiguous, or paged through a block table)
   int RB;      // row blocks per (b, g)
   int S_max;   // prefix splits
   int chunk;   // prefix keys per split (multiple of KT)
@@ -199,7 +202,9 @@ struct MfmaArgs {
 // normal range flush to zero, which is harmless for softmax weights.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int NB, int NW, int SUB>
+// PAGED: cache rows are found through the block table (a.kv); otherwise the
+// cache is contiguous and the kernel never looks at a.kv.table.
+template <int NB, int NW, int SUB, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
   constexpr int NT = NW * 64;
   constexpr int RPW = NW * NB * 32;                    // query rows per workgroup
@@ -265,6 +270,10 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
   if (rb * RPW >= Mb) return;
   if (!build_ancestors(a.parents + (size_t)b * a.n_max, n, anc, &flag)) {
     if (reporter) report(a.dev_error, SPEC_DEVERR_TREE);
+    return;
+  }
+  if (PAGED && !a.kv.blocks_ok(b, 0, L + n)) {
+    if (reporter) report(a.dev_error, SPEC_DEVERR_CAPACITY);
     return;
   }
   const bool last = (s == nsplit - 1);
@@ -340,19 +349,52 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
     nrows = t < ntp ? min(ST, ke0 - row0) : n;
   };
 
+  // Paged: the physical block of each of this thread's rows of a stage,
+  // read from the block table one stage before the rows themselves, so the
+  // table's latency never delays the K/V loads.  The read is unconditional
+  // (index clamped into the sequence's table row): a conditional one would
+  // leave a register copy that waits for every outstanding load.  Entries
+  // for rows past the stage are never used.
+  int tblk[CH];
+  auto table_entries = [&](int t) {
+    if constexpr (PAGED) {
+      int row0, nrows;
+      stage_rows(t, row0, nrows);
+      const int32_t* trow = a.kv.table + (size_t)b * a.kv.max_blocks;
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int r = (tid + j * NT) >> 4;
+        tblk[j] = trow[min((row0 + r) >> a.kv.bs_log2, a.kv.max_blocks - 1)];
+      }
+    }
+  };
+
   uint4 kreg[CH], vreg[CH];
   auto load_stage = [&](int t) {
     int row0, nrows;
     stage_rows(t, row0, nrows);
-    const uint16_t* kbase = kbg + (size_t)row0 * HD;
-    const uint16_t* vbase = vbg + (size_t)row0 * HD;
+    if constexpr (PAGED) {
+      const int mask = (1 << a.kv.bs_log2) - 1;
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int cidx = tid + j * NT;
-      const int r = cidx >> 4;
-      const size_t off = (size_t)r * HD + (cidx & 15) * 8;
-      kreg[j] = r < nrows ? *reinterpret_cast<const uint4*>(kbase + off) : make_uint4(0, 0, 0, 0);
-      vreg[j] = r < nrows ? *reinterpret_cast<const uint4*>(vbase + off) : make_uint4(0, 0, 0, 0);
+      for (int j = 0; j < CH; ++j) {
+        const int cidx = tid + j * NT;
+        const int r = cidx >> 4;
+        const size_t off = ((((size_t)tblk[j] * a.Hkv + g) << a.kv.bs_log2) + ((row0 + r) & mask)) *
+                               HD + (cidx & 15) * 8;
+        kreg[j] = r < nrows ? *reinterpret_cast<const uint4*>(a.k + off) : make_uint4(0, 0, 0, 0);
+        vreg[j] = r < nrows ? *reinterpret_cast<const uint4*>(a.v + off) : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      const uint16_t* kbase = kbg + (size_t)row0 * HD;
+      const uint16_t* vbase = vbg + (size_t)row0 * HD;
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int cidx = tid + j * NT;
+        const int r = cidx >> 4;
+        const size_t off = (size_t)r * HD + (cidx & 15) * 8;
+        kreg[j] = r < nrows ? *reinterpret_cast<const uint4*>(kbase + off) : make_uint4(0, 0, 0, 0);
+        vreg[j] = r < nrows ? *reinterpret_cast<const uint4*>(vbase + off) : make_uint4(0, 0, 0, 0);
+      }
     }
   };
   auto store_stage = [&](int buf) {
@@ -476,13 +518,26 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
   };
 
   if (nt > 0) {
+    table_entries(0);
     load_stage(0);
     store_stage(0);
+    if (nt > 1) table_entries(1);
     __syncthreads();
+  }
+  if constexpr (PAGED) {
+    // Every load issued so far (the Q fragments included) has completed on
+    // all paths into the loop.  Without this the compiler cannot prove the
+    // Q registers ready at the loop's first matrix instruction (the block
+    // check and table reads add paths) and waits there for every load in
+    // flight, the next stage's K/V too, every iteration.
+    __builtin_amdgcn_s_waitcnt(0);
   }
   for (int t = 0; t < nt; ++t) {
     const int buf = t & 1;
-    if (t + 1 < nt) load_stage(t + 1);
+    if (t + 1 < nt) {
+      load_stage(t + 1);
+      if (t + 2 < nt) table_entries(t + 2);
+    }
     int row0, nrows;
     stage_rows(t, row0, nrows);
     const bool tree = (t >= ntp);
@@ -548,6 +603,8 @@ __global__ __launch_bounds__(HD) void attn_merge_kernel(MfmaArgs a, int rows_per
   }
   __syncthreads();
   if (bad) return;
+  // so was a sequence whose rows sit in a block outside the pool
+  if (a.kv.table && !a.kv.blocks_ok(b, 0, L + n)) return;
   const int nsplit = L > 0 ? (L + a.chunk - 1) / a.chunk : 1;
   const size_t base = (((size_t)b * a.Hkv + g) * rows_per_bg + r) * a.S_max;
   float mstar = -INFINITY;
@@ -618,7 +675,8 @@ Plan make_plan(int B, int n_max, int Hq, int Hkv, int d, int L_cap, int dtype) {
 
 spec_status_t check_args(const void* q, const void* k, const void* v, const int32_t* pl,
                          const int32_t* nn, const int32_t* par, int B, int n_max, int Hq,
-                         int Hkv, int d, int L_cap, float scale, int dtype, const float* out) {
+                         int Hkv, int d, int L_cap, float scale, int dtype, const float* out,
+                         bool paged) {
   if (!q || !k || !v || !pl || !nn || !par || !out) return SPEC_E_NULL;
   if (B <= 0 || n_max <= 0 || n_max > SPEC_MAX_NODES || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
       L_cap < n_max)
@@ -628,7 +686,8 @@ spec_status_t check_args(const void* q, const void* k, const void* v, const int3
   if (!(scale > 0.f) || !isfinite(scale)) return SPEC_E_VALUE;
   // query rows and cache rows are counted in 32-bit ints (grid sizes, row
   // indices); byte offsets are 64-bit
-  if ((long)B * n_max * Hq > (1L << 30) || (long)B * Hkv * L_cap >= (1L << 31)) return SPEC_E_SHAPE;
+  if ((long)B * n_max * Hq > (1L << 30) || (!paged && (long)B * Hkv * L_cap >= (1L << 31)))
+    return SPEC_E_SHAPE;
   return SPEC_OK;
 }
 
@@ -645,18 +704,33 @@ extern "C" size_t spec_verify_tree_attn_workspace_size(int32_t B, int32_t n_max,
 }
 
 namespace {
+template <bool PAGED>
+void launch_variant(const Plan& p, unsigned grid, hipStream_t strm, const MfmaArgs& a) {
+  if (p.nb == 1 && p.nw == 2)
+    hipLaunchKernelGGL((attn_mfma_kernel<1, 2, 1, PAGED>), dim3(grid), dim3(128), 0, strm, a);
+  else if (p.nb == 1 && p.nw == 4)
+    hipLaunchKernelGGL((attn_mfma_kernel<1, 4, 1, PAGED>), dim3(grid), dim3(256), 0, strm, a);
+  else if (p.nb == 1 && p.nw == 8 && p.sub == 2)
+    hipLaunchKernelGGL((attn_mfma_kernel<1, 8, 2, PAGED>), dim3(grid), dim3(512), 0, strm, a);
+  else if (p.nb == 1 && p.nw == 8)
+    hipLaunchKernelGGL((attn_mfma_kernel<1, 8, 1, PAGED>), dim3(grid), dim3(512), 0, strm, a);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<2, 4, 1, PAGED>), dim3(grid), dim3(256), 0, strm, a);
+}
+
 spec_status_t launch_attn(const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* prefix_len, const int32_t* n_nodes,
                           const int32_t* parents, int32_t B, int32_t n_max, int32_t Hq,
-                          int32_t Hkv, int32_t head_dim, int32_t L_cap, float scale,
+                          int32_t Hkv, int32_t head_dim, const KvRows& kv, float scale,
                           int32_t dtype, const float* inv_freq, int rope, float* out,
                           void* workspace, size_t workspace_bytes, int32_t* dev_error,
                           void* stream) {
   spec_status_t st = check_args(q, k_cache, v_cache, prefix_len, n_nodes, parents, B, n_max, Hq,
-                                Hkv, head_dim, L_cap, scale, dtype, out);
+                                Hkv, head_dim, kv.L_cap, scale, dtype, out, kv.table != nullptr);
   if (st != SPEC_OK) return st;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
   const float c = scale * kLog2e;
+  const int L_cap = kv.L_cap;
   const Plan p = make_plan(B, n_max, Hq, Hkv, head_dim, L_cap, dtype);
   if (!p.mfma) {
     dim3 grid(n_max * Hq, B);
@@ -664,12 +738,12 @@ spec_status_t launch_attn(const void* q, const void* k_cache, const void* v_cach
       hipLaunchKernelGGL(attn_valu_kernel<float>, grid, dim3(64), 0, strm,
                          static_cast<const float*>(q), static_cast<const float*>(k_cache),
                          static_cast<const float*>(v_cache), prefix_len, n_nodes, parents, n_max,
-                         Hq, Hkv, head_dim, L_cap, c, inv_freq, rope, out, dev_error);
+                         Hq, Hkv, head_dim, kv, c, inv_freq, rope, out, dev_error);
     } else {
       hipLaunchKernelGGL(attn_valu_kernel<uint16_t>, grid, dim3(64), 0, strm,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                          static_cast<const uint16_t*>(v_cache), prefix_len, n_nodes, parents, n_max,
-                         Hq, Hkv, head_dim, L_cap, c, inv_freq, rope, out, dev_error);
+                         Hq, Hkv, head_dim, kv, c, inv_freq, rope, out, dev_error);
     }
     SPEC_HIP_TRY(hipGetLastError());
     return SPEC_OK;
@@ -684,6 +758,7 @@ spec_status_t launch_attn(const void* q, const void* k_cache, const void* v_cach
   a.n_nodes = n_nodes;
   a.parents = parents;
   a.B = B; a.n_max = n_max; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.L_cap = L_cap;
+  a.kv = kv;
   a.RB = p.rb; a.S_max = p.S_max; a.chunk = p.chunk; a.units = p.units; a.sort = p.sort;
   a.c = c;
   a.inv_freq = inv_freq;
@@ -699,16 +774,10 @@ spec_status_t launch_attn(const void* q, const void* k_cache, const void* v_cach
     a.part_ml = reinterpret_cast<float2*>(ws + rows * HD * sizeof(float));
   }
   const unsigned grid = (unsigned)(((p.units + 7) / 8) * 8 * p.rb);
-  if (p.nb == 1 && p.nw == 2)
-    hipLaunchKernelGGL((attn_mfma_kernel<1, 2, 1>), dim3(grid), dim3(128), 0, strm, a);
-  else if (p.nb == 1 && p.nw == 4)
-    hipLaunchKernelGGL((attn_mfma_kernel<1, 4, 1>), dim3(grid), dim3(256), 0, strm, a);
-  else if (p.nb == 1 && p.nw == 8 && p.sub == 2)
-    hipLaunchKernelGGL((attn_mfma_kernel<1, 8, 2>), dim3(grid), dim3(512), 0, strm, a);
-  else if (p.nb == 1 && p.nw == 8)
-    hipLaunchKernelGGL((attn_mfma_kernel<1, 8, 1>), dim3(grid), dim3(512), 0, strm, a);
+  if (kv.table)
+    launch_variant<true>(p, grid, strm, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<2, 4, 1>), dim3(grid), dim3(256), 0, strm, a);
+    launch_variant<false>(p, grid, strm, a);
   SPEC_HIP_TRY(hipGetLastError());
   if (p.S_max > 1) {
     hipLaunchKernelGGL(attn_merge_kernel, dim3(p.rb * p.rpw, Hkv, B), dim3(HD), 0, strm, a,
@@ -724,9 +793,10 @@ extern "C" spec_status_t spec_verify_tree_attn(
     const int32_t* n_nodes, const int32_t* parents, int32_t B, int32_t n_max, int32_t Hq,
     int32_t Hkv, int32_t head_dim, int32_t L_cap, float scale, int32_t dtype, float* out,
     void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream) {
+  if (L_cap <= 0) return SPEC_E_SHAPE;
   return launch_attn(q, k_cache, v_cache, prefix_len, n_nodes, parents, B, n_max, Hq, Hkv,
-                     head_dim, L_cap, scale, dtype, nullptr, 0, out, workspace, workspace_bytes,
-                     dev_error, stream);
+                     head_dim, contiguous_rows(Hkv, L_cap), scale, dtype, nullptr, 0, out,
+                     workspace, workspace_bytes, dev_error, stream);
 }
 
 extern "C" spec_status_t spec_verify_tree_attn_rope(
@@ -737,7 +807,26 @@ extern "C" spec_status_t spec_verify_tree_attn_rope(
     size_t workspace_bytes, int32_t* dev_error, void* stream) {
   if (!inv_freq) return SPEC_E_NULL;
   if (rope_style != kRopeHalf && rope_style != kRopeInterleaved) return SPEC_E_VALUE;
+  if (L_cap <= 0) return SPEC_E_SHAPE;
   return launch_attn(q, k_cache, v_cache, prefix_len, n_nodes, parents, B, n_max, Hq, Hkv,
-                     head_dim, L_cap, scale, dtype, inv_freq, rope_style, out, workspace,
-                     workspace_bytes, dev_error, stream);
+                     head_dim, contiguous_rows(Hkv, L_cap), scale, dtype, inv_freq, rope_style,
+                     out, workspace, workspace_bytes, dev_error, stream);
+}
+
+extern "C" spec_status_t spec_verify_tree_attn_paged(
+    const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+    int32_t max_blocks, int32_t block_size, int32_t num_blocks, const int32_t* prefix_len,
+    const int32_t* n_nodes, const int32_t* parents, int32_t B, int32_t n_max, int32_t Hq,
+    int32_t Hkv, int32_t head_dim, float scale, int32_t dtype, const float* inv_freq,
+    int32_t rope_style, float* out, void* workspace, size_t workspace_bytes, int32_t* dev_error,
+    void* stream) {
+  if (!block_table) return SPEC_E_NULL;
+  if (inv_freq && rope_style != kRopeHalf && rope_style != kRopeInterleaved) return SPEC_E_VALUE;
+  KvRows kv;
+  const spec_status_t st = make_paged_rows(block_table, max_blocks, block_size, num_blocks,
+                                           Hkv > 0 ? Hkv : 1, &kv);
+  if (st != SPEC_OK) return st;
+  return launch_attn(q, k_pool, v_pool, prefix_len, n_nodes, parents, B, n_max, Hq, Hkv,
+                     head_dim, kv, scale, dtype, inv_freq, inv_freq ? rope_style : 0, out,
+                     workspace, workspace_bytes, dev_error, stream);
 }

@@ -20,6 +20,11 @@
 // cache rows prefix_len + 0..a receive scratch rows path[0..a] (no overlap, a
 // plain gather).
 //
+// Paged caches (spec_kv_commit_layers_paged): the same moves on logical rows,
+// each row found through the sequence's block table (KvRows).  A sequence
+// whose rows would come from or go to a block outside the pool is left
+// untouched and reports a capacity error.
+//
 // Lengths: spec_kv_commit has one workgroup per sequence, which also owns the
 // sequence's length.  spec_kv_commit_layers has one workgroup per (sequence,
 // layer), all of which read the length, so the lengths advance in a second,
@@ -36,12 +41,13 @@ constexpr int CPT = 16;        // 16-byte chunks per thread per round
 // Loads sequence b's path into s_path and checks it: a <= max_depth, the
 // committed rows fit (prefix + a + 1 <= L_cap), path[0] == 0, strictly
 // increasing (so path[i] >= i), and every source row exists (prefix +
-// path[i] < L_cap in place, n_rows == 0; path[i] < n_rows from scratch).
-// Returns 0 or SPEC_DEVERR_* bits; *s_moves says whether the in-place form
-// moves anything.  Called by every thread of the workgroup, a >= 0,
-// blockDim.x > a.
-__device__ int load_path(const int32_t* path, int b, int a, int L, int L_cap, int max_depth,
-                         int n_rows, int* s_path, int* s_moves) {
+// path[i] < L_cap in place, n_rows == 0; path[i] < n_rows from scratch), and
+// every block holding a row read or written exists.  Returns 0 or
+// SPEC_DEVERR_* bits; *s_moves says whether the in-place form moves
+// anything.  Called by every thread of the workgroup, a >= 0, blockDim.x > a.
+__device__ int load_path(const int32_t* path, int b, int a, int L, const KvRows& kv,
+                         int max_depth, int n_rows, int* s_path, int* s_moves) {
+  const int L_cap = kv.L_cap;
   if (a > max_depth) return SPEC_DEVERR_TREE;
   if (L < 0 || (int64_t)L + a + 1 > L_cap) return SPEC_DEVERR_CAPACITY;
   const int tid = threadIdx.x;
@@ -57,15 +63,18 @@ __device__ int load_path(const int32_t* path, int b, int a, int L, int L_cap, in
   }
   __syncthreads();
   if (tid > 0 && tid <= a && s_path[tid] <= s_path[tid - 1]) bad = 1;
-  return __syncthreads_or(bad) ? SPEC_DEVERR_TREE : 0;
+  if (__syncthreads_or(bad)) return SPEC_DEVERR_TREE;
+  // rows written: L .. L + a; rows read in place: up to L + path[a]
+  const int hi = L + 1 + (n_rows > 0 ? a : s_path[a]);
+  return kv.blocks_ok(b, L, hi) ? 0 : SPEC_DEVERR_CAPACITY;
 }
 
-// In-place gather of rows 1..a of every (head, K/V) plane of one sequence and
-// one layer; kc, vc point at the sequence's first plane, planes plane_stride
-// chunks apart.  Every thread of the workgroup calls it.
+// In-place gather of rows 1..a of every (head, K/V) plane of sequence b in
+// one layer's cache kc, vc (rows located by kv, in 16-byte chunks).  Every
+// thread of the workgroup calls it.
 template <int NTH>
-__device__ void move_in_place(uint4* kc, uint4* vc, int Hkv, int row_chunks, size_t plane_stride,
-                              int L, int a, const int* s_path) {
+__device__ void move_in_place(uint4* kc, uint4* vc, const KvRows& kv, int b, int Hkv,
+                              int row_chunks, int L, int a, const int* s_path) {
   // chunk c = ((g * 2 + kv) * a + slot - 1) * row_chunks + cc (row 0, the
   // root, is already in place)
   const int plane_chunks = a * row_chunks;
@@ -77,7 +86,7 @@ __device__ void move_in_place(uint4* kc, uint4* vc, int Hkv, int row_chunks, siz
     const int cc = rem - (slot - 1) * row_chunks;
     *pl_out = pl;
     const int row = src ? s_path[slot] : slot;
-    return (size_t)(pl >> 1) * plane_stride + (size_t)(L + row) * row_chunks + cc;
+    return kv.offset(b, pl >> 1, L + row, row_chunks) + cc;
   };
   for (int r0 = 0; r0 < total; r0 += NTH * CPT) {
     uint4 regs[CPT];
@@ -113,15 +122,13 @@ __global__ __launch_bounds__(NT) void commit_kernel(uint4* kc, uint4* vc, int32_
   const int a = accept_len[b];
   const int L = prefix_len[b];
   if (a < 0) return;
-  const int err = load_path(path, b, a, L, L_cap, max_depth, 0, s_path, &s_moves);
+  const KvRows kv = contiguous_rows(Hkv, L_cap);
+  const int err = load_path(path, b, a, L, kv, max_depth, 0, s_path, &s_moves);
   if (err) {
     if (threadIdx.x == 0) report(dev_error, err);
     return;
   }
-  const size_t plane_stride = (size_t)L_cap * row_chunks;
-  if (s_moves)
-    move_in_place<NT>(kc + (size_t)b * Hkv * plane_stride, vc + (size_t)b * Hkv * plane_stride,
-                      Hkv, row_chunks, plane_stride, L, a, s_path);
+  if (s_moves) move_in_place<NT>(kc, vc, kv, b, Hkv, row_chunks, L, a, s_path);
   if (threadIdx.x == 0) prefix_len[b] = L + a + 1;
 }
 
@@ -131,7 +138,7 @@ __global__ __launch_bounds__(NT) void commit_kernel(uint4* kc, uint4* vc, int32_
 __global__ __launch_bounds__(NTL) void commit_layers_kernel(
     uint4* const* kl, uint4* const* vl, const uint4* const* kt, const uint4* const* vt,
     const int32_t* prefix_len, const int32_t* path, const int32_t* accept_len, int Hkv,
-    int row_chunks, int L_cap, int n_rows, int max_depth, int32_t* dev_error) {
+    int row_chunks, KvRows kv, int n_rows, int max_depth, int32_t* dev_error) {
   __shared__ int s_path[SPEC_MAX_NODES + 1];
   __shared__ int s_moves;
   const int b = blockIdx.x;
@@ -140,16 +147,15 @@ __global__ __launch_bounds__(NTL) void commit_layers_kernel(
   const int L = prefix_len[b];
   if (a < 0) return;
   const bool scratch = (kt != nullptr);
-  const int err = load_path(path, b, a, L, L_cap, max_depth, scratch ? n_rows : 0, s_path, &s_moves);
+  const int err = load_path(path, b, a, L, kv, max_depth, scratch ? n_rows : 0, s_path, &s_moves);
   if (err) {
     if (layer == 0 && threadIdx.x == 0) report(dev_error, err);
     return;
   }
-  const size_t plane_stride = (size_t)L_cap * row_chunks;
-  uint4* kc = kl[layer] + (size_t)b * Hkv * plane_stride;
-  uint4* vc = vl[layer] + (size_t)b * Hkv * plane_stride;
+  uint4* kc = kl[layer];
+  uint4* vc = vl[layer];
   if (!scratch) {
-    if (s_moves) move_in_place<NTL>(kc, vc, Hkv, row_chunks, plane_stride, L, a, s_path);
+    if (s_moves) move_in_place<NTL>(kc, vc, kv, b, Hkv, row_chunks, L, a, s_path);
     return;
   }
   // from scratch: chunk c = ((g * 2 + kv) * (a + 1) + slot) * row_chunks + cc
@@ -165,14 +171,14 @@ __global__ __launch_bounds__(NTL) void commit_layers_kernel(
     const int cc = rem - slot * row_chunks;
     const size_t g = (size_t)(pl >> 1);
     const uint4 x = ((pl & 1) ? vs : ks)[g * tree_stride + (size_t)s_path[slot] * row_chunks + cc];
-    ((pl & 1) ? vc : kc)[g * plane_stride + (size_t)(L + slot) * row_chunks + cc] = x;
+    ((pl & 1) ? vc : kc)[kv.offset(b, (int)g, L + slot, row_chunks) + cc] = x;
   }
 }
 
 // Advances the length of every sequence the copy kernel committed.
 __global__ __launch_bounds__(64) void commit_length_kernel(int32_t* prefix_len,
                                                            const int32_t* path,
-                                                           const int32_t* accept_len, int L_cap,
+                                                           const int32_t* accept_len, KvRows kv,
                                                            int n_rows, int max_depth) {
   __shared__ int s_path[SPEC_MAX_NODES + 1];
   __shared__ int s_moves;
@@ -180,7 +186,7 @@ __global__ __launch_bounds__(64) void commit_length_kernel(int32_t* prefix_len,
   const int a = accept_len[b];
   const int L = prefix_len[b];
   if (a < 0) return;
-  if (load_path(path, b, a, L, L_cap, max_depth, n_rows, s_path, &s_moves)) return;
+  if (load_path(path, b, a, L, kv, max_depth, n_rows, s_path, &s_moves)) return;
   if (threadIdx.x == 0) prefix_len[b] = L + a + 1;
 }
 
@@ -218,17 +224,22 @@ extern "C" spec_status_t spec_kv_commit(void* k_cache, void* v_cache, int32_t* p
   return SPEC_OK;
 }
 
-extern "C" spec_status_t spec_kv_commit_layers(
-    void* const* k_layers, void* const* v_layers, const void* const* k_tree,
-    const void* const* v_tree, int32_t num_layers, int32_t* prefix_len, const int32_t* path,
-    const int32_t* accept_len, int32_t B, int32_t n_max, int32_t Hkv, int32_t head_dim,
-    int32_t L_cap, int32_t max_depth, int32_t dtype, int32_t* dev_error, void* stream) {
+namespace specv {
+namespace {
+
+spec_status_t launch_commit_layers(void* const* k_layers, void* const* v_layers,
+                                   const void* const* k_tree, const void* const* v_tree,
+                                   int32_t num_layers, int32_t* prefix_len, const int32_t* path,
+                                   const int32_t* accept_len, int32_t B, int32_t n_max,
+                                   int32_t Hkv, int32_t head_dim, const KvRows& kv,
+                                   int32_t max_depth, int32_t dtype, int32_t* dev_error,
+                                   void* stream) {
   if (!k_layers || !v_layers || !prefix_len || !path || !accept_len) return SPEC_E_NULL;
   if ((k_tree == nullptr) != (v_tree == nullptr)) return SPEC_E_NULL;
   if (num_layers <= 0 || num_layers > 65535) return SPEC_E_SHAPE;
   const bool scratch = (k_tree != nullptr);
   if (scratch && (n_max <= 0 || n_max > SPEC_MAX_NODES)) return SPEC_E_SHAPE;
-  const spec_status_t st = check_commit_shape(B, Hkv, head_dim, L_cap, max_depth, dtype);
+  const spec_status_t st = check_commit_shape(B, Hkv, head_dim, kv.L_cap, max_depth, dtype);
   if (st != SPEC_OK) return st;
   const int esz = dtype == SPEC_F32 ? 4 : 2;
   const int row_chunks = head_dim * esz / 16;
@@ -239,10 +250,40 @@ extern "C" spec_status_t spec_kv_commit_layers(
                      reinterpret_cast<uint4* const*>(v_layers),
                      reinterpret_cast<const uint4* const*>(k_tree),
                      reinterpret_cast<const uint4* const*>(v_tree), prefix_len, path, accept_len,
-                     Hkv, row_chunks, L_cap, n_rows, max_depth, dev_error);
+                     Hkv, row_chunks, kv, n_rows, max_depth, dev_error);
   SPEC_HIP_TRY(hipGetLastError());
   hipLaunchKernelGGL(commit_length_kernel, dim3(B), dim3(64), 0, strm, prefix_len, path,
-                     accept_len, L_cap, n_rows, max_depth);
+                     accept_len, kv, n_rows, max_depth);
   SPEC_HIP_TRY(hipGetLastError());
   return SPEC_OK;
+}
+
+}  // namespace
+}  // namespace specv
+
+extern "C" spec_status_t spec_kv_commit_layers(
+    void* const* k_layers, void* const* v_layers, const void* const* k_tree,
+    const void* const* v_tree, int32_t num_layers, int32_t* prefix_len, const int32_t* path,
+    const int32_t* accept_len, int32_t B, int32_t n_max, int32_t Hkv, int32_t head_dim,
+    int32_t L_cap, int32_t max_depth, int32_t dtype, int32_t* dev_error, void* stream) {
+  if (L_cap <= 0) return SPEC_E_SHAPE;
+  return launch_commit_layers(k_layers, v_layers, k_tree, v_tree, num_layers, prefix_len, path,
+                              accept_len, B, n_max, Hkv, head_dim, contiguous_rows(Hkv, L_cap),
+                              max_depth, dtype, dev_error, stream);
+}
+
+extern "C" spec_status_t spec_kv_commit_layers_paged(
+    void* const* k_layers, void* const* v_layers, const void* const* k_tree,
+    const void* const* v_tree, int32_t num_layers, const int32_t* block_table,
+    int32_t max_blocks, int32_t block_size, int32_t num_blocks, int32_t* prefix_len,
+    const int32_t* path, const int32_t* accept_len, int32_t B, int32_t n_max, int32_t Hkv,
+    int32_t head_dim, int32_t max_depth, int32_t dtype, int32_t* dev_error, void* stream) {
+  if (!block_table) return SPEC_E_NULL;
+  KvRows kv;
+  const spec_status_t st = make_paged_rows(block_table, max_blocks, block_size, num_blocks, Hkv,
+                                           &kv);
+  if (st != SPEC_OK) return st;
+  return launch_commit_layers(k_layers, v_layers, k_tree, v_tree, num_layers, prefix_len, path,
+                              accept_len, B, n_max, Hkv, head_dim, kv, max_depth, dtype,
+                              dev_error, stream);
 }

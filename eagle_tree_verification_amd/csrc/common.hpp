@@ -61,6 +61,58 @@ __device__ __forceinline__ void report(int32_t* dev_error, int bits) {
   if (dev_error) atomicOr(dev_error, bits);
 }
 
+// Where a sequence's logical cache row lives.  A contiguous cache (table ==
+// nullptr) is [B][Hkv][L_cap][d]; a paged one is a pool of blocks
+// [num_blocks][Hkv][block_size][d] with a [B][max_blocks] block table: row r
+// of sequence b is row r % block_size of block table[b][r / block_size].
+// block_size is a power of two; offsets are in units of `unit` (elements, or
+// 16-byte chunks of a row).
+struct KvRows {
+  const int32_t* table;
+  int max_blocks, bs_log2, num_blocks, Hkv, L_cap;
+
+  __device__ __forceinline__ size_t offset(int b, int h, int r, int unit) const {
+    if (!table) return (((size_t)b * Hkv + h) * L_cap + r) * unit;
+    const int blk = table[(size_t)b * max_blocks + (r >> bs_log2)];
+    return ((((size_t)blk * Hkv + h) << bs_log2) + (r & ((1 << bs_log2) - 1))) * unit;
+  }
+
+  // Every block holding rows [r0, r1) of sequence b exists (a contiguous
+  // cache: always).  Called by every thread of the workgroup.
+  __device__ bool blocks_ok(int b, int r0, int r1) const {
+    int bad = 0;
+    if (table && r1 > r0) {
+      const int k0 = r0 >> bs_log2, k1 = (r1 - 1) >> bs_log2;
+      for (int k = k0 + (int)threadIdx.x; k <= k1; k += (int)blockDim.x) {
+        const int blk = table[(size_t)b * max_blocks + k];
+        bad |= (blk < 0 || blk >= num_blocks);
+      }
+    }
+    return !__syncthreads_or(bad);
+  }
+};
+
+__host__ __device__ inline KvRows contiguous_rows(int Hkv, int L_cap) {
+  return KvRows{nullptr, 0, 0, 0, Hkv, L_cap};
+}
+
+// Host checks of a paged cache's geometry: block_size a power of two in
+// [16, 4096], max_blocks and num_blocks positive, the logical capacity and
+// the pool's row count within 32-bit row indices.
+inline spec_status_t make_paged_rows(const int32_t* table, int max_blocks, int block_size,
+                                     int num_blocks, int Hkv, KvRows* kv) {
+  if (block_size < 16 || block_size > 4096 || (block_size & (block_size - 1)) != 0 ||
+      max_blocks <= 0 || num_blocks <= 0 || Hkv <= 0)
+    return SPEC_E_SHAPE;
+  if ((long)max_blocks * block_size >= (1L << 31) ||
+      (long)num_blocks * Hkv * block_size >= (1L << 31))
+    return SPEC_E_SHAPE;
+  int lg = 0;
+  while ((1 << lg) < block_size) ++lg;
+  *kv = KvRows{table, max_blocks, lg, num_blocks, Hkv, max_blocks * block_size};
+  return SPEC_OK;
+}
+
 // Host: compute units of the current device (cached per device ordinal).
 int device_cu_count();
 

@@ -10,6 +10,10 @@
 // of the head dimension turns by pos * inv_freq[i]; planes pair dimension i
 // with i + d/2, or 2i with 2i + 1.  Values are not rotated.
 //
+// The cache is contiguous, or paged (blocks of rows through a block table,
+// KvRows); a sequence whose rows would land in a block outside the pool is
+// not written and reports a capacity error.
+//
 // The work is a few MB per call (memory-bound, small).
 #include "common.hpp"
 
@@ -38,7 +42,7 @@ __global__ __launch_bounds__(NTW) void tree_kv_write_kernel(
     const T* __restrict__ k_new, const T* __restrict__ v_new, T* __restrict__ kc,
     T* __restrict__ vc, const int32_t* __restrict__ prefix_len,
     const int32_t* __restrict__ n_nodes, const int32_t* __restrict__ parents, int n_max, int Hkv,
-    int d, int L_cap, const float* __restrict__ inv_freq, int style,
+    int d, KvRows kv, const float* __restrict__ inv_freq, int style,
     int32_t* __restrict__ dev_error) {
   __shared__ int s_depth;
   __shared__ int s_bad;
@@ -51,7 +55,7 @@ __global__ __launch_bounds__(NTW) void tree_kv_write_kernel(
     if (reporter) report(dev_error, SPEC_DEVERR_TREE);
     return;
   }
-  if (L < 0 || (int64_t)L + n > L_cap) {
+  if (L < 0 || (int64_t)L + n > kv.L_cap) {
     if (reporter) report(dev_error, SPEC_DEVERR_CAPACITY);
     return;
   }
@@ -74,6 +78,10 @@ __global__ __launch_bounds__(NTW) void tree_kv_write_kernel(
     if (reporter) report(dev_error, SPEC_DEVERR_TREE);
     return;
   }
+  if (!kv.blocks_ok(b, L, L + n)) {
+    if (reporter) report(dev_error, SPEC_DEVERR_CAPACITY);
+    return;
+  }
   if (j >= n) return;
   const int half = d / 2;
   const int pos = L + s_depth;
@@ -82,7 +90,7 @@ __global__ __launch_bounds__(NTW) void tree_kv_write_kernel(
     const int t = e % half;
     const int h = e / half;
     const T* src = k_new + (((size_t)b * n_max + j) * Hkv + h) * d;
-    T* dst = kc + (((size_t)b * Hkv + h) * L_cap + L + j) * d;
+    T* dst = kc + kv.offset(b, h, L + j, d);
     const int ia = style == kRopeInterleaved ? 2 * t : t;
     const int ib = style == kRopeInterleaved ? 2 * t + 1 : t + half;
     if (inv_freq) {
@@ -100,8 +108,7 @@ __global__ __launch_bounds__(NTW) void tree_kv_write_kernel(
   for (int e = tid; e < Hkv * d; e += NTW) {
     const int c = e % d;
     const int h = e / d;
-    vc[(((size_t)b * Hkv + h) * L_cap + L + j) * d + c] =
-        v_new[(((size_t)b * n_max + j) * Hkv + h) * d + c];
+    vc[kv.offset(b, h, L + j, d) + c] = v_new[(((size_t)b * n_max + j) * Hkv + h) * d + c];
   }
 }
 
@@ -110,17 +117,19 @@ __global__ __launch_bounds__(NTW) void tree_kv_write_kernel(
 
 using namespace specv;
 
-extern "C" spec_status_t spec_tree_kv_write(const void* k_new, const void* v_new, void* k_cache,
-                                            void* v_cache, const int32_t* prefix_len,
-                                            const int32_t* n_nodes, const int32_t* parents,
-                                            int32_t B, int32_t n_max, int32_t Hkv,
-                                            int32_t head_dim, int32_t L_cap, int32_t dtype,
-                                            const float* inv_freq, int32_t rope_style,
-                                            int32_t* dev_error, void* stream) {
+namespace specv {
+namespace {
+
+spec_status_t launch_kv_write(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const int32_t* prefix_len, const int32_t* n_nodes,
+                              const int32_t* parents, int32_t B, int32_t n_max, int32_t Hkv,
+                              int32_t head_dim, int32_t dtype, const KvRows& kv,
+                              const float* inv_freq, int32_t rope_style, int32_t* dev_error,
+                              void* stream) {
   if (!k_new || !v_new || !k_cache || !v_cache || !prefix_len || !n_nodes || !parents)
     return SPEC_E_NULL;
   if (B <= 0 || B > 65535 || n_max <= 0 || n_max > SPEC_MAX_NODES || Hkv <= 0 ||
-      L_cap < n_max || (long)B * Hkv * L_cap >= (1L << 31))
+      kv.L_cap < n_max || (!kv.table && (long)B * Hkv * kv.L_cap >= (1L << 31)))
     return SPEC_E_SHAPE;
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_E_DTYPE;
   if (head_dim < 2 || head_dim > 1024 || head_dim % 2) return SPEC_E_DTYPE;
@@ -130,14 +139,45 @@ extern "C" spec_status_t spec_tree_kv_write(const void* k_new, const void* v_new
     hipLaunchKernelGGL(tree_kv_write_kernel<float>, dim3(n_max, B), dim3(NTW), 0, s,
                        static_cast<const float*>(k_new), static_cast<const float*>(v_new),
                        static_cast<float*>(k_cache), static_cast<float*>(v_cache), prefix_len,
-                       n_nodes, parents, n_max, Hkv, head_dim, L_cap, inv_freq, rope_style,
+                       n_nodes, parents, n_max, Hkv, head_dim, kv, inv_freq, rope_style,
                        dev_error);
   else
     hipLaunchKernelGGL(tree_kv_write_kernel<uint16_t>, dim3(n_max, B), dim3(NTW), 0, s,
                        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
                        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
-                       prefix_len, n_nodes, parents, n_max, Hkv, head_dim, L_cap, inv_freq,
+                       prefix_len, n_nodes, parents, n_max, Hkv, head_dim, kv, inv_freq,
                        rope_style, dev_error);
   SPEC_HIP_TRY(hipGetLastError());
   return SPEC_OK;
+}
+
+}  // namespace
+}  // namespace specv
+
+extern "C" spec_status_t spec_tree_kv_write(const void* k_new, const void* v_new, void* k_cache,
+                                            void* v_cache, const int32_t* prefix_len,
+                                            const int32_t* n_nodes, const int32_t* parents,
+                                            int32_t B, int32_t n_max, int32_t Hkv,
+                                            int32_t head_dim, int32_t L_cap, int32_t dtype,
+                                            const float* inv_freq, int32_t rope_style,
+                                            int32_t* dev_error, void* stream) {
+  if (L_cap <= 0) return SPEC_E_SHAPE;
+  return launch_kv_write(k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, parents, B, n_max,
+                         Hkv, head_dim, dtype, contiguous_rows(Hkv, L_cap), inv_freq, rope_style,
+                         dev_error, stream);
+}
+
+extern "C" spec_status_t spec_tree_kv_write_paged(
+    const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const int32_t* block_table, int32_t max_blocks, int32_t block_size, int32_t num_blocks,
+    const int32_t* prefix_len, const int32_t* n_nodes, const int32_t* parents, int32_t B,
+    int32_t n_max, int32_t Hkv, int32_t head_dim, int32_t dtype, const float* inv_freq,
+    int32_t rope_style, int32_t* dev_error, void* stream) {
+  if (!block_table) return SPEC_E_NULL;
+  KvRows kv;
+  const spec_status_t st = make_paged_rows(block_table, max_blocks, block_size, num_blocks, Hkv,
+                                           &kv);
+  if (st != SPEC_OK) return st;
+  return launch_kv_write(k_new, v_new, k_pool, v_pool, prefix_len, n_nodes, parents, B, n_max,
+                         Hkv, head_dim, dtype, kv, inv_freq, rope_style, dev_error, stream);
 }

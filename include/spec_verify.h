@@ -455,6 +455,64 @@ spec_status_t spec_tree_finalize(const void* state, size_t state_bytes, int32_t 
                                  uint64_t* anc_mask, int32_t* draft_row, float* value,
                                  int32_t* dev_error, void* stream);
 
+/*
+ * Paged caches.  [LESSON] "KV cache 回滚" names vLLM and TensorRT-LLM as the
+ * systems that write the verify pass's KV to a temporary buffer and commit it
+ * on acceptance; such servers keep the cache in fixed-size blocks.  The pages
+ * do not give the layout; these calls take the usual one:
+ *
+ *   k_pool, v_pool  [num_blocks][Hkv][block_size][head_dim] per layer, dtype
+ *   block_table     [B][max_blocks] int32 device array: logical row r of
+ *                   sequence b is row r % block_size of physical block
+ *                   block_table[b][r / block_size]
+ *   block_size      a power of two in [16, 4096]
+ *   max_blocks      logical blocks per sequence (the table's row length); the
+ *                   logical capacity is max_blocks * block_size (the L_cap of
+ *                   the contiguous calls)
+ *   num_blocks      physical blocks in each pool
+ *
+ * Each call does exactly what its contiguous form does on the logical rows,
+ * with the same kernels (bit-identical results for the same logical
+ * contents).  A sequence that would read or write a row whose block id lies
+ * outside [0, num_blocks) is not processed and sets SPEC_DEVERR_CAPACITY.
+ * The blocks holding rows [prefix_len, prefix_len + n_nodes) of a sequence
+ * must belong to that sequence alone (they are written); blocks of committed
+ * prefix rows may be shared between sequences (they are only read).  Host
+ * errors as the contiguous forms, plus SPEC_E_NULL for a NULL block_table and
+ * SPEC_E_SHAPE for a bad block geometry.
+ */
+
+/* spec_verify_tree_attn_rope / spec_verify_tree_attn on a paged cache
+ * (inv_freq NULL: no rotation, rope_style ignored).  workspace >=
+ * spec_verify_tree_attn_workspace_size(B, n_max, Hq, Hkv, head_dim,
+ * max_blocks * block_size, dtype). */
+spec_status_t spec_verify_tree_attn_paged(
+    const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+    int32_t max_blocks, int32_t block_size, int32_t num_blocks,
+    const int32_t* prefix_len, const int32_t* n_nodes, const int32_t* parents,
+    int32_t B, int32_t n_max, int32_t Hq, int32_t Hkv, int32_t head_dim,
+    float scale, int32_t dtype, const float* inv_freq, int32_t rope_style, float* out,
+    void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream);
+
+/* spec_tree_kv_write on a paged cache: node j's K (rotated when inv_freq is
+ * given) and V go to logical row prefix_len + j. */
+spec_status_t spec_tree_kv_write_paged(
+    const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+    const int32_t* block_table, int32_t max_blocks, int32_t block_size, int32_t num_blocks,
+    const int32_t* prefix_len, const int32_t* n_nodes, const int32_t* parents,
+    int32_t B, int32_t n_max, int32_t Hkv, int32_t head_dim, int32_t dtype,
+    const float* inv_freq, int32_t rope_style, int32_t* dev_error, void* stream);
+
+/* spec_kv_commit_layers on paged caches: k_layers / v_layers point at each
+ * layer's pool (one block table serves every layer); in place or from
+ * scratch rows exactly as spec_kv_commit_layers. */
+spec_status_t spec_kv_commit_layers_paged(
+    void* const* k_layers, void* const* v_layers, const void* const* k_tree,
+    const void* const* v_tree, int32_t num_layers, const int32_t* block_table,
+    int32_t max_blocks, int32_t block_size, int32_t num_blocks, int32_t* prefix_len,
+    const int32_t* path, const int32_t* accept_len, int32_t B, int32_t n_max, int32_t Hkv,
+    int32_t head_dim, int32_t max_depth, int32_t dtype, int32_t* dev_error, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* spec_status_string(spec_status_t status);
 

@@ -22,7 +22,9 @@ def test_every_declared_symbol_is_exported(lib):
                           "spec_kv_commit_layers", "spec_status_string", "spec_abi_version",
                           "spec_tree_state_size", "spec_tree_expand", "spec_tree_finalize",
                           "spec_verify_tree_attn_rope", "spec_tree_kv_write",
-                          "spec_accept_tree_ex", "spec_accept_tree_ex_workspace_size"}
+                          "spec_accept_tree_ex", "spec_accept_tree_ex_workspace_size",
+                          "spec_verify_tree_attn_paged", "spec_tree_kv_write_paged",
+                          "spec_kv_commit_layers_paged"}
     for nm in names:
         assert hasattr(lib, nm), nm
 
@@ -203,3 +205,42 @@ def test_accept_ex_host_checks(lib):
         bad = list(args); bad[7] = V; bad[11] = P; bad[26] = small
         assert f(*bad) == SPEC_E_WORKSPACE
     assert ws(4, 8, 1000, 1001, 0) == 0
+
+
+def test_paged_host_checks(lib):
+    P = _buf()
+    f = lib.spec_verify_tree_attn_paged
+    # q, k_pool, v_pool, table, max_blocks, block_size, num_blocks, prefix_len, n_nodes,
+    # parents, B, n_max, Hq, Hkv, d, scale, dtype, inv_freq, rope_style, out, ws, ws_bytes,
+    # dev_error, stream
+    args = [P, P, P, P, 8, 16, 40, P, P, P, 2, 6, 4, 2, 128, 0.1, 1, None, 0, P, P, 1 << 30,
+            None, None]
+    assert f(*(args[:3] + [None] + args[4:])) == SPEC_E_NULL
+    for bs in (8, 24, 8192):                     # a power of two in [16, 4096]
+        bad = list(args); bad[5] = bs
+        assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[4] = 0
+    assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[6] = 0
+    assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[17] = P; bad[18] = 5   # rope style with frequencies
+    assert f(*bad) == SPEC_E_VALUE
+    g = lib.spec_tree_kv_write_paged
+    # k_new, v_new, k_pool, v_pool, table, max_blocks, block_size, num_blocks, prefix_len,
+    # n_nodes, parents, B, n_max, Hkv, d, dtype, inv_freq, rope_style, dev_error, stream
+    wargs = [P, P, P, P, P, 8, 16, 40, P, P, P, 2, 6, 2, 128, 1, None, 0, None, None]
+    assert g(*(wargs[:4] + [None] + wargs[5:])) == SPEC_E_NULL
+    bad = list(wargs); bad[6] = 100
+    assert g(*bad) == SPEC_E_SHAPE
+    bad = list(wargs); bad[5] = 0                # capacity below n_max
+    assert g(*bad) == SPEC_E_SHAPE
+    h = lib.spec_kv_commit_layers_paged
+    # k_layers, v_layers, k_tree, v_tree, num_layers, table, max_blocks, block_size,
+    # num_blocks, prefix_len, path, accept_len, B, n_max, Hkv, d, max_depth, dtype,
+    # dev_error, stream
+    cargs = [P, P, None, None, 4, P, 8, 16, 40, P, P, P, 2, 0, 2, 128, 8, 1, None, None]
+    assert h(*(cargs[:5] + [None] + cargs[6:])) == SPEC_E_NULL
+    bad = list(cargs); bad[7] = 48
+    assert h(*bad) == SPEC_E_SHAPE
+    bad = list(cargs); bad[2] = P                # k_tree without v_tree
+    assert h(*bad) == SPEC_E_NULL

@@ -1,0 +1,289 @@
+"""GPU parity of the paged-cache calls (spec_verify_tree_attn_paged,
+spec_tree_kv_write_paged, spec_kv_commit_layers_paged).
+
+Pools are built from a contiguous cache by scattering its logical blocks to a
+random permutation of physical blocks; blocks no sequence owns are filled
+with NaN, so a stray read poisons the output and a stray write changes them.
+Every paged result must be bit-identical to the contiguous call on the same
+logical contents (the same kernels run on translated rows), and is also
+compared with the oracle on the logical view (oracle.paged).  A block id
+outside the pool fails only its sequence, which is left untouched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import paged as opaged
+from oracle import rope as orope
+from eagle_tree_verification_amd.workloads import (make_workload, small_cases, storage_to_f64,
+                                                   to_device, _to_storage)
+from gpu_helpers import ATOL, SENTINEL, compare_attention, oracle_accept, say
+
+pytestmark = pytest.mark.gpu
+
+NAN16 = np.uint16(0x7FC0)
+
+
+def _nan_like(kv_dtype):
+    return NAN16 if kv_dtype == "bf16" else np.float32(np.nan)
+
+
+def _to_pool(cache, bs, rng, spare, kv_dtype, table=None):
+    """cache [B][Hkv][L_cap][d] (storage) -> (pool [nb][Hkv][bs][d], table [B][L_cap / bs])."""
+    B, H, Lc, d = cache.shape
+    assert Lc % bs == 0
+    mb = Lc // bs
+    if table is None:
+        table = rng.permutation(B * mb + spare)[: B * mb].reshape(B, mb).astype(np.int32)
+    nb = B * mb + spare
+    pool = np.full((nb, H, bs, d), _nan_like(kv_dtype), dtype=cache.dtype)
+    for b in range(B):
+        for k in range(mb):
+            pool[table[b, k]] = cache[b, :, k * bs:(k + 1) * bs]
+    return pool, table
+
+
+def _dev(arr, kv_dtype):
+    t = torch.from_numpy(np.ascontiguousarray(arr))
+    return t.view(torch.int16).to("cuda").view(torch.bfloat16) if kv_dtype == "bf16" else t.to("cuda")
+
+
+def _host(t, kv_dtype):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16) if kv_dtype == "bf16" else t.cpu().numpy()
+
+
+def _logical(pool, table, bs, rows):
+    return np.stack([opaged.logical_rows(pool, table[b], bs, rows) for b in range(table.shape[0])])
+
+
+def _inv_freq(d):
+    return (500000.0 ** (-np.arange(d // 2) * 2.0 / d)).astype(np.float32)
+
+
+ATTN_CASES = [("c1-t1", 16), ("c2-mini", 64), ("c4-mini", 16), ("c4-mini", 256), ("c5-mini", 32)]
+
+
+def _workload(name, bs, poison=True):
+    kw = dict(small_cases()[name])
+    w0 = make_workload(**kw)
+    l_cap = -(-int(w0.L_cap) // max(bs, 256)) * max(bs, 256)
+    return make_workload(poison=poison, l_cap=l_cap, **kw)
+
+
+@pytest.mark.parametrize("name,bs", ATTN_CASES)
+def test_paged_attention_bit_identical(hip_lib, name, bs):
+    api = hip_lib
+    w = _workload(name, bs)
+    rng = np.random.default_rng(bs)
+    say(f"[gpu] paged attention {name}: B={w.B} L_cap={w.L_cap} block_size={bs} {w.kv_dtype}")
+    kp, table = _to_pool(w.k_cache, bs, rng, 7, w.kv_dtype)
+    vp, _ = _to_pool(w.v_cache, bs, rng, 7, w.kv_dtype, table=table)
+    dev = to_device(w)
+    tdev = torch.from_numpy(table).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for rope in (False, True):
+        f = torch.from_numpy(_inv_freq(w.d)).cuda() if rope else None
+        oc = torch.full((w.B, w.n_max, w.Hq, w.d), SENTINEL, dtype=torch.float32, device="cuda")
+        op = oc.clone()
+        api.verify_tree_attn(dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"],
+                             dev["n_nodes"], dev["parents"], out=oc, dev_error=err, inv_freq=f)
+        api.verify_tree_attn_paged(dev["q"], _dev(kp, w.kv_dtype), _dev(vp, w.kv_dtype), tdev,
+                                   dev["prefix_len"], dev["n_nodes"], dev["parents"], out=op,
+                                   dev_error=err, inv_freq=f)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        assert torch.equal(oc.view(torch.int32), op.view(torch.int32)), f"rope={rope}"
+        if not rope:
+            compare_attention(w, op.cpu().numpy())
+
+
+def test_paged_kv_write_bit_identical(hip_lib):
+    api = hip_lib
+    bs = 16
+    w = _workload("c4-mini", bs)
+    rng = np.random.default_rng(3)
+    shape = (w.B, w.n_max, w.Hkv, w.d)
+    kn = _to_storage(rng.standard_normal(size=shape, dtype=np.float32), w.kv_dtype)
+    vn = _to_storage(rng.standard_normal(size=shape, dtype=np.float32), w.kv_dtype)
+    kp, table = _to_pool(w.k_cache, bs, rng, 5, w.kv_dtype)
+    vp, _ = _to_pool(w.v_cache, bs, rng, 5, w.kv_dtype, table=table)
+    dev = to_device(w)
+    f = torch.from_numpy(_inv_freq(w.d)).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kpd, vpd = _dev(kp, w.kv_dtype), _dev(vp, w.kv_dtype)
+    api.tree_kv_write(_dev(kn, w.kv_dtype), _dev(vn, w.kv_dtype), dev["k_cache"], dev["v_cache"],
+                      dev["prefix_len"], dev["n_nodes"], dev["parents"], inv_freq=f, dev_error=err)
+    api.tree_kv_write_paged(_dev(kn, w.kv_dtype), _dev(vn, w.kv_dtype), kpd, vpd,
+                            torch.from_numpy(table).cuda(), dev["prefix_len"], dev["n_nodes"],
+                            dev["parents"], inv_freq=f, dev_error=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    kc, vc = _host(dev["k_cache"], w.kv_dtype), _host(dev["v_cache"], w.kv_dtype)
+    kp2, vp2 = _host(kpd, w.kv_dtype), _host(vpd, w.kv_dtype)
+    np.testing.assert_array_equal(_logical(kp2, table, bs, w.L_cap).view(np.uint16), kc.view(np.uint16))
+    np.testing.assert_array_equal(_logical(vp2, table, bs, w.L_cap).view(np.uint16), vc.view(np.uint16))
+    # blocks no sequence owns are untouched
+    spare = np.setdiff1d(np.arange(kp.shape[0]), table.ravel())
+    assert (kp2[spare].view(np.uint16) == NAN16).all() and (vp2[spare].view(np.uint16) == NAN16).all()
+    # the oracle's rotated write on the logical view of the pre-write pool
+    for b in range(w.B):
+        n, L = int(w.n_nodes[b]), int(w.prefix_len[b])
+        k0 = storage_to_f64(opaged.logical_rows(kp, table[b], bs, w.L_cap), w.kv_dtype)
+        v0 = storage_to_f64(opaged.logical_rows(vp, table[b], bs, w.L_cap), w.kv_dtype)
+        k2, _ = orope.tree_kv_write(k0, v0, storage_to_f64(kn[b], w.kv_dtype),
+                                    storage_to_f64(vn[b], w.kv_dtype), L, w.parents[b, :n], n,
+                                    _inv_freq(w.d), "half")
+        got = storage_to_f64(opaged.logical_rows(kp2, table[b], bs, w.L_cap), w.kv_dtype)
+        assert np.all(np.abs(got[:, L:L + n] - k2[:, L:L + n]) <= 2.0 ** -8 * np.abs(k2[:, L:L + n]) + 2e-6)
+
+
+def _commit_setup(seed, bs):
+    w = make_workload(4, batch=6, prefix=(0, 150), vocab=2053, drafts=[60, 1, 0, 17, 33, 8],
+                      T=1.0, seed=seed, prefix_lens=[0, 1, 63, 64, 150, 97], l_cap=256)
+    D = w.max_depth
+    path = np.full((w.B, D + 1), -1, dtype=np.int32)
+    acc = np.full(w.B, -1, dtype=np.int32)
+    for b in range(w.B):
+        r = oracle_accept(w, b)
+        acc[b] = r.accept_len
+        path[b, : r.accept_len + 1] = r.path
+    return w, path, acc
+
+
+@pytest.mark.parametrize("scratch", [False, True], ids=["in-place", "scratch"])
+@pytest.mark.parametrize("bs", [16, 64])
+def test_paged_commit_layers_bit_identical(hip_lib, scratch, bs):
+    api = hip_lib
+    nl = 3
+    w, path, acc = _commit_setup(57, bs)
+    rng = np.random.default_rng(bs + scratch)
+    shape_c = (w.B, w.Hkv, w.L_cap, w.d)
+    shape_t = (w.B, w.Hkv, w.n_max, w.d)
+    kc = [rng.integers(0, 1 << 15, size=shape_c, dtype=np.uint16) for _ in range(nl)]
+    vc = [rng.integers(0, 1 << 15, size=shape_c, dtype=np.uint16) for _ in range(nl)]
+    kt = [rng.integers(0, 1 << 15, size=shape_t, dtype=np.uint16) for _ in range(nl)]
+    vt = [rng.integers(0, 1 << 15, size=shape_t, dtype=np.uint16) for _ in range(nl)]
+    _, table = _to_pool(kc[0], bs, rng, 4, "bf16")
+    kp = [_to_pool(a, bs, rng, 4, "bf16", table=table)[0] for a in kc]
+    vp = [_to_pool(a, bs, rng, 4, "bf16", table=table)[0] for a in vc]
+    say(f"[gpu] paged commit {'scratch' if scratch else 'in-place'} bs={bs}: accept={acc.tolist()}")
+    d = lambda a: _dev(a, "bf16")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pdev, adev = torch.from_numpy(path).cuda(), torch.from_numpy(acc).cuda()
+    kcd, vcd, kpd, vpd = [d(a) for a in kc], [d(a) for a in vc], [d(a) for a in kp], [d(a) for a in vp]
+    td = ([d(a) for a in kt], [d(a) for a in vt]) if scratch else (None, None)
+    plen_c = torch.from_numpy(w.prefix_len.copy()).cuda()
+    plen_p = plen_c.clone()
+    keep = [api.kv_commit_layers(kcd, vcd, plen_c, pdev, adev, w.max_depth, k_tree=td[0],
+                                 v_tree=td[1], dev_error=err),
+            api.kv_commit_layers_paged(kpd, vpd, torch.from_numpy(table).cuda(), plen_p, pdev, adev,
+                                       w.max_depth, k_tree=td[0], v_tree=td[1], dev_error=err)]
+    torch.cuda.synchronize()
+    del keep
+    assert int(err.item()) == 0
+    np.testing.assert_array_equal(plen_p.cpu().numpy(), w.prefix_len + acc + 1)
+    np.testing.assert_array_equal(plen_p.cpu().numpy(), plen_c.cpu().numpy())
+    spare = np.setdiff1d(np.arange(kp[0].shape[0]), table.ravel())
+    for l in range(nl):
+        for pool_d, cont_d, before in ((kpd[l], kcd[l], kp[l]), (vpd[l], vcd[l], vp[l])):
+            pool = _host(pool_d, "bf16")
+            logical = _logical(pool, table, bs, w.L_cap)
+            np.testing.assert_array_equal(logical, _host(cont_d, "bf16"))
+            assert (pool[spare] == NAN16).all()
+        for b in range(w.B):
+            a, L = int(acc[b]), int(w.prefix_len[b])
+            k0 = opaged.logical_rows(kp[l], table[b], bs, w.L_cap)
+            v0 = opaged.logical_rows(vp[l], table[b], bs, w.L_cap)
+            if scratch:
+                k2, _, _ = oracle.kv_commit_from_buffer(k0, v0, kt[l][b], vt[l][b], L,
+                                                        path[b, : a + 1], a)
+            else:
+                k2, _, _ = oracle.kv_commit(k0, v0, L, path[b, : a + 1], a)
+            np.testing.assert_array_equal(
+                opaged.logical_rows(_host(kpd[l], "bf16"), table[b], bs, w.L_cap), k2)
+
+
+def test_paged_block_out_of_range_fails_its_sequence(hip_lib):
+    api = hip_lib
+    bs = 16
+    w = _workload("c4-mini", bs)
+    rng = np.random.default_rng(11)
+    kp, table = _to_pool(w.k_cache, bs, rng, 3, w.kv_dtype)
+    vp, _ = _to_pool(w.v_cache, bs, rng, 3, w.kv_dtype, table=table)
+    nb = kp.shape[0]
+    bad_b = int(np.argmax(w.prefix_len))
+    L, n = int(w.prefix_len[bad_b]), int(w.n_nodes[bad_b])
+    bad = table.copy()
+    bad[bad_b, L // bs] = nb                    # the block of its root row
+    ok_b = [b for b in range(w.B) if b != bad_b]
+    # entries past a sequence's rows are never read: garbage there is harmless
+    for b in ok_b:
+        used = -(-(int(w.prefix_len[b]) + int(w.n_nodes[b])) // bs)
+        bad[b, used:] = -1
+    say(f"[gpu] paged errors: sequence {bad_b} gets block id {nb} of {nb}")
+    dev = to_device(w)
+    tdev = torch.from_numpy(bad).cuda()
+    kpd, vpd = _dev(kp, w.kv_dtype), _dev(vp, w.kv_dtype)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    op = torch.full((w.B, w.n_max, w.Hq, w.d), SENTINEL, dtype=torch.float32, device="cuda")
+    api.verify_tree_attn_paged(dev["q"], kpd, vpd, tdev, dev["prefix_len"], dev["n_nodes"],
+                               dev["parents"], out=op, dev_error=err)
+    oc = torch.full_like(op, SENTINEL)
+    api.verify_tree_attn(dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"],
+                         dev["n_nodes"], dev["parents"], out=oc)
+    torch.cuda.synchronize()
+    assert int(err.item()) == api.DEVERR_CAPACITY
+    assert (op[bad_b] == SENTINEL).all()
+    assert torch.equal(op[ok_b], oc[ok_b])
+    # the write leaves the failed sequence's blocks alone
+    err.zero_()
+    shape = (w.B, w.n_max, w.Hkv, w.d)
+    kn = _to_storage(rng.standard_normal(size=shape, dtype=np.float32), w.kv_dtype)
+    api.tree_kv_write_paged(_dev(kn, w.kv_dtype), _dev(kn, w.kv_dtype), kpd, vpd, tdev,
+                            dev["prefix_len"], dev["n_nodes"], dev["parents"], dev_error=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == api.DEVERR_CAPACITY
+    kp2 = _host(kpd, w.kv_dtype)
+    mine = [table[bad_b, k] for k in range(-(-(L + n) // bs)) if k != L // bs]
+    np.testing.assert_array_equal(kp2[mine].view(np.uint16), kp[mine].view(np.uint16))
+    # the commit leaves its length and rows alone
+    err.zero_()
+    path = np.full((w.B, w.max_depth + 1), -1, dtype=np.int32)
+    path[:, 0] = 0
+    acc = np.zeros(w.B, dtype=np.int32)
+    plen = dev["prefix_len"].clone()
+    keep = api.kv_commit_layers_paged([kpd], [vpd], tdev, plen, torch.from_numpy(path).cuda(),
+                                      torch.from_numpy(acc).cuda(), w.max_depth, dev_error=err)
+    torch.cuda.synchronize()
+    del keep
+    assert int(err.item()) == api.DEVERR_CAPACITY
+    got = plen.cpu().numpy()
+    assert got[bad_b] == L
+    np.testing.assert_array_equal(got[ok_b], w.prefix_len[ok_b] + 1)
+
+
+@pytest.mark.timeout(900)
+def test_paged_attention_full_size(hip_lib):
+    """The serving shape (batch 64, prefixes 512-4096) over 16-row blocks in
+    a shuffled pool: bit-identical to the contiguous kernel."""
+    api = hip_lib
+    bs = 16
+    w = make_workload(4)
+    if w.L_cap % bs:
+        pytest.skip("L_cap not a multiple of the block size")
+    rng = np.random.default_rng(5)
+    kp, table = _to_pool(w.k_cache, bs, rng, 64, w.kv_dtype)
+    vp, _ = _to_pool(w.v_cache, bs, rng, 64, w.kv_dtype, table=table)
+    dev = to_device(w)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    oc = api.verify_tree_attn(dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"],
+                              dev["n_nodes"], dev["parents"], dev_error=err)
+    op = api.verify_tree_attn_paged(dev["q"], _dev(kp, w.kv_dtype), _dev(vp, w.kv_dtype),
+                                    torch.from_numpy(table).cuda(), dev["prefix_len"],
+                                    dev["n_nodes"], dev["parents"], dev_error=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    for b in range(w.B):
+        n = int(w.n_nodes[b])
+        assert torch.equal(oc[b, :n].view(torch.int32), op[b, :n].view(torch.int32)), b
