@@ -380,41 +380,49 @@ __device__ __forceinline__ int elem_index(int lo, int k) {
 }
 
 // Loads group g (W consecutive entries) of this thread's share of a row
-// slice; entries past `hi` read as `fill`.
+// slice; entries past `hi` read as `fill`.  The load itself is unconditional,
+// at an index clamped into the slice (a slice holds at least W entries, and
+// with W = 4 its bounds are multiples of 4), and the fill is a select: a load
+// under a branch makes the compiler wait for it at once, which would undo the
+// prefetching of stream_slice.
 template <int W>
 __device__ __forceinline__ void load_group(const float* row, int lo, int hi, int g, float fill, float* x) {
   const int i = elem_index<W>(lo, g * W);
+  const bool ok = i < hi;
+  const int ic = ok ? i : hi - W;
   if (W == 4) {
-    if (i < hi) {
-      const float4 f = *reinterpret_cast<const float4*>(row + i);
-      x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
-    } else {
-      x[0] = x[1] = x[2] = x[3] = fill;
-    }
+    const float4 f = *reinterpret_cast<const float4*>(row + ic);
+    x[0] = ok ? f.x : fill;
+    x[1] = ok ? f.y : fill;
+    x[2] = ok ? f.z : fill;
+    x[3] = ok ? f.w : fill;
   } else {
-    x[0] = i < hi ? row[i] : fill;
+    const float f = row[ic];
+    x[0] = ok ? f : fill;
   }
 }
 
 // Group g of a draft row held over a draft vocabulary: target entry i reads
-// p_draft[t2d[i]], or 0 when no draft id maps to i.
+// p_draft[t2d[i]], or 0 when no draft id maps to i.  Loads and gathers are
+// unconditional (clamped index, id -1 read as id 0) for the same reason.
 template <int W>
 __device__ __forceinline__ void load_group_mapped(const float* row, const int32_t* t2d, int lo,
                                                   int hi, int g, float fill, float* x) {
   const int i = elem_index<W>(lo, g * W);
+  const bool ok = i < hi;
+  const int ic = ok ? i : hi - W;
   if (W == 4) {
-    if (i < hi) {
-      const int4 t = *reinterpret_cast<const int4*>(t2d + i);
-      x[0] = t.x >= 0 ? row[t.x] : 0.f;
-      x[1] = t.y >= 0 ? row[t.y] : 0.f;
-      x[2] = t.z >= 0 ? row[t.z] : 0.f;
-      x[3] = t.w >= 0 ? row[t.w] : 0.f;
-    } else {
-      x[0] = x[1] = x[2] = x[3] = fill;
-    }
+    const int4 t = *reinterpret_cast<const int4*>(t2d + ic);
+    const float p0 = row[max(t.x, 0)], p1 = row[max(t.y, 0)];
+    const float p2 = row[max(t.z, 0)], p3 = row[max(t.w, 0)];
+    x[0] = ok ? (t.x >= 0 ? p0 : 0.f) : fill;
+    x[1] = ok ? (t.y >= 0 ? p1 : 0.f) : fill;
+    x[2] = ok ? (t.z >= 0 ? p2 : 0.f) : fill;
+    x[3] = ok ? (t.w >= 0 ? p3 : 0.f) : fill;
   } else {
-    const int t = i < hi ? t2d[i] : -1;
-    x[0] = i < hi ? (t >= 0 ? row[t] : 0.f) : fill;
+    const int t = t2d[ic];
+    const float p = row[max(t, 0)];
+    x[0] = ok ? (t >= 0 ? p : 0.f) : fill;
   }
 }
 
