@@ -287,3 +287,72 @@ def test_paged_attention_full_size(hip_lib):
     for b in range(w.B):
         n = int(w.n_nodes[b])
         assert torch.equal(oc[b, :n].view(torch.int32), op[b, :n].view(torch.int32)), b
+
+
+@pytest.mark.parametrize("bs", [16, 128])
+def test_paged_step_matches_contiguous(hip_lib, bs):
+    """One whole verify step on paged caches: rotated tree K/V write, tree
+    attention, the walk, and the all-layer commit (two layers sharing the
+    table), against the same step on contiguous caches, bit for bit."""
+    api = hip_lib
+    w = _workload("c4-mini", bs)
+    rng = np.random.default_rng(70 + bs)
+    kp0, table = _to_pool(w.k_cache, bs, rng, 9, w.kv_dtype)
+    vp0, _ = _to_pool(w.v_cache, bs, rng, 9, w.kv_dtype, table=table)
+    shape = (w.B, w.n_max, w.Hkv, w.d)
+    kn = _to_storage(rng.standard_normal(size=shape, dtype=np.float32), w.kv_dtype)
+    vn = _to_storage(rng.standard_normal(size=shape, dtype=np.float32), w.kv_dtype)
+    dev = to_device(w)
+    f = torch.from_numpy(_inv_freq(w.d)).cuda()
+    tdev = torch.from_numpy(table).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    results = []
+    for paged in (False, True):
+        plen = dev["prefix_len"].clone()
+        if paged:
+            ks = [_dev(kp0, w.kv_dtype), _dev(kp0, w.kv_dtype)]
+            vs = [_dev(vp0, w.kv_dtype), _dev(vp0, w.kv_dtype)]
+            api.tree_kv_write_paged(_dev(kn, w.kv_dtype), _dev(vn, w.kv_dtype), ks[0], vs[0], tdev,
+                                    plen, dev["n_nodes"], dev["parents"], inv_freq=f, dev_error=err)
+            api.tree_kv_write_paged(_dev(kn, w.kv_dtype), _dev(vn, w.kv_dtype), ks[1], vs[1], tdev,
+                                    plen, dev["n_nodes"], dev["parents"], dev_error=err)
+            out = api.verify_tree_attn_paged(dev["q"], ks[0], vs[0], tdev, plen, dev["n_nodes"],
+                                             dev["parents"], dev_error=err, inv_freq=f)
+        else:
+            ks = [_dev(w.k_cache, w.kv_dtype), _dev(w.k_cache, w.kv_dtype)]
+            vs = [_dev(w.v_cache, w.kv_dtype), _dev(w.v_cache, w.kv_dtype)]
+            api.tree_kv_write(_dev(kn, w.kv_dtype), _dev(vn, w.kv_dtype), ks[0], vs[0], plen,
+                              dev["n_nodes"], dev["parents"], inv_freq=f, dev_error=err)
+            api.tree_kv_write(_dev(kn, w.kv_dtype), _dev(vn, w.kv_dtype), ks[1], vs[1], plen,
+                              dev["n_nodes"], dev["parents"], dev_error=err)
+            out = api.verify_tree_attn(dev["q"], ks[0], vs[0], plen, dev["n_nodes"], dev["parents"],
+                                       dev_error=err, inv_freq=f)
+        acc = api.accept_tree(dev["tokens"], dev["parents"], dev["n_nodes"], dev["draft_p"],
+                              dev["logits"], w.T, dev["u_accept"], dev["u_sample"], w.max_depth,
+                              dev_error=err)
+        if paged:
+            keep = api.kv_commit_layers_paged(ks, vs, tdev, plen, acc["path"], acc["accept_len"],
+                                              w.max_depth, dev_error=err)
+        else:
+            keep = api.kv_commit_layers(ks, vs, plen, acc["path"], acc["accept_len"], w.max_depth,
+                                        dev_error=err)
+        torch.cuda.synchronize()
+        del keep
+        assert int(err.item()) == 0
+        caches = []
+        for t in ks + vs:
+            h = _host(t, w.kv_dtype)
+            caches.append(_logical(h, table, bs, w.L_cap) if paged else h)
+        n = w.n_nodes
+        results.append({"out": [out[b, : int(n[b])].cpu().numpy() for b in range(w.B)],
+                        "acc": acc["accept_len"].cpu().numpy(), "path": acc["path"].cpu().numpy(),
+                        "plen": plen.cpu().numpy(), "caches": caches})
+    c, p = results
+    for b in range(w.B):
+        np.testing.assert_array_equal(c["out"][b].view(np.int32), p["out"][b].view(np.int32))
+    np.testing.assert_array_equal(c["acc"], p["acc"])
+    np.testing.assert_array_equal(c["path"], p["path"])
+    np.testing.assert_array_equal(c["plen"], p["plen"])
+    np.testing.assert_array_equal(c["plen"], w.prefix_len + c["acc"] + 1)
+    for x, y in zip(c["caches"], p["caches"]):
+        np.testing.assert_array_equal(x.view(np.uint16), y.view(np.uint16))
