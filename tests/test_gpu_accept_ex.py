@@ -304,3 +304,30 @@ def test_filters_full_size(hip_lib):
                         top_p=p)
     say(f"[gpu]   sampled {sample}; near-tie excluded {excluded}")
     assert len(excluded) <= 2
+
+
+@pytest.mark.parametrize("name", ["c1-kp1", "c4-w1", "c4-ties", "c4-w4"])
+def test_top_k_alone(hip_lib, name):
+    """Top-k with top-p off, k from 1 to 1000, against the oracle on distinct
+    and on heavily tied logits (the search may stop early on a bucket holding
+    exactly the entries top-k needs, or run all four rounds)."""
+    api = hip_lib
+    kw, step = FILTER_CASES[name]
+    w = make_workload(poison=True, **kw)
+    logits = w.logits if step is None else (np.round(w.logits / step) * step).astype(np.float32)
+    ks = np.array([1, 2, 3, 17, 50, 63, 64, 65, 200, 1000], np.int32)
+    k = ks[np.arange(w.B) % len(ks)]
+    say(f"[gpu] top-k alone {name}: B={w.B} V={w.V} k={k.tolist()}")
+    dev = to_device(w)
+    host = _run(api, w, dev, dev["draft_p"], logits=torch.from_numpy(logits).to("cuda"),
+                top_k=torch.from_numpy(k).to("cuda"))
+    assert host["dev_error"] == 0
+    excluded = _compare(w, host, np.full(w.B, w.T, np.float32), lambda b: w.draft_p[b], w.tokens,
+                        top_k=k, logits=logits)
+    assert len(excluded) <= max(1, w.B // 4)
+    for b in range(w.B):
+        if b in excluded:
+            continue
+        v = int(host["path"][b, host["accept_len"][b]])
+        keep, _ = oracle.filter_keep(logits[b, v], float(w.T), int(k[b]), 0.0)
+        assert np.all(host["final_dist"][b][~keep] == 0.0), b
