@@ -52,6 +52,7 @@
 #include <stdlib.h>
 #include <unistd.h>
 
+#include <algorithm>
 #include <atomic>
 #include <chrono>
 
@@ -496,9 +497,13 @@ struct FilterShared {
 // Publishes this workgroup's 256-bucket histogram (h_cnt, h_mass: bucket j at
 // index j * kCopies) and returns
 // the sums over the KP workgroups of bucket jb.  Like exchange(), with no
-// fence: every 64-bit word carries a 32-bit tag (20 bits of launch id, 12 of
-// exchange number) above 32 payload bits, is written and read with
-// device-coherent atomic accesses, and is valid once its tag is current.  A
+// fence: every 64-bit word carries a 32-bit tag (a set top bit, 19 bits of
+// launch id, 12 of exchange number) above 32 payload bits, is written and read
+// with device-coherent atomic accesses, and is valid once its tag is current.
+// A tag this short could recur after 2^19 launches, so every call clears the
+// buffers first (hist_clear_kernel); the set bit keeps a tag from ever
+// matching a cleared word, and the launch id keeps the launches of one call
+// (consecutive groups of sequences) apart.  A
 // bucket is two words: count (16 bits; a slice holds at most 16384 entries)
 // with mass bits 47..32, then mass bits 31..0.  Each thread issues the loads
 // of kHistBatch workgroups at once before checking tags.  Buffers alternate with
@@ -519,7 +524,8 @@ __device__ bool exchange_hist(const AcceptArgs& a, int bl, int part, int& gen,
     mass = h_mass[jb * kCopies];
     return true;
   }
-  const uint64_t tag = (((a.epoch & 0xFFFFFull) << 12) | (uint64_t)(gen & 0xfff)) << 32;
+  const uint64_t tag = (((0x80000ull | (a.epoch & 0x7FFFFull)) << 12) | (uint64_t)(gen & 0xfff))
+                       << 32;
   uint64_t* data = a.hist + ((size_t)bl * 2 + (gen & 1)) * (size_t)a.KP * 512;
   ++gen;
   const uint64_t m = h_mass[t * kCopies];
@@ -1220,6 +1226,13 @@ accept_fn pick_kernel(int w, int ng, bool mapped = false, bool filt = false) {
 // Inverse of a draft-vocabulary map: t2d[x] = i where x = i + d2t[i], -1 for
 // target tokens no draft id maps to; *bad set when the map leaves [0, V) or
 // is not one-to-one.  Two launches: fill, then scatter.
+// Zeroes the histogram exchange buffers of a filtered call.
+__global__ void hist_clear_kernel(uint64_t* h, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    h[i] = 0;
+}
+
 __global__ void t2d_fill_kernel(int32_t* t2d, int V, int32_t* bad) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < V) t2d[i] = -1;
@@ -1399,6 +1412,12 @@ extern "C" spec_status_t spec_accept_tree_ex(
   }
   if (tie_count) {
     hipLaunchKernelGGL(accept_init_kernel, dim3(1), dim3(64), 0, strm, tie_count);
+    SPEC_HIP_TRY(hipGetLastError());
+  }
+  if (a.hist) {
+    const size_t n = (size_t)B * 2 * p.KP * 512;
+    const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(hist_clear_kernel, dim3(blocks), dim3(256), 0, strm, a.hist, n);
     SPEC_HIP_TRY(hipGetLastError());
   }
   if (mapped) {  // inverse map in the workspace, after the exchange words
