@@ -204,7 +204,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // PAGED: cache rows are found through the block table (a.kv); otherwise the
 // cache is contiguous and the kernel never looks at a.kv.table.
-template <int NB, int NW, int SUB, bool PAGED>
+template <int NB, int NW, int SUB, bool PAGED, bool PIPE = false>
 __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
   constexpr int NT = NW * 64;
   constexpr int RPW = NW * NB * 32;                    // query rows per workgroup
@@ -517,6 +517,143 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
     }
   };
 
+  // Pipelined order (PIPE, two sub-tiles per stage): the PV product of the
+  // previous sub-tile is issued step by step between the exponentials of
+  // the current one, so each wave's matrix and vector work overlap.  The
+  // operations on O keep their order (the previous sub-tile's PV, then the
+  // current rescale, then the current PV one sub-tile later), so the result
+  // equals the plain order's bit for bit.  The pending sub-tile's weights
+  // sit in pfA at the end of every stage, its keys in (pbuf, psub); the
+  // first pending product is of zero weights.
+  // (pipelined order) S^T (keys x rows) of the sub-tile of keys [64 * sub, 64 * sub + nrows) of
+  // the stage in buffer buf, for its two 32-key halves, masked.
+  auto qk = [&](int buf, int sub, int nrows, bool tree, f32x16_t (*sacc)[2]) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      sacc[nb][0] = f32x16_t{};
+      sacc[nb][1] = f32x16_t{};
+    }
+    const uint16_t* ks_ = Ks[buf] + sub * KT * KS_STRIDE;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(ks_ + (kb * 32 + lr) * KS_STRIDE + ks * 16 + lh * 8);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          sacc[nb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nb][ks], sacc[nb][kb], 0, 0, 0);
+      }
+    }
+
+    // Mask only the ragged last prefix sub-tile and the tree tile (uniform).
+    // Lane (lr, lh) holds keys 8*gq + 4*lh + e4 of each 32-key half.
+    if (tree || nrows < KT) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = kb * 32 + 8 * (e >> 2) + 4 * lh + (e & 3);
+            const bool vis = key < nrows && (!tree || ((anc_r[nb] >> key) & 1ull));
+            if (!vis) sacc[nb][kb][e] = -INFINITY;
+          }
+    }
+  };
+
+  // V^T operand of contraction step `step` (key block step / 8, half
+  // (step / 4) % 2, dim block step % 4) of the sub-tile whose transpose-read
+  // base is vs_.
+  auto vread = [&](const uint16_t* vs_, int step) {
+    const int kb = step >> 3, hb = (step >> 2) & 1, db = step & 3;
+    const uint16_t* src = vs_ + (kb * 32 + hb * 16) * VS_STRIDE + db * 32;
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (v4i16_t __attribute__((address_space(3)))*)(src));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (v4i16_t __attribute__((address_space(3)))*)(src + 8 * VS_STRIDE));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  bf16x8_t pfA[NB][2][2], pfB[NB][2][2];
+  int pbuf = 0, psub = 0;
+  if constexpr (PIPE) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) pfA[nb][kb][hb] = bf16x8_t{};
+  }
+  // One sub-tile in the pipelined order: its scores, the softmax reductions,
+  // then 16 steps of (one PV instruction of the pending sub-tile, two of
+  // this sub-tile's exponentials), then the rescale.  pold holds the pending
+  // weights, pnew receives this sub-tile's.
+  auto piped_sub = [&](int buf, int sub, int nrows, bool tree, bf16x8_t (*pnew)[2][2],
+                       bf16x8_t (*pold)[2][2]) {
+    f32x16_t sacc[NB][2];
+    qk(buf, sub, nrows, tree, sacc);
+    float alpha[NB], muc[NB], ls[NB];
+    int moved = 0;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[nb][kb][e]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      // the lazy reference max of the plain order
+      const bool up = (mt - mrow[nb]) * cs > kLazy;
+      const float mn = up ? mt : mrow[nb];
+      const float mu = (mn == -INFINITY) ? 0.f : mn;
+      muc[nb] = mu * cs;
+      alpha[nb] = up ? fast_exp2(mrow[nb] * cs - muc[nb]) : 1.f;
+      moved |= up;
+      mrow[nb] = mn;
+      ls[nb] = 0.f;
+    }
+    // the transposed V reads run two steps ahead of their product
+    const uint16_t* vs_ = Vs[pbuf] + (psub * KT + tr_key) * VS_STRIDE + tr_dim;
+    bf16x8_t vf_q[3];
+    vf_q[0] = vread(vs_, 0);
+    vf_q[1] = vread(vs_, 1);
+#pragma unroll
+    for (int step = 0; step < 16; ++step) {
+      const int kb = step >> 3, hb = (step >> 2) & 1, db = step & 3;
+      const bf16x8_t vf = vf_q[step % 3];
+      if (step + 2 < 16) vf_q[(step + 2) % 3] = vread(vs_, step + 2);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        o[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pold[nb][kb][hb], o[nb][db], 0, 0, 0);
+      // scores 2 step and 2 step + 1 of the 32 this lane holds, in the plain
+      // order's summation order
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int idx = 2 * step + q, skb = idx >> 4, e = idx & 15;
+          float pw = fast_exp2(fmaf(sacc[nb][skb][e], cs, -muc[nb]));
+          // An empty asm ties each exponential to its step: without it the
+          // exponentials, whose results are not needed until the next
+          // sub-tile, all sink below the 16 matrix instructions.
+          asm volatile("" : "+v"(pw));
+          ls[nb] += pw;
+          pnew[nb][skb][e >> 3][e & 7] = static_cast<__bf16>(pw);
+        }
+      // nothing crosses a step boundary
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) lrow[nb] = lrow[nb] * alpha[nb] + ls[nb];
+    if (__any(moved)) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[nb][db] *= alpha[nb];
+    }
+    pbuf = buf;
+    psub = sub;
+  };
+
   if (nt > 0) {
     table_entries(0);
     load_stage(0);
@@ -541,14 +678,46 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
     int row0, nrows;
     stage_rows(t, row0, nrows);
     const bool tree = (t >= ntp);
+    if constexpr (PIPE) {
+      static_assert(SUB == 2, "the pipelined order alternates two weight buffers");
+      piped_sub(buf, 0, min(KT, nrows), tree, pfB, pfA);
+      if (nrows > KT) {
+        piped_sub(buf, 1, min(KT, nrows - KT), tree, pfA, pfB);
+      } else {
 #pragma unroll
-    for (int sub = 0; sub < SUB; ++sub) {
-      const int rows_sub = nrows - sub * KT;
-      if (rows_sub <= 0) break;
-      compute_sub(buf, sub, min(KT, rows_sub), tree);
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) pfA[nb][kb][hb] = pfB[nb][kb][hb];
+      }
+      // The store below overwrites the other buffer, whose last sub-tile
+      // the first product above read: every wave must be past it.
+      __syncthreads();
+    } else {
+#pragma unroll
+      for (int sub = 0; sub < SUB; ++sub) {
+        const int rows_sub = nrows - sub * KT;
+        if (rows_sub <= 0) break;
+        compute_sub(buf, sub, min(KT, rows_sub), tree);
+      }
     }
     if (t + 1 < nt) store_stage(buf ^ 1);
     __syncthreads();
+  }
+  if constexpr (PIPE) {
+    // the last sub-tile's product
+    if (nt > 0) {
+      const uint16_t* vs_ = Vs[pbuf] + (psub * KT + tr_key) * VS_STRIDE + tr_dim;
+#pragma unroll
+      for (int step = 0; step < 16; ++step) {
+        const int kb = step >> 3, hb = (step >> 2) & 1, db = step & 3;
+        const bf16x8_t vf = vread(vs_, step);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          o[nb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pfA[nb][kb][hb], o[nb][db], 0, 0, 0);
+      }
+    }
   }
 
   // ---- epilogue: lane holds dims db*32 + 8*gq + 4*lh + e4 of its query row.
@@ -627,6 +796,7 @@ __global__ __launch_bounds__(HD) void attn_merge_kernel(MfmaArgs a, int rows_per
 struct Plan {
   bool mfma = false;
   int nb = 0, nw = 0, sub = 1, rpw = 0, rb = 0, S_max = 1, chunk = 0, units = 0, sort = 0;
+  bool pipe = false;
   size_t ws = 0;
 };
 
@@ -652,6 +822,10 @@ Plan make_plan(int B, int n_max, int Hq, int Hkv, int d, int L_cap, int dtype) {
       p.sub = (nb == 1 && nw == 8 && sub == 2) ? 2 : 1;
     }
   }
+  // The two-sub-tile variant runs in the pipelined order (SPEC_ATTN_PIPE=0:
+  // the plain order, for comparisons).
+  p.pipe = p.sub == 2;
+  if (const char* env = getenv("SPEC_ATTN_PIPE")) p.pipe = p.pipe && env[0] != '0';
   p.rpw = p.nw * p.nb * 32;
   p.rb = (M + p.rpw - 1) / p.rpw;
   const long base = (long)B * Hkv * p.rb;
@@ -710,6 +884,9 @@ void launch_variant(const Plan& p, unsigned grid, hipStream_t strm, const MfmaAr
     hipLaunchKernelGGL((attn_mfma_kernel<1, 2, 1, PAGED>), dim3(grid), dim3(128), 0, strm, a);
   else if (p.nb == 1 && p.nw == 4)
     hipLaunchKernelGGL((attn_mfma_kernel<1, 4, 1, PAGED>), dim3(grid), dim3(256), 0, strm, a);
+  else if (p.nb == 1 && p.nw == 8 && p.sub == 2 && p.pipe)
+    hipLaunchKernelGGL((attn_mfma_kernel<1, 8, 2, PAGED, true>), dim3(grid), dim3(512), 0, strm,
+                       a);
   else if (p.nb == 1 && p.nw == 8 && p.sub == 2)
     hipLaunchKernelGGL((attn_mfma_kernel<1, 8, 2, PAGED>), dim3(grid), dim3(512), 0, strm, a);
   else if (p.nb == 1 && p.nw == 8)

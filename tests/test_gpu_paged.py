@@ -98,6 +98,36 @@ def test_paged_attention_bit_identical(hip_lib, name, bs):
             compare_attention(w, op.cpu().numpy())
 
 
+def test_paged_pipelined_order_is_bit_identical(hip_lib, monkeypatch):
+    """The paged two-sub-tile kernel in its default pipelined order against
+    its plain order (SPEC_ATTN_PIPE=0): every output bit equal."""
+    api = hip_lib
+    bs = 32
+    w = make_workload(4, batch=6, prefix=(0, 3000), vocab=64, drafts=[63, 0, 40, 63, 5, 33],
+                      poison=True, seed=516, prefix_lens=[0, 1, 64, 129, 1000, 3000],
+                      l_cap=3072 + 64)
+    rng = np.random.default_rng(bs)
+    say(f"[gpu] paged pipelined vs plain order: n={w.n_nodes.tolist()} L={w.prefix_len.tolist()}")
+    assert w.n_max * (w.Hq // w.Hkv) > 128
+    kp, table = _to_pool(w.k_cache, bs, rng, 3, w.kv_dtype)
+    vp, _ = _to_pool(w.v_cache, bs, rng, 3, w.kv_dtype, table=table)
+    dev = to_device(w)
+    kpd, vpd, tdev = _dev(kp, w.kv_dtype), _dev(vp, w.kv_dtype), torch.from_numpy(table).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    outs = []
+    for pipe in ("1", "0"):
+        monkeypatch.setenv("SPEC_ATTN_PIPE", pipe)
+        out = torch.full((w.B, w.n_max, w.Hq, w.d), SENTINEL, dtype=torch.float32, device="cuda")
+        api.verify_tree_attn_paged(dev["q"], kpd, vpd, tdev, dev["prefix_len"], dev["n_nodes"],
+                                   dev["parents"], out=out, dev_error=err)
+        torch.cuda.synchronize()
+        outs.append(out)
+    monkeypatch.delenv("SPEC_ATTN_PIPE")
+    assert int(err.item()) == 0
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+    compare_attention(w, outs[0].cpu().numpy(), nodes_per_seq=6, rng=np.random.default_rng(6))
+
+
 def test_paged_kv_write_bit_identical(hip_lib):
     api = hip_lib
     bs = 16

@@ -14,8 +14,8 @@ import torch
 
 from eagle_tree_verification_amd.workloads import make_workload, small_cases, to_device
 import oracle
-from gpu_helpers import (compare_accept, compare_attention, compare_commit, kv_host, oracle_accept,
-                         run_gpu_step, say)
+from gpu_helpers import (SENTINEL, compare_accept, compare_attention, compare_commit, kv_host,
+                         oracle_accept, run_gpu_step, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -90,6 +90,39 @@ def test_attention_layouts(hip_lib, hq, hkv, d, dt):
     dev = to_device(w)
     host = run_gpu_step(w, dev, commit=False)
     compare_attention(w, host["attn"])
+
+
+@pytest.mark.parametrize("rope", [False, True])
+def test_pipelined_order_is_bit_identical(hip_lib, monkeypatch, rope):
+    """The two-sub-tile attention kernel runs in a pipelined order by default
+    (a sub-tile's PV product interleaved with the next sub-tile's softmax);
+    SPEC_ATTN_PIPE=0 selects the plain order.  The operations on O keep their
+    order, so every output bit must agree: stages of one and of two
+    sub-tiles, a tree-only pass (empty prefix), single-node trees, and
+    prefixes long enough to be split over several workgroups."""
+    api = hip_lib
+    w = make_workload(4, batch=8, prefix=(0, 8000), vocab=64, drafts=[63, 0, 40, 63, 5, 63, 33, 63],
+                      poison=True, seed=515, prefix_lens=[0, 1, 64, 127, 128, 129, 4097, 8000])
+    say(f"[gpu] pipelined vs plain order rope={rope}: n={w.n_nodes.tolist()} "
+        f"L={w.prefix_len.tolist()}")
+    assert w.n_max * (w.Hq // w.Hkv) > 128          # the two-sub-tile kernel
+    dev = to_device(w)
+    f = (torch.from_numpy((500000.0 ** (-np.arange(w.d // 2) * 2.0 / w.d)).astype(np.float32)).cuda()
+         if rope else None)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    outs = []
+    for pipe in ("1", "0"):
+        monkeypatch.setenv("SPEC_ATTN_PIPE", pipe)
+        out = torch.full((w.B, w.n_max, w.Hq, w.d), SENTINEL, dtype=torch.float32, device="cuda")
+        api.verify_tree_attn(dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"],
+                             dev["n_nodes"], dev["parents"], out=out, dev_error=err, inv_freq=f)
+        torch.cuda.synchronize()
+        outs.append(out)
+    monkeypatch.delenv("SPEC_ATTN_PIPE")
+    assert int(err.item()) == 0
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+    if not rope:
+        compare_attention(w, outs[0].cpu().numpy(), nodes_per_seq=8, rng=np.random.default_rng(5))
 
 
 def test_device_errors_are_reported(hip_lib):
