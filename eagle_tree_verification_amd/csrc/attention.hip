@@ -616,6 +616,9 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
     bf16x8_t vf_q[3];
     vf_q[0] = vread(vs_, 0);
     vf_q[1] = vread(vs_, 1);
+    // raised issue priority while this wave interleaves matrix and vector
+    // work, so the SIMD's other wave (in its score phase) fills the gaps
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int step = 0; step < 16; ++step) {
       const int kb = step >> 3, hb = (step >> 2) & 1, db = step & 3;
@@ -642,6 +645,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
       // nothing crosses a step boundary
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) lrow[nb] = lrow[nb] * alpha[nb] + ls[nb];
     if (__any(moved)) {
