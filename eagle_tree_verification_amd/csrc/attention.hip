@@ -37,18 +37,23 @@ constexpr float kLazy = 8.f;  // log2 of the largest weight the online softmax l
 // ---------------------------------------------------------------------------
 // Tree validation and ancestor masks.  anc[j] has bit i set iff node i is on
 // the root path of node j (j included).  Returns false for an invalid tree.
+// par_t is this thread's entry of the parent row (thread t < n holds node
+// t's parent), loaded by the caller together with the sequence's sizes: the
+// row is staged in LDS (par_s, 64 ints) and every root path is walked there,
+// so a deep tree costs LDS reads, not a chain of dependent global loads.
 // Called by every thread of the block; blockDim.x >= 64.
 // ---------------------------------------------------------------------------
-__device__ bool build_ancestors(const int32_t* par_b, int n, uint64_t* anc, int* flag) {
-  if (threadIdx.x == 0) *flag = 0;
-  __syncthreads();
+__device__ bool build_ancestors(int par_t, int n, uint64_t* anc, int* par_s, int* flag) {
   const int t = threadIdx.x;
+  if (t == 0) *flag = 0;
+  if (t < n) par_s[t] = par_t;
+  __syncthreads();
   if (t < n) {
     uint64_t m = 1ull << t;
-    bool bad = (t == 0) ? (par_b[0] != -1) : false;
+    bool bad = (t == 0) ? (par_s[0] != -1) : false;
     int j = t;
     while (!bad && j > 0) {
-      const int p = par_b[j];
+      const int p = par_s[j];
       if (p < 0 || p >= j) {
         bad = true;
       } else {
@@ -75,6 +80,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
     int32_t* dev_error) {
   __shared__ uint64_t anc[64];
   __shared__ int flag;
+  __shared__ int par_s[64];
   __shared__ int rows[64];
   __shared__ float qs[128];
   const int b = blockIdx.y;
@@ -84,6 +90,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
   const bool reporter = (blockIdx.x == 0 && lane == 0);
   const int n = n_nodes[b];
   const int L = prefix_len[b];
+  const int par_t = lane < n_max ? parents[(size_t)b * n_max + lane] : -1;
   if (n < 1 || n > n_max) {
     if (reporter) report(dev_error, SPEC_DEVERR_TREE);
     return;
@@ -92,7 +99,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(
     if (reporter) report(dev_error, SPEC_DEVERR_CAPACITY);
     return;
   }
-  if (!build_ancestors(parents + (size_t)b * n_max, n, anc, &flag)) {
+  if (!build_ancestors(par_t, n, anc, par_s, &flag)) {
     if (reporter) report(dev_error, SPEC_DEVERR_TREE);
     return;
   }
@@ -216,6 +223,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][ST * VS_STRIDE];
   __shared__ uint64_t anc[64];
   __shared__ int flag;
+  __shared__ int par_s[64];
   __shared__ int sorted_b;
   __shared__ int lens[256];
 
@@ -255,6 +263,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
 
   const int n = a.n_nodes[b];
   const int L = a.prefix_len[b];
+  const int par_t = tid < a.n_max ? a.parents[(size_t)b * a.n_max + tid] : -1;
   const bool reporter = (g == 0 && rb == 0 && s == 0 && tid == 0);
   if (n < 1 || n > a.n_max) {
     if (reporter) report(a.dev_error, SPEC_DEVERR_TREE);
@@ -268,7 +277,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
   if (s >= nsplit) return;
   const int Mb = n * a.G;
   if (rb * RPW >= Mb) return;
-  if (!build_ancestors(a.parents + (size_t)b * a.n_max, n, anc, &flag)) {
+  if (!build_ancestors(par_t, n, anc, par_s, &flag)) {
     if (reporter) report(a.dev_error, SPEC_DEVERR_TREE);
     return;
   }
