@@ -479,6 +479,71 @@ def paged_bench(w, dev, ws_attn, block_size=16, reps=20):
     return res
 
 
+def shard_bench(cfg_id, shards=8, reps=20):
+    """One GPU's share of an 8-way tensor-parallel target, at the workload's
+    batch, prefixes and trees.  Attention shards by KV head with no exchange:
+    the share is Hq/8 query heads over Hkv/8 KV heads (one, here).  The walk
+    shards the vocabulary: the share is a V/8 slice, walked here as a whole
+    vocabulary of that size; the small per-pass exchanges between shards are
+    not part of it."""
+    import torch
+
+    from eagle_tree_verification_amd import api
+    from eagle_tree_verification_amd.workloads import CONFIGS, make_workload, to_device
+
+    cfg = CONFIGS[cfg_id]
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
+
+    res = {"shards": shards}
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    if cfg.kv_dtype == "bf16" and cfg.hkv % shards == 0:
+        wa = make_workload(cfg_id, hq=cfg.hq // shards, hkv=cfg.hkv // shards, vocab=64)
+        da = to_device(wa)
+        out = torch.empty((wa.B, wa.n_max, wa.Hq, wa.d), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(1, api.verify_tree_attn_workspace_size(
+            wa.B, wa.n_max, wa.Hq, wa.Hkv, wa.d, wa.L_cap, api.SPEC_BF16)) * 4,
+            dtype=torch.uint8, device="cuda")
+        ms = timed(lambda: api.verify_tree_attn(da["q"], da["k_cache"], da["v_cache"],
+                                                da["prefix_len"], da["n_nodes"], da["parents"],
+                                                out=out, workspace=ws, dev_error=err))
+        nbytes, flops = attention_cost(wa)
+        res["attention"] = {"hq": wa.Hq, "hkv": wa.Hkv, "ms": round(ms, 4),
+                            "algorithmic_bytes": nbytes, "GBps": round(nbytes / ms / 1e6, 1),
+                            "frac_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBPS, 3),
+                            "mfma_tflops": round(flops / ms / 1e9, 1)}
+        del da, out, ws
+    Vs = -(-cfg.vocab // shards)
+    wv = make_workload(cfg_id, vocab=Vs, hq=4, hkv=1)
+    dv = to_device(wv)
+    acc = {}
+
+    def walk():
+        acc.update(api.accept_tree(dv["tokens"], dv["parents"], dv["n_nodes"], dv["draft_p"],
+                                   dv["logits"], wv.T, dv["u_accept"], dv["u_sample"],
+                                   wv.max_depth, dev_error=err))
+    ms = timed(walk)
+    al, path = acc["accept_len"].cpu().numpy(), acc["path"].cpu().numpy()
+    nbytes = accept_bytes(wv, al, path)
+    res["walk"] = {"vocab": Vs, "T": wv.T, "ms": round(ms, 4), "algorithmic_bytes": int(nbytes),
+                   "GBps": round(nbytes / ms / 1e6, 1), "mean_accept_len": round(float(al.mean()), 3)}
+    if int(err.item()) != 0:
+        raise RuntimeError(f"shard bench device error bits {int(err.item())}")
+    del dv
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -497,6 +562,8 @@ def main():
                     help="skip timing the EAGLE-2 tree construction")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip timing tree attention over a paged (block-table) cache")
+    ap.add_argument("--no-shard", action="store_true",
+                    help="skip timing one GPU's share of an 8-way tensor-parallel target")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -633,6 +700,8 @@ def main():
         rec["tree_build"] = tree_build_bench(w.B, 10, cfg.depth, w.V, cfg.drafts)
     if not args.no_paged:
         rec["paged"] = paged_bench(w, dev, ws_attn)
+    if not args.no_shard:
+        rec["shard"] = shard_bench(args.config)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)
