@@ -82,7 +82,8 @@ def test_maximum_trees(hip_lib, T):
 
 
 @pytest.mark.parametrize("hq,hkv,d,dt", [(4, 4, 16, "f32"), (8, 2, 64, "bf16"), (6, 3, 32, "f32"),
-                                         (16, 16, 128, "f32"), (12, 4, 128, "bf16")])
+                                         (16, 16, 128, "f32"), (12, 4, 128, "bf16"),
+                                         (4, 1, 128, "bf16"), (8, 1, 128, "bf16")])
 def test_attention_layouts(hip_lib, hq, hkv, d, dt):
     w = make_workload(4, batch=3, prefix=(70, 200), vocab=64, hq=hq, hkv=hkv, head_dim=d,
                       kv_dtype=dt, poison=True, seed=hq * 100 + d)
@@ -90,6 +91,28 @@ def test_attention_layouts(hip_lib, hq, hkv, d, dt):
     dev = to_device(w)
     host = run_gpu_step(w, dev, commit=False)
     compare_attention(w, host["attn"])
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 7])
+def test_forced_prefix_splits(hip_lib, monkeypatch, splits):
+    """SPEC_ATTN_SPLITS forces the number of prefix splits (merged by
+    log-sum-exp); every count, odd ones included, must give the oracle's
+    attention, on one KV head per sequence (the tensor-parallel share's
+    layout) with ragged prefixes and a tree-only sequence."""
+    api = hip_lib
+    w = make_workload(4, batch=5, prefix=(0, 1500), vocab=64, hq=4, hkv=1, poison=True, seed=600 + splits,
+                      prefix_lens=[0, 1, 200, 777, 1500])
+    say(f"[gpu] forced splits {splits}: n={w.n_nodes.tolist()} L={w.prefix_len.tolist()}")
+    monkeypatch.setenv("SPEC_ATTN_SPLITS", str(splits))
+    dev = to_device(w)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.full((w.B, w.n_max, w.Hq, w.d), SENTINEL, dtype=torch.float32, device="cuda")
+    api.verify_tree_attn(dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"],
+                         dev["n_nodes"], dev["parents"], out=out, dev_error=err)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("SPEC_ATTN_SPLITS")
+    assert int(err.item()) == 0
+    compare_attention(w, out.cpu().numpy())
 
 
 @pytest.mark.parametrize("rope", [False, True])
