@@ -819,12 +819,22 @@ Plan make_plan(int B, int n_max, int Hq, int Hkv, int d, int L_cap, int dtype) {
   if (!p.mfma) return p;
   const int G = Hq / Hkv;
   const int M = n_max * G;
+  const long cus = device_cu_count();
+  const long smax_by_len = (L_cap + 127) / 128;  // splits keep >= 128 keys
   if (M <= 64) {
     p.nb = 1; p.nw = 2;
   } else if (M <= 128) {
     p.nb = 1; p.nw = 4;
   } else {
     p.nb = 1; p.nw = 8; p.sub = 2;
+    // Few (sequence, head) units and short prefixes leave the 8-wave kernel
+    // fewer workgroups than CUs even at the most splits; 2-wave workgroups
+    // of 64 rows then fill the GPU (their row blocks re-read K/V from the
+    // XCD's L2).  Measured on one sequence of the 8B layout: 32 -> 25 us.
+    const long units8 = (long)B * Hkv * ((M + 255) / 256);
+    if (units8 * smax_by_len < cus) {
+      p.nw = 2; p.sub = 1;
+    }
   }
   if (const char* env = getenv("SPEC_ATTN_VARIANT")) {  // "NBxNW[xSUB]", tuning sweeps
     int nb = 0, nw = 0;
@@ -847,13 +857,12 @@ Plan make_plan(int B, int n_max, int Hq, int Hkv, int d, int L_cap, int dtype) {
   // outputs to write and merge (measured: a 16-sequence 70B-layout batch
   // runs 22% faster unsplit than in two splits, an 8-way KV-head shard 25%
   // faster in 4 splits than in 8).
-  const long target = device_cu_count();
+  const long target = cus;
   long S = base >= target ? 1 : (target + base - 1) / base;
   if (const char* env = getenv("SPEC_ATTN_SPLITS")) {  // prefix splits, tuning sweeps
     const long v = atol(env);
     if (v >= 1) S = v;
   }
-  const long smax_by_len = (L_cap + 127) / 128;
   if (S > smax_by_len) S = smax_by_len;
   if (S < 1) S = 1;
   long chunk = (L_cap + S - 1) / S;
