@@ -15,6 +15,8 @@
 // not written and reports a capacity error.
 //
 // The work is a few MB per call (memory-bound, small).
+#include <stdlib.h>
+
 #include "common.hpp"
 
 namespace specv {
@@ -32,6 +34,14 @@ __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) {
   const uint32_t u = __float_as_uint(x);
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// One plane pair (x, y) turned by the angle whose cosine and sine are (c, s).
+// Both write kernels call this, so they round the same expressions.
+__device__ __forceinline__ void rotate_pair(float x, float y, float c, float s, float* a,
+                                            float* b) {
+  *a = x * c - y * s;
+  *b = y * c + x * s;
 }
 
 // One workgroup per (node, sequence).  Every workgroup of a sequence checks
@@ -94,11 +104,11 @@ __global__ __launch_bounds__(NTW) void tree_kv_write_kernel(
     const int ia = style == kRopeInterleaved ? 2 * t : t;
     const int ib = style == kRopeInterleaved ? 2 * t + 1 : t + half;
     if (inv_freq) {
-      float c, s;
+      float c, s, ra, rb;
       rope_cs(pos, inv_freq[t], &c, &s);
-      const float x = load_as_f32(src + ia), y = load_as_f32(src + ib);
-      dst[ia] = from_f32<T>(x * c - y * s);
-      dst[ib] = from_f32<T>(y * c + x * s);
+      rotate_pair(load_as_f32(src + ia), load_as_f32(src + ib), c, s, &ra, &rb);
+      dst[ia] = from_f32<T>(ra);
+      dst[ib] = from_f32<T>(rb);
     } else {
       dst[ia] = src[ia];
       dst[ib] = src[ib];
@@ -109,6 +119,124 @@ __global__ __launch_bounds__(NTW) void tree_kv_write_kernel(
     const int c = e % d;
     const int h = e / d;
     vc[kv.offset(b, h, L + j, d) + c] = v_new[(((size_t)b * n_max + j) * Hkv + h) * d + c];
+  }
+}
+
+// bf16 caches with head_dim a multiple of 16 and 16-byte aligned buffers:
+// the same write in 16-byte chunks (eight values per load and store).  The
+// parent row is read together with the sequence's sizes, so a workgroup
+// waits for one round trip before its tree check instead of two.
+__device__ __forceinline__ void unpack8(const uint4& u, float* f) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ uint4 pack8(const float* f) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (uint32_t)from_f32<uint16_t>(f[2 * i]) | ((uint32_t)from_f32<uint16_t>(f[2 * i + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ __launch_bounds__(NTW) void tree_kv_write_vec_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ prefix_len,
+    const int32_t* __restrict__ n_nodes, const int32_t* __restrict__ parents, int n_max, int Hkv,
+    int d, KvRows kv, const float* __restrict__ inv_freq, int style,
+    int32_t* __restrict__ dev_error) {
+  __shared__ int s_depth;
+  __shared__ int s_bad;
+  __shared__ int s_par[SPEC_MAX_NODES];
+  const int j = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int n = n_nodes[b];
+  const int L = prefix_len[b];
+  const int par_t = tid < n_max ? parents[(size_t)b * n_max + tid] : -1;
+  const bool reporter = j == 0 && tid == 0;
+  if (n < 1 || n > n_max) {
+    if (reporter) report(dev_error, SPEC_DEVERR_TREE);
+    return;
+  }
+  if (L < 0 || (int64_t)L + n > kv.L_cap) {
+    if (reporter) report(dev_error, SPEC_DEVERR_CAPACITY);
+    return;
+  }
+  if (tid == 0) s_bad = 0;
+  if (tid < n) s_par[tid] = par_t;
+  __syncthreads();
+  if (tid < n) {  // walk to the root in LDS: parents[x] < x, root -1
+    int dep = 0, x = tid;
+    bool bad = tid == 0 ? s_par[0] != -1 : false;
+    while (!bad && x > 0) {
+      const int p = s_par[x];
+      if (p < 0 || p >= x) bad = true;
+      else { x = p; ++dep; }
+    }
+    if (tid == j) s_depth = dep;
+    if (bad) atomicOr(&s_bad, 1);
+  }
+  __syncthreads();
+  if (s_bad) {
+    if (reporter) report(dev_error, SPEC_DEVERR_TREE);
+    return;
+  }
+  if (!kv.blocks_ok(b, L, L + n)) {
+    if (reporter) report(dev_error, SPEC_DEVERR_CAPACITY);
+    return;
+  }
+  if (j >= n) return;
+  const int pos = L + s_depth;
+  const int cpr = d / 8;  // 16-byte chunks per head row
+  const size_t row = ((size_t)b * n_max + j) * Hkv;
+  // V: copied chunk by chunk
+  for (int e = tid; e < Hkv * cpr; e += NTW) {
+    const int h = e / cpr, c = e % cpr;
+    *reinterpret_cast<uint4*>(vc + kv.offset(b, h, L + j, d) + c * 8) =
+        *reinterpret_cast<const uint4*>(v_new + (row + h) * d + c * 8);
+  }
+  if (!inv_freq) {
+    for (int e = tid; e < Hkv * cpr; e += NTW) {
+      const int h = e / cpr, c = e % cpr;
+      *reinterpret_cast<uint4*>(kc + kv.offset(b, h, L + j, d) + c * 8) =
+          *reinterpret_cast<const uint4*>(k_new + (row + h) * d + c * 8);
+    }
+  } else if (style == kRopeInterleaved) {
+    // chunk c holds the planes 4c .. 4c + 3 as (2t, 2t + 1) pairs
+    for (int e = tid; e < Hkv * cpr; e += NTW) {
+      const int h = e / cpr, c = e % cpr;
+      float f[8], r[8];
+      unpack8(*reinterpret_cast<const uint4*>(k_new + (row + h) * d + c * 8), f);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        float cs, sn;
+        rope_cs(pos, inv_freq[4 * c + p], &cs, &sn);
+        rotate_pair(f[2 * p], f[2 * p + 1], cs, sn, &r[2 * p], &r[2 * p + 1]);
+      }
+      *reinterpret_cast<uint4*>(kc + kv.offset(b, h, L + j, d) + c * 8) = pack8(r);
+    }
+  } else {
+    // chunk c of the first half (planes 8c .. 8c + 7) pairs with chunk
+    // c + cpr / 2 of the second
+    const int hc = cpr / 2;
+    for (int e = tid; e < Hkv * hc; e += NTW) {
+      const int h = e / hc, c = e % hc;
+      const uint16_t* src = k_new + (row + h) * d + c * 8;
+      uint16_t* dst = kc + kv.offset(b, h, L + j, d) + c * 8;
+      float x[8], y[8], ra[8], rb[8];
+      unpack8(*reinterpret_cast<const uint4*>(src), x);
+      unpack8(*reinterpret_cast<const uint4*>(src + d / 2), y);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        float cs, sn;
+        rope_cs(pos, inv_freq[8 * c + p], &cs, &sn);
+        rotate_pair(x[p], y[p], cs, sn, &ra[p], &rb[p]);
+      }
+      *reinterpret_cast<uint4*>(dst) = pack8(ra);
+      *reinterpret_cast<uint4*>(dst + d / 2) = pack8(rb);
+    }
   }
 }
 
@@ -135,12 +263,26 @@ spec_status_t launch_kv_write(const void* k_new, const void* v_new, void* k_cach
   if (head_dim < 2 || head_dim > 1024 || head_dim % 2) return SPEC_E_DTYPE;
   if (inv_freq && rope_style != kRopeHalf && rope_style != kRopeInterleaved) return SPEC_E_VALUE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // The chunked kernel needs bf16, head_dim a multiple of 16 (whole chunks,
+  // and the half layout's planes paired chunk with chunk) and 16-byte
+  // aligned buffers.  SPEC_KV_WRITE_SCALAR=1 selects the element-wise kernel
+  // for comparisons; both write the same bits.
+  const auto aligned = [](const void* p) { return ((uintptr_t)p & 15u) == 0; };
+  bool vec_ok = dtype == SPEC_BF16 && head_dim % 16 == 0 && aligned(k_new) && aligned(v_new) &&
+                aligned(k_cache) && aligned(v_cache);
+  if (const char* env = getenv("SPEC_KV_WRITE_SCALAR")) vec_ok = vec_ok && env[0] != '1';
   if (dtype == SPEC_F32)
     hipLaunchKernelGGL(tree_kv_write_kernel<float>, dim3(n_max, B), dim3(NTW), 0, s,
                        static_cast<const float*>(k_new), static_cast<const float*>(v_new),
                        static_cast<float*>(k_cache), static_cast<float*>(v_cache), prefix_len,
                        n_nodes, parents, n_max, Hkv, head_dim, kv, inv_freq, rope_style,
                        dev_error);
+  else if (vec_ok)
+    hipLaunchKernelGGL(tree_kv_write_vec_kernel, dim3(n_max, B), dim3(NTW), 0, s,
+                       static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                       static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                       prefix_len, n_nodes, parents, n_max, Hkv, head_dim, kv, inv_freq,
+                       rope_style, dev_error);
   else
     hipLaunchKernelGGL(tree_kv_write_kernel<uint16_t>, dim3(n_max, B), dim3(NTW), 0, s,
                        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),

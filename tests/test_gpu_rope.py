@@ -159,6 +159,49 @@ def test_rope_write_errors(hip_lib):
     assert not np.array_equal(after[0], before[0])
 
 
+@pytest.mark.parametrize("style", ["half", "interleaved", None])
+@pytest.mark.parametrize("d", [64, 128])
+def test_chunked_write_equals_elementwise(hip_lib, monkeypatch, style, d):
+    """bf16 caches with head_dim a multiple of 16 are written by a chunked
+    kernel (16-byte loads and stores); SPEC_KV_WRITE_SCALAR=1 selects the
+    element-wise kernel.  Both must leave the same bits in the whole cache,
+    with the rotation or without, and the keys must match the oracle."""
+    api = hip_lib
+    w = make_workload(4, batch=6, prefix=(0, 300), vocab=64, head_dim=d, poison=True, seed=70 + d,
+                      drafts=[60, 0, 17, 33, 5, 60], prefix_lens=[0, 1, 63, 128, 250, 300])
+    say(f"[gpu] chunked vs element-wise write d={d} style={style}: n={w.n_nodes.tolist()}")
+    f = inv_freq(w.d, 500000.0, scale_low=8.0)
+    fdev = torch.from_numpy(f).to("cuda") if style else None
+    kn, vn = _kv_new(w, 5)
+    caches = []
+    for scalar in ("0", "1"):
+        monkeypatch.setenv("SPEC_KV_WRITE_SCALAR", scalar)
+        dev = to_device(w)
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        api.tree_kv_write(_dev(kn, w.kv_dtype), _dev(vn, w.kv_dtype), dev["k_cache"], dev["v_cache"],
+                          dev["prefix_len"], dev["n_nodes"], dev["parents"], inv_freq=fdev,
+                          rope_style=style or "half", dev_error=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        caches.append((_host(dev["k_cache"], w.kv_dtype), _host(dev["v_cache"], w.kv_dtype)))
+    monkeypatch.delenv("SPEC_KV_WRITE_SCALAR")
+    np.testing.assert_array_equal(caches[0][0], caches[1][0])
+    np.testing.assert_array_equal(caches[0][1], caches[1][1])
+    kc = caches[0][0]
+    for b in range(w.B):
+        n, L = int(w.n_nodes[b]), int(w.prefix_len[b])
+        par = w.parents[b, :n]
+        k0 = storage_to_f64(w.k_cache[b], w.kv_dtype)
+        v0 = storage_to_f64(w.v_cache[b], w.kv_dtype)
+        if style:
+            k2, _ = orope.tree_kv_write(k0, v0, storage_to_f64(kn[b], w.kv_dtype),
+                                        storage_to_f64(vn[b], w.kv_dtype), L, par, n, f, style)
+            got = storage_to_f64(kc[b], w.kv_dtype)[:, L:L + n]
+            assert np.all(np.abs(got - k2[:, L:L + n]) <= _key_tol(w.kv_dtype, k2[:, L:L + n]))
+        else:
+            np.testing.assert_array_equal(kc[b][:, L:L + n], np.transpose(kn[b][:n], (1, 0, 2)))
+
+
 @pytest.mark.timeout(900)
 def test_rope_full_size_serving(hip_lib):
     """Batch 64 (config 4 shape) with the rotated path, sampled against the
