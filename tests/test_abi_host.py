@@ -57,6 +57,43 @@ def test_attention_host_checks(lib):
     assert f(*bad) == SPEC_E_VALUE
 
 
+def _attn_ws(B, n_max, Hq, Hkv, L_cap):
+    """Workspace bytes the attention plan asks for: zero when the prefix is
+    not split, else fp32 partial rows plus their (max, sum) pairs."""
+    return api.verify_tree_attn_workspace_size(B, n_max, Hq, Hkv, 128, L_cap, api.SPEC_BF16)
+
+
+def _split_ws(B, Hkv, row_blocks, rows_per_block, L_cap, splits):
+    # the plan's chunking: ceil(L_cap / splits) rounded up to 64 keys
+    chunk = -(-L_cap // splits)
+    chunk = -(-chunk // 64) * 64
+    s_max = -(-L_cap // chunk)
+    rows = B * Hkv * row_blocks * rows_per_block * s_max
+    return rows * 128 * 4 + rows * 8 + 256
+
+
+def test_attention_plan_splits_and_variants(lib, monkeypatch):
+    """Host-side plan (no GPU: 256 CUs assumed).  Prefixes are split only up
+    to about one workgroup per CU, and a batch that the 8-wave kernel cannot
+    fill even fully split takes 64-row (2-wave) workgroups."""
+    for env in ("SPEC_ATTN_VARIANT", "SPEC_ATTN_SPLITS", "SPEC_ATTN_PIPE"):
+        monkeypatch.delenv(env, raising=False)
+    # 64 sequences x 8 KV heads, 244 rows per head: 512 workgroups, unsplit
+    assert _attn_ws(64, 61, 32, 8, 4160) == 0
+    # 16 sequences x 8 KV heads, 392 rows (2 row blocks of 256): 256, unsplit
+    assert _attn_ws(16, 49, 64, 8, 8256) == 0
+    # one KV head per sequence: 64 workgroups -> 4 splits of the prefix
+    assert _attn_ws(64, 61, 4, 1, 4160) == _split_ws(64, 1, 1, 256, 4160, 4)
+    # one sequence, 8 KV heads: 8 x 17 splits < 256 CUs -> 2-wave workgroups,
+    # 4 row blocks of 64, 32 units -> 8 splits
+    assert _attn_ws(1, 61, 32, 8, 2112) == _split_ws(1, 8, 4, 64, 2112, 8)
+    # a forced split count and variant are honoured
+    monkeypatch.setenv("SPEC_ATTN_SPLITS", "3")
+    assert _attn_ws(64, 61, 32, 8, 4160) == _split_ws(64, 8, 1, 256, 4160, 3)
+    monkeypatch.setenv("SPEC_ATTN_VARIANT", "1x8x2")
+    assert _attn_ws(1, 61, 32, 8, 2112) == _split_ws(1, 8, 1, 256, 2112, 3)
+
+
 def test_accept_host_checks(lib):
     P = _buf()
     f = lib.spec_accept_tree
