@@ -766,41 +766,56 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
   }
 }
 
-// Log-sum-exp merge of prefix splits: one block (HD threads) per query row.
-__global__ __launch_bounds__(HD) void attn_merge_kernel(MfmaArgs a, int rows_per_bg) {
-  const int r = blockIdx.x;
+// Log-sum-exp merge of prefix splits.  32 lanes per query row, four head
+// dims each (16-byte loads and stores); a 256-thread block merges
+// kMergeRows rows of one (sequence, KV head).  The parent row is read with
+// the sequence's sizes, so a block waits for one round trip before its tree
+// check.  Per element the splits are combined in split order, as ever.
+constexpr int kMergeRows = 8;
+__global__ __launch_bounds__(32 * kMergeRows) void attn_merge_kernel(MfmaArgs a,
+                                                                     int rows_per_bg) {
+  static_assert(HD == 32 * 4, "32 lanes of four dims cover a row");
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x * kMergeRows + (tid >> 5);
+  const int lane = tid & 31;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int n = a.n_nodes[b];
   const int L = a.prefix_len[b];
+  const int par_t = tid < a.n_max ? a.parents[(size_t)b * a.n_max + tid] : -1;
   if (n < 1 || n > a.n_max || L < 0 || (int64_t)L + n > a.L_cap) return;
-  if (r >= n * a.G) return;
+  if (blockIdx.x * kMergeRows >= n * a.G) return;
   // an invalid tree was skipped by the main kernel; skip it here as well
   __shared__ int bad;
-  if (threadIdx.x == 0) bad = 0;
+  if (tid == 0) bad = 0;
   __syncthreads();
-  if (threadIdx.x < n) {
-    const int p = a.parents[(size_t)b * a.n_max + threadIdx.x];
-    if (threadIdx.x == 0 ? p != -1 : (p < 0 || p >= (int)threadIdx.x)) atomicOr(&bad, 1);
-  }
+  if (tid < n && (tid == 0 ? par_t != -1 : (par_t < 0 || par_t >= tid))) atomicOr(&bad, 1);
   __syncthreads();
   if (bad) return;
   // so was a sequence whose rows sit in a block outside the pool
   if (a.kv.table && !a.kv.blocks_ok(b, 0, L + n)) return;
+  if (r >= n * a.G) return;
   const int nsplit = L > 0 ? (L + a.chunk - 1) / a.chunk : 1;
   const size_t base = (((size_t)b * a.Hkv + g) * rows_per_bg + r) * a.S_max;
   float mstar = -INFINITY;
   for (int s = 0; s < nsplit; ++s) mstar = fmaxf(mstar, a.part_ml[base + s].x);
-  float lsum = 0.f, acc = 0.f;
+  float lsum = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s = 0; s < nsplit; ++s) {
     const float2 ml = a.part_ml[base + s];
     const float wgt = fast_exp2((ml.x - mstar) * a.c);
     lsum += ml.y * wgt;
-    acc += a.part_o[(base + s) * HD + threadIdx.x] * wgt;
+    const float4 po = *reinterpret_cast<const float4*>(a.part_o + (base + s) * HD + lane * 4);
+    acc.x += po.x * wgt;
+    acc.y += po.y * wgt;
+    acc.z += po.z * wgt;
+    acc.w += po.w * wgt;
   }
   const int i = r / a.G;
   const int hh = r % a.G;
-  a.out[(((size_t)b * a.n_max + i) * a.Hq + (size_t)g * a.G + hh) * HD + threadIdx.x] = acc / lsum;
+  *reinterpret_cast<float4*>(a.out + (((size_t)b * a.n_max + i) * a.Hq + (size_t)g * a.G + hh) * HD +
+                             lane * 4) =
+      make_float4(acc.x / lsum, acc.y / lsum, acc.z / lsum, acc.w / lsum);
 }
 
 // ---------------------------------------------------------------------------
@@ -956,7 +971,12 @@ spec_status_t launch_attn(const void* q, const void* k_cache, const void* v_cach
     SPEC_HIP_TRY(hipGetLastError());
     return SPEC_OK;
   }
-  if (p.ws > 0 && (workspace == nullptr || workspace_bytes < p.ws)) return SPEC_E_WORKSPACE;
+  // 16-byte vector loads and stores (Q and K/V fragments, output rows,
+  // split partials)
+  const auto aligned = [](const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; };
+  if (!aligned(q) || !aligned(k_cache) || !aligned(v_cache) || !aligned(out)) return SPEC_E_SHAPE;
+  if (p.ws > 0 && (workspace == nullptr || workspace_bytes < p.ws || !aligned(workspace)))
+    return SPEC_E_WORKSPACE;
 
   MfmaArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -988,8 +1008,9 @@ spec_status_t launch_attn(const void* q, const void* k_cache, const void* v_cach
     launch_variant<false>(p, grid, strm, a);
   SPEC_HIP_TRY(hipGetLastError());
   if (p.S_max > 1) {
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(p.rb * p.rpw, Hkv, B), dim3(HD), 0, strm, a,
-                       p.rb * p.rpw);
+    hipLaunchKernelGGL(attn_merge_kernel,
+                       dim3((p.rb * p.rpw + kMergeRows - 1) / kMergeRows, Hkv, B),
+                       dim3(32 * kMergeRows), 0, strm, a, p.rb * p.rpw);
     SPEC_HIP_TRY(hipGetLastError());
   }
   return SPEC_OK;

@@ -66,10 +66,12 @@ typedef int32_t spec_status_t;
 enum {
   SPEC_OK = 0,
   SPEC_E_NULL = -1,        /* a required pointer is NULL                          */
-  SPEC_E_SHAPE = -2,       /* a size argument is out of range                     */
+  SPEC_E_SHAPE = -2,       /* a size argument is out of range, or a buffer that
+                              must be 16-byte aligned is not                      */
   SPEC_E_DTYPE = -3,       /* unsupported dtype / head_dim combination            */
   SPEC_E_VALUE = -4,       /* bad scalar (temperature < 0 or NaN, scale <= 0)     */
-  SPEC_E_WORKSPACE = -5,   /* workspace NULL or smaller than required             */
+  SPEC_E_WORKSPACE = -5,   /* workspace NULL, smaller than required, or (where it
+                              must be) not 16-byte aligned                        */
   SPEC_E_HIP = -6,         /* a HIP runtime call or launch failed                 */
   SPEC_E_UNSUPPORTED = -7  /* the current device cannot run this configuration    */
 };
@@ -120,6 +122,9 @@ typedef struct {
  *   out        [B][n_max][Hq][head_dim] float32; rows i >= n_nodes[b] and
  *              rows of failed sequences are not written
  *   workspace  >= spec_verify_tree_attn_workspace_size(...) bytes
+ * The matrix-core path (SPEC_BF16, head_dim 128) moves 16-byte vectors: q,
+ * k_cache, v_cache and out must then be 16-byte aligned (else SPEC_E_SHAPE),
+ * and so must a workspace it uses (else SPEC_E_WORKSPACE).
  * Device errors: SPEC_DEVERR_TREE, SPEC_DEVERR_CAPACITY.
  */
 spec_status_t spec_verify_tree_attn(

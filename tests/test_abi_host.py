@@ -57,6 +57,32 @@ def test_attention_host_checks(lib):
     assert f(*bad) == SPEC_E_VALUE
 
 
+def _aligned_buf(size=256):
+    raw = ctypes.create_string_buffer(size + 64)
+    addr = (ctypes.addressof(raw) + 63) // 64 * 64
+    return raw, addr
+
+
+def test_attention_alignment_checks(lib):
+    """The matrix-core path (bf16, head_dim 128) moves 16-byte vectors: a
+    misaligned q, K/V, output or used workspace is refused before any launch
+    (only refused calls are made here)."""
+    raw, A = _aligned_buf()
+    f = lib.spec_verify_tree_attn
+    P = ctypes.c_void_p(A)
+    good = [P] * 6 + [1, 6, 4, 4, 128, 4096, 0.25, api.SPEC_BF16, P]
+    for k in (0, 1, 2, 14):  # q, k_cache, v_cache, out
+        args = list(good)
+        args[k] = ctypes.c_void_p(A + 2)
+        assert f(*args, None, 0, None, None) == SPEC_E_SHAPE, k
+    # one sequence over a 4096-row cache is split, so the workspace is used
+    need = api.verify_tree_attn_workspace_size(1, 6, 4, 4, 128, 4096, api.SPEC_BF16)
+    assert need > 0
+    assert f(*good, ctypes.c_void_p(A + 4), need + 64, None, None) == SPEC_E_WORKSPACE
+    assert f(*good, None, need, None, None) == SPEC_E_WORKSPACE
+    del raw
+
+
 def _attn_ws(B, n_max, Hq, Hkv, L_cap):
     """Workspace bytes the attention plan asks for: zero when the prefix is
     not split, else fp32 partial rows plus their (max, sum) pairs."""
