@@ -202,6 +202,32 @@ def test_chunked_write_equals_elementwise(hip_lib, monkeypatch, style, d):
             np.testing.assert_array_equal(kc[b][:, L:L + n], np.transpose(kn[b][:n], (1, 0, 2)))
 
 
+def test_misaligned_new_rows_fall_back(hip_lib):
+    """New K rows that start 2 bytes past a 16-byte boundary cannot use the
+    chunked kernel; the write falls back to the element-wise one and leaves
+    the same cache bits as an aligned call."""
+    api = hip_lib
+    w = make_workload(4, batch=3, prefix=(10, 200), vocab=64, poison=True, seed=91)
+    f = torch.from_numpy(inv_freq(w.d, 500000.0, scale_low=8.0)).to("cuda")
+    kn, vn = _kv_new(w, 6)
+    kd, vd = _dev(kn, w.kv_dtype), _dev(vn, w.kv_dtype)
+    buf = torch.empty(kd.numel() + 1, dtype=kd.dtype, device="cuda")
+    k_off = buf[1:].view(kd.shape)
+    k_off.copy_(kd)
+    assert k_off.data_ptr() % 16 == 2
+    caches = []
+    for k_in in (kd, k_off):
+        dev = to_device(w)
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        api.tree_kv_write(k_in, vd, dev["k_cache"], dev["v_cache"], dev["prefix_len"],
+                          dev["n_nodes"], dev["parents"], inv_freq=f, dev_error=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        caches.append((_host(dev["k_cache"], w.kv_dtype), _host(dev["v_cache"], w.kv_dtype)))
+    np.testing.assert_array_equal(caches[0][0], caches[1][0])
+    np.testing.assert_array_equal(caches[0][1], caches[1][1])
+
+
 @pytest.mark.timeout(900)
 def test_rope_full_size_serving(hip_lib):
     """Batch 64 (config 4 shape) with the rotated path, sampled against the
