@@ -534,8 +534,11 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma_kernel(MfmaArgs a) {
   // equals the plain order's bit for bit.  The pending sub-tile's weights
   // sit in pfA at the end of every stage, its keys in (pbuf, psub); the
   // first pending product is of zero weights.
-  // (pipelined order) S^T (keys x rows) of the sub-tile of keys [64 * sub, 64 * sub + nrows) of
-  // the stage in buffer buf, for its two 32-key halves, masked.
+  // (pipelined order) S^T (keys x rows) of the sub-tile of keys
+  // [64 * sub, 64 * sub + nrows) of the stage in buffer buf, for its two
+  // 32-key halves, masked.  The plain order keeps its own inline copy of
+  // these lines: routing both through one helper changed the code generated
+  // for the other variants and made them slower.
   auto qk = [&](int buf, int sub, int nrows, bool tree, f32x16_t (*sacc)[2]) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
