@@ -39,10 +39,11 @@ longest passing prefix plus one corrected token lands each cycle).
 Sampling filters.  top_k / top_p restrict every q of the walk (filter_keep);
 the rule itself is unchanged, so the output follows the filtered q.
 
-Near ties.  Decisions whose |u - min(1, ratio)| < TIE_BAND and samples whose
-threshold u * W lies within SAMPLE_BAND * W of an edge of the chosen bucket
-are flagged; a flagged sequence-step is excluded from bit-exact comparison
-with another implementation and logged.
+Near ties.  Decisions whose |u - min(1, ratio)| < TIE_BAND, samples whose
+threshold u * W lies within SAMPLE_BAND * W of an edge of the chosen bucket,
+and residuals whose mass is a positive fraction below DEGENERATE_BAND of the
+distribution they came from are flagged; a flagged sequence-step is excluded
+from bit-exact comparison with another implementation and logged.
 """
 from dataclasses import dataclass, field
 from typing import List, Optional
@@ -53,6 +54,7 @@ from .validate import ERR_NONFINITE, ERR_TOKEN, ERR_TREE, validate_tree
 
 TIE_BAND = 1e-6
 SAMPLE_BAND = 1e-9
+DEGENERATE_BAND = 1e-12
 
 
 def _full_distribution(lr, T):
@@ -109,21 +111,36 @@ def target_distribution(logit_row, T, top_k=0, top_p=0.0):
     return e / e.sum()
 
 
-def accept_rule(q_x, p_x, u):
-    """Build step 1: accept when p(x) <= 0, else iff u < min(1, q(x)/p(x))."""
-    if p_x <= 0.0:
-        return True, np.inf
-    thr = min(1.0, q_x / p_x)
-    return bool(u < thr), thr
+def keep_probability(target_x, draft_x):
+    """Probability with which a draft token x survives its test.
+
+    Page "推测解码与 EAGLE-3", build step 1 (section "第 1 步：拒绝规则"): the
+    token is kept with probability min(1, target(x) / draft(x)).  A token the
+    draft distribution gives no mass is kept outright; that case is returned
+    as +inf so that every u in [0, 1) passes the strict comparison u < value.
+    """
+    if draft_x > 0.0:
+        return min(1.0, target_x / draft_x)
+    return np.inf
 
 
-def residual(q, p):
-    """Build step 2: (q - p)_+ normalised; zero mass returns q unchanged."""
-    raw = np.maximum(0.0, q - p)
-    s = raw.sum()
-    if s == 0.0:
-        return np.array(q, dtype=np.float64, copy=True)
-    return raw / s
+def remove_draft_mass(dist, draft):
+    """The distribution a rejection leaves behind, and the mass it had.
+
+    Page "推测解码与 EAGLE-3", build step 2 (section "第 2 步：残差分布"): after
+    a rejection the next token comes from the part of the distribution the
+    draft under-covers, (dist - draft)_+, renormalised.  When that part is
+    empty (draft >= dist everywhere) the page keeps the distribution that was
+    being corrected.  Returns (next distribution, mass of (dist - draft)_+);
+    the mass is the ratio of successive residual masses that a closed-form
+    implementation computes, and a tiny positive value marks a residual that
+    rounding decides.
+    """
+    excess = np.clip(np.asarray(dist, np.float64) - np.asarray(draft, np.float64), 0.0, None)
+    mass = float(excess.sum())
+    if mass > 0.0:
+        return excess / mass, mass
+    return np.array(dist, dtype=np.float64, copy=True), mass
 
 
 def sample_inverse_cdf(dist, u):
@@ -182,6 +199,48 @@ def _fail(err):
     return AcceptResult(-1, [], [], None, [], False, err)
 
 
+def _children_lists(parents, n):
+    kids = [[] for _ in range(n)]
+    for j in range(1, n):
+        kids[int(parents[j])].append(j)
+    return kids
+
+
+def visit_node(v, target, draft_row, kids, toks, u_accept, records):
+    """The child tests at one visited node (T > 0).
+
+    target: the verifier's distribution at v (already filtered).  The
+    children are tested in ascending id (reading for several children, module
+    docstring); each rejection replaces the distribution under test by what
+    remove_draft_mass leaves of it against v's draft row.  The draft row is
+    checked for non-finite entries only once a rejection uses all of it (a
+    walk reads nothing else of it).  Appends a record per test and per
+    residual to `records` and returns (accepted child or None, the
+    distribution under test when the node's tests ended, error bits).
+    """
+    dist = target
+    checked = False
+    for c in kids:
+        x = toks[c]
+        px = float(draft_row[x])
+        if not np.isfinite(px):
+            return None, dist, ERR_NONFINITE
+        u = float(u_accept[c])
+        kp = keep_probability(dist[x], px)
+        passed = u < kp
+        records.append((v, c, "accept-test", u, kp, abs(u - kp) if np.isfinite(kp) else np.inf,
+                        passed))
+        if passed:
+            return c, dist, 0
+        if not checked:
+            if not np.all(np.isfinite(np.asarray(draft_row, dtype=np.float64))):
+                return None, dist, ERR_NONFINITE
+            checked = True
+        dist, mass = remove_draft_mass(dist, draft_row)
+        records.append((v, c, "residual", None, mass, mass, None))
+    return None, dist, 0
+
+
 def accept_tree(tokens, parents, n_nodes, draft_p, logits, T, u_accept, u_sample,
                 max_depth, n_max=None, top_k=0, top_p=0.0):
     """One sequence's acceptance walk.
@@ -192,6 +251,12 @@ def accept_tree(tokens, parents, n_nodes, draft_p, logits, T, u_accept, u_sample
     after v.  top_k / top_p: the sampling filters of filter_keep, applied to
     every q of the walk at T > 0 (greedy decoding is unaffected: the argmax
     always passes both).
+
+    Near ties (flag `near_tie`): a test with |u - keep probability| <
+    TIE_BAND, a sample whose threshold lies within SAMPLE_BAND of an edge of
+    the chosen bucket, a top-p boundary within TIE_BAND, and a residual whose
+    mass is positive but below DEGENERATE_BAND of the distribution it came
+    from (rounding then decides what is left).
     """
     n = int(n_nodes)
     if n_max is None:
@@ -203,25 +268,21 @@ def accept_tree(tokens, parents, n_nodes, draft_p, logits, T, u_accept, u_sample
     toks = [int(t) for t in tokens[:n]]
     if any(t < 0 or t >= V for t in toks[1:]):
         return _fail(ERR_TOKEN)
-    children = [[] for _ in range(n)]
-    for j in range(1, n):
-        children[int(parents[j])].append(j)
+    kids = _children_lists(parents, n)
 
+    path, emitted, records = [0], [], []
     v = 0
-    path = [0]
-    out = []
-    decisions = []
-    near = False
     while True:
         lrow = np.asarray(logits[v], dtype=np.float64)
         if not np.all(np.isfinite(lrow)):
             return _fail(ERR_NONFINITE)
         if T == 0:
+            # greedy: the first child carrying the verifier's argmax survives
             best = int(np.argmax(lrow))
-            nxt = next((c for c in children[v] if toks[c] == best), None)
-            decisions.append((v, -1 if nxt is None else nxt, "argmax", None, best, None,
-                              nxt is not None))
-            out.append(best)
+            nxt = next((c for c in kids[v] if toks[c] == best), None)
+            records.append((v, -1 if nxt is None else nxt, "argmax", None, best, None,
+                            nxt is not None))
+            emitted.append(best)
             if nxt is None:
                 final = np.zeros(V)
                 final[best] = 1.0
@@ -230,41 +291,51 @@ def accept_tree(tokens, parents, n_nodes, draft_p, logits, T, u_accept, u_sample
             v = nxt
             continue
 
-        cur = target_distribution(lrow, T, top_k, top_p)
+        target = target_distribution(lrow, T, top_k, top_p)
         if 0.0 < top_p < 1.0:
             _, fm = filter_keep(lrow, T, top_k, top_p)
-            near |= fm < TIE_BAND
-            decisions.append((v, -1, "filter", None, top_p, fm, None))
-        prow = None
-        nxt = None
-        for c in children[v]:
-            x = toks[c]
-            px = float(draft_p[v][x])
-            if not np.isfinite(px):
-                return _fail(ERR_NONFINITE)
-            u = float(u_accept[c])
-            acc, thr = accept_rule(cur[x], px, u)
-            margin = abs(u - thr) if np.isfinite(thr) else np.inf
-            near |= margin < TIE_BAND
-            decisions.append((v, c, "accept-test", u, thr, margin, acc))
-            if acc:
-                nxt = c
-                break
-            if prow is None:
-                prow = np.asarray(draft_p[v], dtype=np.float64)
-                if not np.all(np.isfinite(prow)):
-                    return _fail(ERR_NONFINITE)
-            cur = residual(cur, prow)
+            records.append((v, -1, "filter", None, top_p, fm, None))
+        nxt, dist, err = visit_node(v, target, draft_p[v], kids[v], toks, u_accept, records)
+        if err:
+            return _fail(err)
         if nxt is not None:
             path.append(nxt)
-            out.append(toks[nxt])
+            emitted.append(toks[nxt])
             v = nxt
             continue
         us = float(u_sample[v])
-        tok, margin = sample_inverse_cdf(cur, us)
-        near |= margin < SAMPLE_BAND
-        decisions.append((v, -1, "sample", us, tok, margin, None))
-        out.append(tok)
-        final = cur
+        tok, margin = sample_inverse_cdf(dist, us)
+        records.append((v, -1, "sample", us, tok, margin, None))
+        emitted.append(tok)
+        final = dist
         break
-    return AcceptResult(len(path) - 1, path, out, final, decisions, near, 0)
+    near = any(_is_near_tie(r) for r in records)
+    return AcceptResult(len(path) - 1, path, emitted, final, records, near, 0)
+
+
+def _is_near_tie(record):
+    kind, margin = record[2], record[5]
+    if kind in ("accept-test", "filter"):
+        return margin < TIE_BAND
+    if kind == "sample":
+        return margin < SAMPLE_BAND
+    if kind == "residual":
+        return 0.0 < margin < DEGENERATE_BAND
+    return False
+
+
+def terminal_distribution(node, tokens, parents, n_nodes, draft_p, logits, T, top_k=0, top_p=0.0):
+    """The distribution a walk that stops at `node` draws its last token
+    from: the verifier's distribution there with every child of the node
+    rejected in ascending id (T > 0), or the point mass at the argmax (T = 0).
+    Used to check a walk taken by another implementation."""
+    lrow = np.asarray(logits[node], dtype=np.float64)
+    if T == 0:
+        out = np.zeros(len(lrow))
+        out[int(np.argmax(lrow))] = 1.0
+        return out
+    dist = target_distribution(lrow, T, top_k, top_p)
+    draft = np.asarray(draft_p[node], dtype=np.float64)
+    for c in _children_lists(parents, int(n_nodes))[node]:
+        dist, _ = remove_draft_mass(dist, draft)
+    return dist

@@ -1,12 +1,12 @@
 """GPU parity at the five configs' full sizes, in the launch configuration the
 benchmark times (the library's default plan for each shape).
 
-Attention is compared with the oracle on sampled outputs: the sequences with
-the longest and shortest prefix plus one more, the root, the last node and
-random nodes, the first and last head of a KV group and random heads; every
-other output is checked to be finite.  The acceptance walk is compared on
-every sequence (bit-exact except logged near ties) and the commit on every
-sequence (bit-exact).
+Attention is compared with the oracle on every sequence and every query head,
+at the root, the last node and random nodes of each tree (every node of a
+small tree); every other output is checked to be finite.  The acceptance walk is compared on
+every sequence (bit-exact except a near tie the oracle confirms, at most one
+per case, itself checked for a valid walk) and the commit on every sequence
+(bit-exact).
 
 A second test runs 50,000 independent tiny-chain steps in one launch and
 checks the Leviathan invariant on the GPU's own output: the first emitted
@@ -45,20 +45,16 @@ def test_full_size_step(hip_lib, cfg, T):
     for b in range(w.B):
         assert np.isfinite(attn[b, : w.n_nodes[b]]).all(), b
     rng = np.random.default_rng(1000 + cfg)
-    if w.B <= 2:
-        seqs = list(range(w.B))
-    else:
-        seqs = sorted({int(np.argmax(w.prefix_len)), int(np.argmin(w.prefix_len)),
-                       int(rng.integers(w.B))})
-    G = w.Hq // w.Hkv
-    heads = sorted({0, G - 1, min(G, w.Hq - 1), w.Hq - 1, *rng.choice(w.Hq, size=2).tolist()})
-    nodes = None if w.n_max <= 8 else 6
-    worst = compare_attention(w, attn, nodes_per_seq=nodes, heads=heads, seqs=seqs, rng=rng)
+    # every sequence and every query head (so every KV head and, in a large
+    # batch, the longest-first order of the sequences); the root, the last
+    # node and random nodes of each tree (all of a small tree; six random
+    # ones at batch 1, one in a batch)
+    nodes = None if w.n_max <= 8 else (6 if w.B <= 2 else 1)
+    worst = compare_attention(w, attn, nodes_per_seq=nodes, rng=rng)
 
     excluded = compare_accept(w, host)
-    say(f"[gpu]   attention max|diff|={worst:.3g} on sequences {seqs}, heads {heads}; "
+    say(f"[gpu]   attention max|diff|={worst:.3g} on all {w.B} sequences and {w.Hq} heads; "
         f"accepted {int(host['accept_len'].sum())} drafts; near-tie sequences excluded: {excluded}")
-    assert len(excluded) <= max(1, w.B // 8)
     compare_commit(w, host, kv_host(dev["k_cache"], w.kv_dtype),
                    kv_host(dev["v_cache"], w.kv_dtype), dev["prefix_len"].cpu().numpy())
 
@@ -97,8 +93,7 @@ def test_leviathan_marginals_50k_steps(hip_lib):
     host = run_gpu_step(w, dev, final_dist=False, commit=False)
     assert host["dev_error"] == 0
     # the GPU's steps agree with the oracle's (first 500 sequences)
-    excluded = compare_accept(w, host, seqs=range(500))
-    assert len(excluded) <= 5
+    compare_accept(w, host, seqs=range(500))
 
     rng = np.random.default_rng(20240501)
     q0 = [oracle.target_distribution(w.logits[b, 0], w.T) for b in range(B)]

@@ -5,8 +5,9 @@ shrinks the prefix and vocabulary so the oracle finishes in seconds; all still
 span several 64-key tiles with a ragged tail.  Inputs are poisoned with NaN
 everywhere the path must not read.  Bars: attention within 1e-5 (f32) /
 2e-2 (bf16) absolute; accepted lengths, paths, emitted tokens and committed KV
-bit-exact except sequence-steps with a logged near tie; residual
-distributions within 1e-5 absolute.
+bit-exact except a near tie the oracle confirms (at most one sequence per
+case, itself checked for a valid walk); residual distributions within 1e-5
+absolute.
 """
 import numpy as np
 import pytest
@@ -33,7 +34,6 @@ def test_step_parity(hip_lib, name):
     worst = compare_attention(w, host["attn"])
     excluded = compare_accept(w, host)
     say(f"[gpu]   attention max|diff|={worst:.3g}; near-tie sequences excluded: {excluded}")
-    assert len(excluded) <= max(1, w.B // 4)
     compare_commit(w, host, kv_host(dev["k_cache"], w.kv_dtype), kv_host(dev["v_cache"], w.kv_dtype),
                    dev["prefix_len"].cpu().numpy())
 
@@ -75,8 +75,7 @@ def test_maximum_trees(hip_lib, T):
     host = run_gpu_step(w, dev)
     assert host["dev_error"] == 0
     compare_attention(w, host["attn"], nodes_per_seq=12, rng=np.random.default_rng(1))
-    excluded = compare_accept(w, host)
-    assert len(excluded) <= 1
+    compare_accept(w, host)
     compare_commit(w, host, kv_host(dev["k_cache"], w.kv_dtype), kv_host(dev["v_cache"], w.kv_dtype),
                    dev["prefix_len"].cpu().numpy())
 

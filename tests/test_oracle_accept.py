@@ -156,7 +156,7 @@ def test_enumeration_depth_two(V, K1, K2):
 
 def test_enumeration_detects_testing_siblings_against_the_same_q(monkeypatch):
     # Planted mistake: no residual update between siblings.  Not lossless.
-    monkeypatch.setattr(oacc, "residual", lambda q, p: np.array(q, copy=True))
+    monkeypatch.setattr(oacc, "remove_draft_mass", lambda q, p: (np.array(q, copy=True), 1.0))
     qf, pf = _dists(4, 143)
     P1, _ = _tree_marginals(4, [-1, 0, 0, 0], qf, pf)
     assert np.abs(P1 - qf(())).max() > 1e-3
@@ -164,9 +164,9 @@ def test_enumeration_detects_testing_siblings_against_the_same_q(monkeypatch):
 
 def test_enumeration_detects_swapped_ratio(monkeypatch):
     # Planted mistake: min(1, p/q) instead of min(1, q/p).
-    real = oacc.accept_rule
-    monkeypatch.setattr(oacc, "accept_rule",
-                        lambda qx, px, u: real(px * px / max(qx, 1e-300), px, u))
+    real = oacc.keep_probability
+    monkeypatch.setattr(oacc, "keep_probability",
+                        lambda qx, px: real(px * px / max(qx, 1e-300), px))
     qf, pf = _dists(3, 121)
     P1, _ = _tree_marginals(3, [-1, 0, 0], qf, pf)
     assert np.abs(P1 - qf(())).max() > 1e-3
@@ -263,7 +263,7 @@ def test_leviathan_chi_square_50k(cfg1):
 
 
 def test_leviathan_negative_control_always_accept(cfg1, monkeypatch):
-    monkeypatch.setattr(oacc, "accept_rule", lambda qx, px, u: (True, 1.0))
+    monkeypatch.setattr(oacc, "keep_probability", lambda qx, px: np.inf)
     first, _ = _chain_steps(cfg1, 10_000, seed=7)
     q0 = softmax(cfg1.logits[0, 0].astype(np.float64))
     stat, crit = _gof(first, q0)
@@ -406,13 +406,34 @@ def test_iterated_residual_equals_closed_form(seed):
     c = 0.0
     W = 1.0
     for k in range(1, 6):
-        cur = oracle.residual(cur, p)
+        cur, mass = oracle.remove_draft_mass(cur, p)
         c = c + W
         raw = np.maximum(0.0, q - c * p)
-        W = raw.sum()
+        W_prev, W = W, raw.sum()
         if W == 0:
             break
         np.testing.assert_allclose(cur, raw / W, rtol=0, atol=1e-12)
+        # the mass a rejection removes is the ratio of successive closed-form masses
+        assert abs(mass - W / W_prev) <= 1e-12 * max(1.0, W / W_prev)
+
+
+def test_degenerate_residual_is_a_near_tie():
+    # q and p differ by 1e-14 on two tokens: the residual after the child's
+    # rejection has mass ~1e-14, which rounding decides
+    V = 4
+    p = np.full(V, 0.25)
+    for eps, flagged in ((1e-14, True), (1e-3, False)):
+        q = p + np.array([eps, -eps, 0.0, 0.0])
+        logits = np.log(np.stack([q, q]))
+        draft = np.stack([p, p])
+        # token 1 has ratio (0.25 - eps) / 0.25 < 1; u just below 1 rejects it
+        r = oracle.accept_tree([0, 1], [-1, 0], 2, draft, logits, 1.0, [0.0, HI], [0.5, 0.5], 1)
+        assert r.accept_len == 0
+        res = [d for d in r.decisions if d[2] == "residual"]
+        assert len(res) == 1 and abs(res[0][4] - eps) < 1e-15
+        assert r.near_tie == flagged
+        if not flagged:
+            assert r.out_tokens == [0]   # all the residual mass sits on token 0
 
 
 def test_inverse_cdf_hand_worked_cases():
