@@ -684,7 +684,9 @@ __device__ bool filter_threshold(const AcceptArgs& a, int bl, int part, int& gen
       if (use_p) {
         // P - (mass above t) > 0 always; (mass at or above t) - P matters
         // only when top-p chose the bucket
-        double mg = (double)(P - above_m) / kMassOne;
+        // nothing above the largest logit: an exactly zero mass, which no
+        // rounding can bring to P
+        double mg = above_m > 0 ? (double)(P - above_m) / kMassOne : 1.0;
         if (js == jp) mg = fmin(mg, (double)(selF - P) / kMassOne);
         margin = mg;
       }

@@ -79,8 +79,9 @@ def filter_keep(logit_row, T, top_k=0, top_p=0.0):
     turns it on.
 
     Returns (keep, margin): margin is the smallest |mass above - top_p| over
-    the tokens the top-k filter keeps (inf with top-p off); a margin under
-    TIE_BAND marks a decision rounding could flip.
+    the tokens the top-k filter keeps, leaving out the largest logit's tokens
+    (nothing is above them, an exactly zero mass); inf with top-p off.  A
+    margin under TIE_BAND marks a decision rounding could flip.
     """
     lr = np.asarray(logit_row, dtype=np.float64)
     V = len(lr)
@@ -95,7 +96,12 @@ def filter_keep(logit_row, T, top_k=0, top_p=0.0):
         _, grp = np.unique(-lr, return_inverse=True)
         gmass = np.bincount(grp, weights=q)
         above = np.concatenate([[0.0], np.cumsum(gmass)[:-1]])[grp]
-        margin = float(np.min(np.abs(above[keep] - top_p)))
+        # the tokens of the largest logit have nothing above them: that mass
+        # is an empty sum, exactly 0 < top_p in any precision, so it decides
+        # nothing rounding could flip
+        cand = above[keep]
+        cand = cand[cand > 0.0]
+        margin = float(np.min(np.abs(cand - top_p))) if cand.size else np.inf
         keep &= above < top_p
     return keep, margin
 

@@ -613,3 +613,14 @@ def test_top_p_boundary_is_a_near_tie():
     assert not r.near_tie
     # token 0 is outside the nucleus at 0.7: q(0) = 0, so it is rejected
     assert r.accept_len == 0 and r.out_tokens[0] in (1, 2, 3)
+
+
+def test_top_p_below_the_largest_token_is_not_a_near_tie():
+    # A nucleus smaller than the largest token's mass keeps only that token;
+    # nothing lies above it (an exactly zero mass), so its margin is not counted.
+    lg = np.log(np.array([1.0, 3.0, 2.0, 0.5]))
+    keep, margin = oracle.filter_keep(lg, 1.0, 0, 1e-30)
+    assert keep.tolist() == [False, True, False, False] and margin > 0.1
+    r = oracle.accept_tree([0, 1], [-1, 0], 2, np.full((2, 4), 0.25), np.stack([lg, lg]), 1.0,
+                           [0.0, 0.5], [0.5, 0.5], 1, top_p=1e-30)
+    assert not r.near_tie and r.accept_len == 1 and r.out_tokens == [1, 1]
