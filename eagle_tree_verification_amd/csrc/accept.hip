@@ -157,20 +157,19 @@ struct AcceptArgs {
   int spin_limit;
 };
 
-// ---- block reductions (fixed order, so results are deterministic) ---------
-__device__ double block_sum(double v, double* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  const int wv = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wv] = v;
-  __syncthreads();
-  double t = 0.0;
-#pragma unroll
-  for (int k = 0; k < NT / 64; ++k) t += red[k];
-  return t;
+// ---- wave-uniform values ------------------------------------------------------
+// The walk's combined statistics are identical in every lane and wave (they
+// come from fixed-order butterfly reductions whose every lane holds the same
+// bits).  Taking them from the first lane tells the compiler so, which keeps
+// them in scalar registers.
+__device__ __forceinline__ double uni(double x) {
+  const long long bits = __double_as_longlong(x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(bits & 0xffffffffll));
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(bits >> 32));
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
 
+// ---- block reductions (fixed order, so results are deterministic) ---------
 __device__ float block_max(float v, double* red) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -184,19 +183,70 @@ __device__ float block_max(float v, double* red) {
   return t;
 }
 
-// Butterfly reductions over one wave.  Every lane ends with the same value,
-// and every wave running them on the same inputs gets the same bits, so all
-// workgroups of a sequence reach identical decisions.
+// Reductions over one wave on DPP lane moves (no LDS round trip per step):
+// swaps within quads (lane ^ 1, lane ^ 2), mirrors within eight and sixteen
+// lanes, then the row broadcasts that add row 0 into row 1, row 2 into row 3,
+// and rows 0-1 into rows 2-3, leaving the total in lane 63, which is read
+// back as a wave-uniform value.  A fixed sequence of operations: every wave
+// reducing the same 64 inputs gets the same bits, so all workgroups of a
+// sequence reach identical decisions.  Lanes a row broadcast leaves out take
+// the operation's identity.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_move(double x, double ident) {
+  const unsigned long long xb = (unsigned long long)__double_as_longlong(x);
+  const unsigned long long ib = (unsigned long long)__double_as_longlong(ident);
+  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp((int)(ib & 0xffffffffu),
+                                                            (int)(xb & 0xffffffffu), CTRL, ROWS,
+                                                            0xf, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp((int)(ib >> 32), (int)(xb >> 32),
+                                                            CTRL, ROWS, 0xf, false);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double lane63(double x) {
+  const unsigned long long xb = (unsigned long long)__double_as_longlong(x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(xb & 0xffffffffu), 63);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(xb >> 32), 63);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm(1, 0, 3, 2)
+constexpr int kDppXor2 = 0x4E;        // quad_perm(2, 3, 0, 1)
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142;
+constexpr int kDppBcast31 = 0x143;
+
 __device__ __forceinline__ double wave_max_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
-  return v;
+  v = fmax(v, dpp_move<kDppXor1, 0xf>(v, -INFINITY));
+  v = fmax(v, dpp_move<kDppXor2, 0xf>(v, -INFINITY));
+  v = fmax(v, dpp_move<kDppHalfMirror, 0xf>(v, -INFINITY));
+  v = fmax(v, dpp_move<kDppMirror, 0xf>(v, -INFINITY));
+  v = fmax(v, dpp_move<kDppBcast15, 0xa>(v, -INFINITY));
+  v = fmax(v, dpp_move<kDppBcast31, 0xc>(v, -INFINITY));
+  return lane63(v);
 }
 
 __device__ __forceinline__ double wave_sum_d(double v) {
+  v += dpp_move<kDppXor1, 0xf>(v, 0.0);
+  v += dpp_move<kDppXor2, 0xf>(v, 0.0);
+  v += dpp_move<kDppHalfMirror, 0xf>(v, 0.0);
+  v += dpp_move<kDppMirror, 0xf>(v, 0.0);
+  v += dpp_move<kDppBcast15, 0xa>(v, 0.0);
+  v += dpp_move<kDppBcast31, 0xc>(v, 0.0);
+  return lane63(v);
+}
+
+__device__ double block_sum(double v, double* red) {
+  v = wave_sum_d(v);
+  const int wv = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wv] = v;
+  __syncthreads();
+  double t = 0.0;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  for (int k = 0; k < NT / 64; ++k) t += red[k];
+  return t;
 }
 
 // Combines per-thread (max, sum of exp relative to max) over the workgroup:
@@ -714,10 +764,15 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   // [256][kCopies] uint32 counts in rows 4-5
   __shared__ double scan[FILT && NG < 6 ? 6 : (NG < 2 ? 2 : NG)][NT];
   __shared__ FilterShared fsh;
-  __shared__ double gtot[NG];
-  __shared__ int s_or, s_hit, s_gsel, s_tsel;
+  __shared__ double gsum_w[NG][NT / 64];   // wave sums of each group (ordered scan)
+  // scan[g][t]: thread t's sum over group g of the last pass, kept for the
+  // ordered scan of the terminal sample; after a statistics pass each sum is
+  // relative to exp(mref[k][t]), k = g / BG1, the thread's running maximum of
+  // z when it summed the batch holding group g
+  __shared__ double mref[NG / BG1][NT];
+  __shared__ double wtot[NT / 64];
+  __shared__ int s_or, s_hit, s_first;
   __shared__ float s_kp[SPEC_MAX_NODES], s_kl[SPEC_MAX_NODES], s_ku[SPEC_MAX_NODES], s_us;
-  __shared__ double s_before;
   __shared__ double s_tab[kTab];
 
   const int bl = blockIdx.x / a.KP;   // sequence within this launch's group
@@ -891,17 +946,29 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
               nf |= valid && !isfinite(xv[gb][j]);
               bmax = fmaxf(bmax, xv[gb][j]);
             }
-          if (bmax == -INFINITY) return;  // nothing valid in this batch
+          if (bmax == -INFINITY) {  // nothing valid in this batch
+#pragma unroll
+            for (int gb = 0; gb < BG1; ++gb) scan[g0 + gb][tid] = 0.0;
+            mref[g0 / BG1][tid] = -INFINITY;
+            return;
+          }
           const double zb = (double)bmax * invT;
           if (zb > m) {
             es *= exp_tab(m - zb, s_tab);  // m = -inf: es is still 0
             m = zb;
           }
+          mref[g0 / BG1][tid] = m;
 #pragma unroll
-          for (int gb = 0; gb < BG1; ++gb)
+          for (int gb = 0; gb < BG1; ++gb) {
+            double sg = 0.0;
 #pragma unroll
-            for (int j = 0; j < W; ++j) es += exp_tab(fma((double)xv[gb][j], invT, -m), s_tab);
+            for (int j = 0; j < W; ++j) sg += exp_tab(fma((double)xv[gb][j], invT, -m), s_tab);
+            es += sg;
+            scan[g0 + gb][tid] = sg;
+          }
         });
+    // scan holds this node's sums of exp(z - M) once rescaled by mref
+    bool scan_ok = true, scan_rel = true;
     nf = block_or(nf, &s_or);
     block_lse(m, es, red);
     if (!exchange(a, bl, part, gen, m, nf ? -1.0 : es, xs, &s_or)) {
@@ -916,9 +983,9 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       if (writer0) write_failure(a, b, SPEC_DEVERR_NONFINITE);
       return;
     }
-    const double M = wave_max_d(pm);
+    const double M = uni(wave_max_d(pm));
     double pterm = (has && pm != -INFINITY) ? ps * exp_nonpos(pm - M) : 0.0;
-    double S = wave_sum_d(pterm);
+    double S = uni(wave_sum_d(pterm));
 
     // ---- sampling filters: threshold, then the kept mass per slice ----------
     float lcut = -INFINITY;  // q is restricted to logits >= lcut
@@ -937,20 +1004,25 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
         log_tie(a, b, v, 3, a.top_p[b], fmargin);
       double ek = 0.0;
       stream_slice<NG, W, BG2, false>(lrow, -INFINITY, lrow, 0.f, lo, hi,
-          [&](int, float (*xv)[W], float (*)[W]) {
+          [&](int g0, float (*xv)[W], float (*)[W]) {
 #pragma unroll
-            for (int gb = 0; gb < BG2; ++gb)
+            for (int gb = 0; gb < BG2; ++gb) {
+              double sg = 0.0;
 #pragma unroll
               for (int j = 0; j < W; ++j)
-                if (kept(xv[gb][j])) ek += exp_tab(fma((double)xv[gb][j], invT, -M), s_tab);
+                if (kept(xv[gb][j])) sg += exp_tab(fma((double)xv[gb][j], invT, -M), s_tab);
+              ek += sg;
+              scan[g0 + gb][tid] = sg;
+            }
           });
+      scan_rel = false;  // the filter's histograms overwrote scan; it now holds kept sums
       ek = block_sum(ek, red);
       if (!exchange(a, bl, part, gen, ek, 0.0, xs, &s_or)) {
         fail_sync(a, b, writer0);
         return;
       }
       pterm = has ? xs[lane][0] : 0.0;
-      S = wave_sum_d(pterm);
+      S = uni(wave_sum_d(pterm));
     }
     // slice masses of q (in units of S) for the sample when no child is rejected
     if (tid < a.KP) cur_sums[tid] = pterm;
@@ -1013,16 +1085,20 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       int pnf = 0;
       const double CnS = Cn * S;
       stream_slice<NG, W, BG2, true, MAPPED>(lrow, -INFINITY, prow, 0.f, lo, hi,
-          [&](int, float (*xv)[W], float (*pv)[W]) {
+          [&](int g0, float (*xv)[W], float (*pv)[W]) {
 #pragma unroll
-            for (int gb = 0; gb < BG2; ++gb)
+            for (int gb = 0; gb < BG2; ++gb) {
+              double sg = 0.0;
 #pragma unroll
               for (int j = 0; j < W; ++j) {
                 pnf |= !isfinite(pv[gb][j]);
                 const double e =
                     kept(xv[gb][j]) ? exp_tab(fma((double)xv[gb][j], invT, -M), s_tab) : 0.0;
-                zp += fmax(0.0, e - CnS * (double)pv[gb][j]);
+                sg += fmax(0.0, e - CnS * (double)pv[gb][j]);
               }
+              zp += sg;
+              scan[g0 + gb][tid] = sg;
+            }
           }, a.t2d);
       pnf = block_or(pnf, &s_or);
       zp = block_sum(zp, red);
@@ -1031,12 +1107,16 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
         return;
       }
       const bool has = lane < a.KP;
-      const double Zs = wave_sum_d(has ? xs[lane][0] : 0.0);
+      const double Zs = uni(wave_sum_d(has ? xs[lane][0] : 0.0));
       if (__any(has && xs[lane][1] != 0.0)) {
         if (writer0) write_failure(a, b, SPEC_DEVERR_NONFINITE);
         return;
       }
       const double Zn = Zs / S;
+      // scan now holds the sums for coefficient Cn: right for the terminal
+      // sample only if Cn is taken
+      scan_ok = Zn > 0.0;
+      scan_rel = false;
       if (Zn > 0.0) {
         if (writer0 && tid == 0 && Zn < kDegenerate * Z) log_tie(a, b, c, 2, uf, Zn / Z);
         C = Cn;
@@ -1078,78 +1158,109 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       off_sel = off - cur_sums[last_pos];
     }
     int dummy = 0;
-    if (a.final_dist) {
-      float* fd = a.final_dist + (size_t)b * a.V;
-#pragma unroll 1
-      for (int g = 0; g < NG; ++g) {
-        double rv[W];
-        r_group(g, CS, use_p, rv, &dummy);
+    // One streamed pass over r (loads pipelined as in the statistics
+    // passes): final_dist entry by entry, and in the workgroup of the
+    // selected slice each thread's sum of r per group for the ordered scan.
+    const bool is_sel = part == sel;
+    if (a.final_dist || (is_sel && !scan_ok)) {
+      float* fd = a.final_dist ? a.final_dist + (size_t)b * a.V : nullptr;
+      auto body = [&](int g0, float (*xv)[W], float (*pv)[W]) {
 #pragma unroll
-        for (int j = 0; j < W; ++j) {
-          const int i = elem_index<W>(lo, g * W + j);
-          if (i < hi) fd[i] = (float)(rv[j] / Wt);
-        }
-      }
-    }
-    if (part != sel) return;
-
-    // ordered scan of this slice: groups of NT * W entries, then threads,
-    // then the W entries of one thread
-#pragma unroll 1
-    for (int g = 0; g < NG; ++g) {
-      double rv[W];
-      r_group(g, CS, use_p, rv, &dummy);
-      double t = 0.0;
+        for (int gb = 0; gb < BG2; ++gb) {
+          double t = 0.0;
 #pragma unroll
-      for (int j = 0; j < W; ++j) t += rv[j];
-      scan[g][tid] = t;
-    }
-    __syncthreads();
-    if (tid < NG) {
-      double t = 0.0;
-      for (int k = 0; k < NT; ++k) t += scan[tid][k];
-      gtot[tid] = t;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      double run = off_sel;
-      int gs = -1, ts = -1;
-      for (int g = 0; g < NG && gs < 0; ++g) {
-        if (run + gtot[g] > thr) {
-          gs = g;
-          for (int k = 0; k < NT; ++k) {
-            if (run + scan[g][k] > thr) {
-              ts = k;
-              break;
-            }
-            run += scan[g][k];
+          for (int j = 0; j < W; ++j) {
+            const double e =
+                kept(xv[gb][j]) ? exp_tab(fma((double)xv[gb][j], invT, -M), s_tab) : 0.0;
+            const double r = fmax(0.0, e - (use_p ? CS * (double)pv[gb][j] : 0.0));
+            t += r;
+            const int i = elem_index<W>(lo, (g0 + gb) * W + j);
+            if (fd && i < hi) fd[i] = (float)(r / Wt);
           }
-        } else {
-          run += gtot[g];
+          if (g0 + gb < NG) scan[g0 + gb][tid] = t;
         }
-      }
-      s_gsel = gs;
-      s_tsel = ts;
-      s_before = run;
+      };
+      if (use_p)
+        stream_slice<NG, W, BG2, true, MAPPED>(lrow, -INFINITY, prow, 0.f, lo, hi, body, a.t2d);
+      else
+        stream_slice<NG, W, BG2, false>(lrow, -INFINITY, lrow, 0.f, lo, hi, body);
+    }
+    if (!is_sel) return;
+    if (!a.final_dist && scan_ok && scan_rel) {
+      // sums of the statistics pass: relative to each thread's running max
+      for (int g = 0; g < NG; ++g) scan[g][tid] *= exp_tab(mref[g / BG1][tid] - M, s_tab);
+    }
+
+    // Ordered scan of this slice (entries in ascending id: group, then
+    // thread, then a thread's W entries), in parallel: the group holding the
+    // threshold from the group totals (wave sums), then the thread from an
+    // exclusive scan over the threads' sums of that group, then the entry
+    // within the thread.
+    __syncthreads();
+    const int lane_ = tid & 63, wv_ = tid >> 6;
+    // group totals in four parts per group (one per 64 threads), each a
+    // plain running sum over LDS by one thread: short dependent chains
+    // instead of a shuffle reduction per group
+    if (tid < NG * (NT / 64)) {
+      const int g = tid / (NT / 64), k = tid % (NT / 64);
+      double t = 0.0;
+      for (int i = 0; i < 64; ++i) t += scan[g][k * 64 + i];
+      gsum_w[g][k] = t;
+    }
+    if (tid == 0) {
+      s_first = 0x7fffffff;
       s_hit = -1;
     }
     __syncthreads();
+    double run = off_sel;
+    int gs = -1;
+    for (int g = 0; g < NG; ++g) {
+      double gt = 0.0;
+#pragma unroll
+      for (int k = 0; k < NT / 64; ++k) gt += gsum_w[g][k];
+      if (gs < 0) {
+        if (run + gt > thr) gs = g;
+        else run += gt;
+      }
+    }
+    const double tsel = gs >= 0 ? scan[gs][tid] : 0.0;
+    double incl = tsel;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double y = __shfl_up(incl, o);
+      if (lane_ >= o) incl += y;
+    }
+    double excl = __shfl_up(incl, 1);
+    if (lane_ == 0) excl = 0.0;
+    if (lane_ == 63) wtot[wv_] = incl;
+    __syncthreads();
+    double woff = 0.0;
+    for (int k = 0; k < wv_; ++k) woff += wtot[k];
+    const double start = run + (woff + excl);
+    if (gs >= 0 && tsel > 0.0 && start + tsel > thr) atomicMin(&s_first, tid);
+    __syncthreads();
     double margin = 0.0;
-    if (tid == s_tsel && s_gsel >= 0) {
-      const int g = s_gsel;
+    if (gs >= 0 && tid == s_first) {
       double rv[W];
-      r_group(g, CS, use_p, rv, &dummy);
-      double run = s_before;
-      int tok = -1;
+      r_group(gs, CS, use_p, rv, &dummy);
+      double cum = start;
+      int tok = -1, lastp = -1;
 #pragma unroll
       for (int j = 0; j < W; ++j) {
-        if (tok < 0 && run + rv[j] > thr) {
-          tok = elem_index<W>(lo, g * W + j);
-          margin = fmin(thr - run, run + rv[j] - thr) / Wt;
+        if (rv[j] > 0.0) {
+          lastp = elem_index<W>(lo, gs * W + j);
+          if (tok < 0 && cum + rv[j] > thr) {
+            tok = lastp;
+            margin = fmin(thr - cum, cum + rv[j] - thr) / Wt;
+          }
         }
-        run += rv[j];
+        cum += rv[j];
       }
-      if (tok >= 0) s_hit = tok;
+      if (tok < 0) {  // rounding: the thread's own running sum stayed below
+        tok = lastp;
+        margin = 0.0;
+      }
+      s_hit = tok;
     }
     __syncthreads();
     if (s_hit < 0) {
@@ -1166,7 +1277,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       if (lastpos >= 0) atomicMax(&s_hit, lastpos);
       __syncthreads();
       if (tid == 0) log_tie(a, b, v, 1, usf, 0.0);
-    } else if (tid == s_tsel && margin < kSampleBand) {
+    } else if (tid == s_first && margin < kSampleBand) {
       log_tie(a, b, v, 1, usf, margin);
     }
     __syncthreads();
