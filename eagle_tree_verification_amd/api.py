@@ -56,6 +56,9 @@ def load():
     lib.spec_accept_tree.argtypes = [P, P, P, P, P, I, I, I, I, F, P, P, P, P, P, P, P, P, I, P,
                                      P, Z, P, P]
     lib.spec_accept_tree.restype = I
+    lib.spec_accept_tree_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, F, P, P, P, P, P, P, P,
+                                             P, I, P, P, P]
+    lib.spec_accept_tree_noalloc.restype = I
     lib.spec_accept_tree_workspace_size.argtypes = [I, I, I]
     lib.spec_accept_tree_workspace_size.restype = Z
     lib.spec_accept_tree_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, P, P, P, P, I, P, P, P, P,
@@ -212,7 +215,7 @@ def tree_kv_write(k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, parents, 
 def accept_tree(tokens, parents, n_nodes, draft_p, logits, temperature, u_accept, u_sample,
                 max_depth, *, final_dist=False, tie_cap=0, workspace=None, dev_error=None,
                 outputs=None, stream=None, temperatures=None, d2t=None, top_k=None,
-                top_p=None):
+                top_p=None, noalloc=False):
     """Acceptance walk; returns a dict of device tensors.
 
     Keys: accept_len [B], path [B][max_depth+1], out_tokens [B][max_depth+1],
@@ -222,7 +225,9 @@ def accept_tree(tokens, parents, n_nodes, draft_p, logits, temperature, u_accept
     temperatures ([B] float32 device tensor) gives each sequence its own
     temperature; d2t ([Vd] int32 device tensor) means draft_p rows hold the
     draft vocabulary's Vd entries; top_k ([B] int32) and top_p ([B] float32)
-    are per-sequence sampling filters on q (spec_accept_tree_ex).
+    are per-sequence sampling filters on q (spec_accept_tree_ex).  noalloc
+    calls spec_accept_tree_noalloc, whose exchange words live in the
+    library's fixed device array instead of a workspace.
     """
     lib = load()
     B, n_max, V = logits.shape
@@ -251,6 +256,16 @@ def accept_tree(tokens, parents, n_nodes, draft_p, logits, temperature, u_accept
     fd = torch.empty((B, V), dtype=torch.float32, device=dev) if final_dist else None
     tlog = torch.zeros(max(tie_cap, 1) * TIE_DTYPE.itemsize, dtype=torch.uint8, device=dev) if tie_cap else None
     tcount = torch.zeros(1, dtype=torch.int32, device=dev) if tie_cap else None
+    if noalloc:
+        st = lib.spec_accept_tree_noalloc(_ptr(tokens), _ptr(parents), _ptr(n_nodes),
+                                          _ptr(draft_p), _ptr(logits), B, n_max, V, int(max_depth),
+                                          float(temperature), _ptr(u_accept), _ptr(u_sample),
+                                          _ptr(acc), _ptr(path), _ptr(toks), _ptr(nout), _ptr(fd),
+                                          _ptr(tlog), int(tie_cap), _ptr(tcount), _ptr(dev_error),
+                                          _stream(stream))
+        _check("spec_accept_tree_noalloc", st)
+        return {"accept_len": acc, "path": path, "out_tokens": toks, "n_out": nout,
+                "final_dist": fd, "tie_log": tlog, "tie_count": tcount}
     ws, wsb = _workspace(accept_tree_workspace_size(B, n_max, V), dev, workspace)
     st = lib.spec_accept_tree(_ptr(tokens), _ptr(parents), _ptr(n_nodes), _ptr(draft_p),
                               _ptr(logits), B, n_max, V, int(max_depth), float(temperature),

@@ -34,6 +34,8 @@ extern "C" const char* spec_status_string(spec_status_t s) {
     case SPEC_E_WORKSPACE: return "workspace NULL or smaller than required";
     case SPEC_E_HIP: return "a HIP runtime call or kernel launch failed";
     case SPEC_E_UNSUPPORTED: return "configuration not supported on the current device";
+    case SPEC_E_SCRATCH:
+      return "the call needs more device scratch than the library's fixed array holds";
     default: return "unknown status";
   }
 }

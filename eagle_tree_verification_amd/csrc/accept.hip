@@ -1582,3 +1582,60 @@ extern "C" spec_status_t spec_accept_tree(
                              u_sample, accept_len, path, out_tokens, n_out, final_dist, tie_log,
                              tie_cap, tie_count, workspace, workspace_bytes, dev_error, stream);
 }
+
+// ---- the allocation-free form ------------------------------------------------
+namespace specv {
+namespace {
+
+// Scratch of spec_accept_tree_noalloc: the exchange words of one call, in a
+// fixed array of the code object (one copy per GPU, zero at load, held until
+// the process ends).  Host code must not pass `scratch` itself to a kernel:
+// its host-side name is not the device address, which noalloc_scratch()
+// looks up per device.
+__device__ __align__(256) uint8_t scratch[SPEC_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+// The device address of the current GPU's copy of `scratch`, looked up with
+// hipGetSymbolAddress on the first call with that GPU current and kept.
+spec_status_t noalloc_scratch(void** addr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPEC_E_HIP;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return SPEC_E_HIP;
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *addr = p;
+  return SPEC_OK;
+}
+
+}  // namespace
+}  // namespace specv
+
+extern "C" spec_status_t spec_accept_tree_noalloc(
+    const int32_t* tokens, const int32_t* parents, const int32_t* n_nodes, const float* draft_p,
+    const float* logits, int32_t B, int32_t n_max, int32_t V, int32_t max_depth,
+    float temperature, const float* u_accept, const float* u_sample, int32_t* accept_len,
+    int32_t* path, int32_t* out_tokens, int32_t* n_out, float* final_dist, spec_tie_t* tie_log,
+    int32_t tie_cap, int32_t* tie_count, int32_t* dev_error, void* stream) {
+  // the argument checks of spec_accept_tree come first, so that a bad
+  // argument reports the same status as there, without touching a device
+  if (!tokens || !parents || !n_nodes || !draft_p || !logits || !u_accept || !u_sample ||
+      !accept_len || !path || !out_tokens || !n_out || (tie_log && !tie_count))
+    return SPEC_E_NULL;
+  if (B <= 0 || n_max <= 0 || n_max > SPEC_MAX_NODES || V <= 0 || max_depth < 0 ||
+      max_depth >= SPEC_MAX_NODES || (tie_log && tie_cap < 0))
+    return SPEC_E_SHAPE;
+  if (!(temperature >= 0.f) || !isfinite(temperature)) return SPEC_E_VALUE;
+  if (make_accept_plan(B, V).ws > SPEC_NOALLOC_SCRATCH_BYTES) return SPEC_E_SCRATCH;
+  void* ws = nullptr;
+  const spec_status_t st = noalloc_scratch(&ws);
+  if (st != SPEC_OK) return st;
+  return spec_accept_tree_ex(tokens, parents, n_nodes, draft_p, logits, B, n_max, V, max_depth,
+                             temperature, nullptr, nullptr, nullptr, nullptr, 0, u_accept,
+                             u_sample, accept_len, path, out_tokens, n_out, final_dist, tie_log,
+                             tie_cap, tie_count, ws, SPEC_NOALLOC_SCRATCH_BYTES, dev_error, stream);
+}

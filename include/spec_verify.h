@@ -73,7 +73,9 @@ enum {
   SPEC_E_WORKSPACE = -5,   /* workspace NULL, smaller than required, or (where it
                               must be) not 16-byte aligned                        */
   SPEC_E_HIP = -6,         /* a HIP runtime call or launch failed                 */
-  SPEC_E_UNSUPPORTED = -7  /* the current device cannot run this configuration    */
+  SPEC_E_UNSUPPORTED = -7, /* the current device cannot run this configuration    */
+  SPEC_E_SCRATCH = -8      /* the call needs more device scratch than the
+                              library's fixed array holds (spec_accept_tree_noalloc) */
 };
 
 enum { SPEC_F32 = 0, SPEC_BF16 = 1 };
@@ -255,6 +257,37 @@ spec_status_t spec_accept_tree(
     void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream);
 
 size_t spec_accept_tree_workspace_size(int32_t B, int32_t n_max, int32_t V);
+
+/*
+ * spec_accept_tree_noalloc -- spec_accept_tree without a workspace argument,
+ * for callers that cannot allocate device memory around the call: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, outputs, arithmetic and device errors as
+ * spec_accept_tree (the same kernels; outputs are bit-identical), minus
+ * workspace / workspace_bytes.
+ *
+ * The words the workgroups exchange live in a fixed device array of the
+ * library, SPEC_NOALLOC_SCRATCH_BYTES (1 MiB) per GPU, created with the
+ * library's code object on each GPU it runs on and held until the process
+ * ends; the call never allocates or frees memory (no hipMalloc, hipFree or
+ * allocating library routine).  The array's device address is looked up once
+ * per GPU, on the first call with that GPU current.  A batch needing more
+ * than the array (spec_accept_tree_workspace_size(B, n_max, V) > 1 MiB, about
+ * 1,000 sequences of a 128k vocabulary) returns SPEC_E_SCRATCH before any
+ * launch.  The array keeps what the last call left in it; nothing in it needs
+ * clearing (each exchange word carries its launch's tag).  Every call on one
+ * GPU shares the array: calls that may overlap on one GPU (different streams
+ * without ordering between them) race and must not be issued.
+ */
+#define SPEC_NOALLOC_SCRATCH_BYTES (1u << 20)
+spec_status_t spec_accept_tree_noalloc(
+    const int32_t* tokens, const int32_t* parents, const int32_t* n_nodes,
+    const float* draft_p, const float* logits,
+    int32_t B, int32_t n_max, int32_t V, int32_t max_depth, float temperature,
+    const float* u_accept, const float* u_sample,
+    int32_t* accept_len, int32_t* path, int32_t* out_tokens, int32_t* n_out,
+    float* final_dist, spec_tie_t* tie_log, int32_t tie_cap, int32_t* tie_count,
+    int32_t* dev_error, void* stream);
 
 /*
  * spec_accept_tree_ex -- spec_accept_tree with variants of its inputs

@@ -8,6 +8,7 @@ import pytest
 from eagle_tree_verification_amd import api
 
 SPEC_E_NULL, SPEC_E_SHAPE, SPEC_E_DTYPE, SPEC_E_VALUE, SPEC_E_WORKSPACE = -1, -2, -3, -4, -5
+SPEC_E_SCRATCH = -8
 
 
 @pytest.fixture(scope="module")
@@ -24,14 +25,14 @@ def test_every_declared_symbol_is_exported(lib):
                           "spec_verify_tree_attn_rope", "spec_tree_kv_write",
                           "spec_accept_tree_ex", "spec_accept_tree_ex_workspace_size",
                           "spec_verify_tree_attn_paged", "spec_tree_kv_write_paged",
-                          "spec_kv_commit_layers_paged"}
+                          "spec_kv_commit_layers_paged", "spec_accept_tree_noalloc"}
     for nm in names:
         assert hasattr(lib, nm), nm
 
 
 def test_version_and_status_strings(lib):
     assert lib.spec_abi_version() == 1
-    for s in range(-7, 1):
+    for s in range(-8, 1):
         assert len(lib.spec_status_string(s)) > 0
     assert lib.spec_status_string(-99) == b"unknown status"
 
@@ -133,6 +134,27 @@ def test_accept_host_checks(lib):
     assert f(*bad) == SPEC_E_VALUE
     bad = list(args); bad[17] = P          # tie_log without tie_count
     assert f(*bad) == SPEC_E_NULL
+
+
+def test_accept_noalloc_host_checks(lib):
+    """The allocation-free form checks its arguments as spec_accept_tree does
+    and refuses a batch beyond its fixed scratch array before any device call."""
+    P = _buf()
+    f = lib.spec_accept_tree_noalloc
+    args = [P] * 5 + [2, 6, 100, 5, 1.0, P, P, P, P, P, P, None, None, 0, None, None, None]
+    assert f(*([None] + args[1:])) == SPEC_E_NULL
+    bad = list(args); bad[6] = 65
+    assert f(*bad) == SPEC_E_SHAPE
+    bad = list(args); bad[9] = float("nan")
+    assert f(*bad) == SPEC_E_VALUE
+    bad = list(args); bad[17] = P          # tie_log without tie_count
+    assert f(*bad) == SPEC_E_NULL
+    # 8,192 sequences of a 128k vocabulary need several exchange words each,
+    # far beyond the 1 MiB array
+    big = list(args); big[5] = 8192; big[7] = 128256
+    assert lib.spec_accept_tree_workspace_size(8192, 6, 128256) > (1 << 20)
+    assert f(*big) == SPEC_E_SCRATCH
+    assert lib.spec_status_string(SPEC_E_SCRATCH).startswith(b"the call needs more device scratch")
 
 
 def test_commit_host_checks(lib):
