@@ -18,7 +18,9 @@ LIB_PATH = os.path.join(HERE, "libspecverify.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "spec_verify.h")
 
 SPEC_F32, SPEC_BF16 = 0, 1
+LAUNCH = {"ordinary": 0, "cooperative": 1}  # SPEC_LAUNCH_ORDINARY, SPEC_LAUNCH_COOPERATIVE
 DEVERR_TREE, DEVERR_TOKEN, DEVERR_NONFINITE, DEVERR_CAPACITY, DEVERR_SYNC = 1, 2, 4, 8, 16
+DEVERR_ALIGN = 32
 TIE_DTYPE = np.dtype([("b", "<i4"), ("node", "<i4"), ("kind", "<i4"), ("u", "<f4"),
                       ("margin", "<f8")])
 
@@ -62,7 +64,7 @@ def load():
     lib.spec_accept_tree_workspace_size.argtypes = [I, I, I]
     lib.spec_accept_tree_workspace_size.restype = Z
     lib.spec_accept_tree_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, P, P, P, P, I, P, P, P, P,
-                                        P, P, P, P, I, P, P, Z, P, P]
+                                        P, P, P, P, I, P, P, Z, I, P, P]
     lib.spec_accept_tree_ex.restype = I
     lib.spec_accept_tree_ex_workspace_size.argtypes = [I, I, I, I, I]
     lib.spec_accept_tree_ex_workspace_size.restype = Z
@@ -215,7 +217,7 @@ def tree_kv_write(k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, parents, 
 def accept_tree(tokens, parents, n_nodes, draft_p, logits, temperature, u_accept, u_sample,
                 max_depth, *, final_dist=False, tie_cap=0, workspace=None, dev_error=None,
                 outputs=None, stream=None, temperatures=None, d2t=None, top_k=None,
-                top_p=None, noalloc=False):
+                top_p=None, noalloc=False, launch="ordinary"):
     """Acceptance walk; returns a dict of device tensors.
 
     Keys: accept_len [B], path [B][max_depth+1], out_tokens [B][max_depth+1],
@@ -227,16 +229,24 @@ def accept_tree(tokens, parents, n_nodes, draft_p, logits, temperature, u_accept
     draft vocabulary's Vd entries; top_k ([B] int32) and top_p ([B] float32)
     are per-sequence sampling filters on q (spec_accept_tree_ex).  noalloc
     calls spec_accept_tree_noalloc, whose exchange words live in the
-    library's fixed device array instead of a workspace.
+    library's fixed device array instead of a workspace.  launch is
+    "ordinary" or "cooperative" (spec_accept_tree_ex's launch argument; the
+    cooperative launch has the runtime guarantee that a sequence's
+    workgroups are resident together).
     """
     lib = load()
     B, n_max, V = logits.shape
     Vd = 0 if d2t is None else int(d2t.numel())
-    if temperatures is not None or d2t is not None or top_k is not None or top_p is not None:
+    if launch not in LAUNCH:
+        raise ValueError(f"launch must be one of {sorted(LAUNCH)}")
+    if (temperatures is not None or d2t is not None or top_k is not None or top_p is not None
+            or launch != "ordinary"):
+        if noalloc:
+            raise ValueError("noalloc takes none of temperatures, d2t, top_k, top_p, launch")
         return _accept_tree_ex(lib, tokens, parents, n_nodes, draft_p, logits, temperature,
                                u_accept, u_sample, max_depth, final_dist, tie_cap, workspace,
                                dev_error, outputs, stream, temperatures, d2t, top_k, top_p, B,
-                               n_max, V, Vd)
+                               n_max, V, Vd, LAUNCH[launch])
     dev = logits.device
     for t, nm in ((tokens, "tokens"), (parents, "parents"), (n_nodes, "n_nodes")):
         _dev(t, nm, torch.int32)
@@ -283,7 +293,7 @@ def accept_tree_ex_workspace_size(B, n_max, V, Vd, filters=False):
 
 def _accept_tree_ex(lib, tokens, parents, n_nodes, draft_p, logits, temperature, u_accept,
                     u_sample, max_depth, final_dist, tie_cap, workspace, dev_error, outputs,
-                    stream, temperatures, d2t, top_k, top_p, B, n_max, V, Vd):
+                    stream, temperatures, d2t, top_k, top_p, B, n_max, V, Vd, launch):
     dev = logits.device
     for t, nm in ((tokens, "tokens"), (parents, "parents"), (n_nodes, "n_nodes")):
         _dev(t, nm, torch.int32)
@@ -321,7 +331,7 @@ def _accept_tree_ex(lib, tokens, parents, n_nodes, draft_p, logits, temperature,
                                  _ptr(u_accept),
                                  _ptr(u_sample), _ptr(acc), _ptr(path), _ptr(toks), _ptr(nout),
                                  _ptr(fd), _ptr(tlog), int(tie_cap), _ptr(tcount), _ptr(ws), wsb,
-                                 _ptr(dev_error), _stream(stream))
+                                 int(launch), _ptr(dev_error), _stream(stream))
     _check("spec_accept_tree_ex", st)
     return {"accept_len": acc, "path": path, "out_tokens": toks, "n_out": nout,
             "final_dist": fd, "tie_log": tlog, "tie_count": tcount}

@@ -64,6 +64,9 @@ namespace {
 constexpr int NT = 256;   // threads per workgroup
 constexpr double kTieBand = 1e-6;
 constexpr double kSampleBand = 1e-9;
+// top-p boundaries: the masses are fixed point of 2^-47 per entry, so their
+// truncation error stays below V * 2^-47, under 1e-9 for a 128k vocabulary
+constexpr double kFilterBand = 1e-8;
 constexpr double kDegenerate = 1e-12;
 
 // exp(y) for y <= 0 in float64: y = n ln2 + r with |r| <= ln2 / 2 (ln2 split
@@ -645,7 +648,7 @@ __device__ bool filter_threshold(const AcceptArgs& a, int bl, int part, int& gen
   const int cp = lane % kCopies;
   const bool use_k = fk > 0, use_p = P > 0;
   const double fscale = kMassOne / S;
-  const uint64_t band = (uint64_t)(kTieBand * kMassOne);
+  const uint64_t band = (uint64_t)(kFilterBand * kMassOne);
   uint32_t prefix = 0;
   uint64_t above_c = 0, above_m = 0;
   margin = 1.0;
@@ -1000,7 +1003,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
         fail_sync(a, b, writer0);
         return;
       }
-      if (writer0 && tid == 0 && fmargin < kTieBand)
+      if (writer0 && tid == 0 && fmargin < kFilterBand)
         log_tie(a, b, v, 3, a.top_p[b], fmargin);
       double ek = 0.0;
       stream_slice<NG, W, BG2, false>(lrow, -INFINITY, lrow, 0.f, lo, hi,
@@ -1467,10 +1470,11 @@ extern "C" spec_status_t spec_accept_tree_ex(
     const int32_t* d2t, int32_t Vd, const float* u_accept, const float* u_sample,
     int32_t* accept_len, int32_t* path, int32_t* out_tokens, int32_t* n_out, float* final_dist,
     spec_tie_t* tie_log, int32_t tie_cap, int32_t* tie_count, void* workspace,
-    size_t workspace_bytes, int32_t* dev_error, void* stream) {
+    size_t workspace_bytes, int32_t launch, int32_t* dev_error, void* stream) {
   if (!tokens || !parents || !n_nodes || !draft_p || !logits || !u_accept || !u_sample ||
       !accept_len || !path || !out_tokens || !n_out)
     return SPEC_E_NULL;
+  if (launch != SPEC_LAUNCH_ORDINARY && launch != SPEC_LAUNCH_COOPERATIVE) return SPEC_E_VALUE;
   const bool mapped = d2t != nullptr;
   if (mapped && (Vd <= 0 || Vd > V)) return SPEC_E_SHAPE;
   if (tie_log && !tie_count) return SPEC_E_NULL;
@@ -1512,8 +1516,7 @@ extern "C" spec_status_t spec_accept_tree_ex(
   a.spin_limit = 1 << 22;
   if (const char* env = getenv("SPEC_ACCEPT_SPIN_LIMIT")) a.spin_limit = atoi(env);
   const accept_fn fn = pick_kernel(p.W, p.NG, mapped, filters);
-  const char* coop_env = getenv("SPEC_ACCEPT_COOPERATIVE");
-  const bool cooperative = coop_env && coop_env[0] == '1';
+  const bool cooperative = launch == SPEC_LAUNCH_COOPERATIVE;
 
   // Sequences per launch: all of them, unless the KP > 1 workgroups of every
   // sequence cannot be resident together (their exchanges need that).
@@ -1554,9 +1557,9 @@ extern "C" spec_status_t spec_accept_tree_ex(
       SPEC_HIP_TRY(hipGetLastError());
     } else {
       // The plan keeps every workgroup of the launch resident at once on an
-      // otherwise idle GPU, so an ordinary launch is used (a cooperative one
-      // costs about 17 us more per call); SPEC_ACCEPT_COOPERATIVE=1 asks the
-      // runtime to guarantee residency where the GPU is shared.
+      // otherwise idle GPU, so the ordinary launch suffices there (a
+      // cooperative one costs about 17 us more per call); the cooperative
+      // launch has the runtime guarantee residency where the GPU is shared.
       if (cooperative) {
         void* args[] = {&a};
         SPEC_HIP_TRY(hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(grid),
@@ -1580,7 +1583,8 @@ extern "C" spec_status_t spec_accept_tree(
   return spec_accept_tree_ex(tokens, parents, n_nodes, draft_p, logits, B, n_max, V, max_depth,
                              temperature, nullptr, nullptr, nullptr, nullptr, 0, u_accept,
                              u_sample, accept_len, path, out_tokens, n_out, final_dist, tie_log,
-                             tie_cap, tie_count, workspace, workspace_bytes, dev_error, stream);
+                             tie_cap, tie_count, workspace, workspace_bytes, SPEC_LAUNCH_ORDINARY,
+                             dev_error, stream);
 }
 
 // ---- the allocation-free form ------------------------------------------------
@@ -1637,5 +1641,6 @@ extern "C" spec_status_t spec_accept_tree_noalloc(
   return spec_accept_tree_ex(tokens, parents, n_nodes, draft_p, logits, B, n_max, V, max_depth,
                              temperature, nullptr, nullptr, nullptr, nullptr, 0, u_accept,
                              u_sample, accept_len, path, out_tokens, n_out, final_dist, tie_log,
-                             tie_cap, tie_count, ws, SPEC_NOALLOC_SCRATCH_BYTES, dev_error, stream);
+                             tie_cap, tie_count, ws, SPEC_NOALLOC_SCRATCH_BYTES,
+                             SPEC_LAUNCH_ORDINARY, dev_error, stream);
 }

@@ -132,6 +132,22 @@ __global__ __launch_bounds__(NT) void commit_kernel(uint4* kc, uint4* vc, int32_
   if (threadIdx.x == 0) prefix_len[b] = L + a + 1;
 }
 
+// Whether any layer buffer of the call (cache, and scratch rows when given)
+// is off the 16-byte alignment the chunked moves need.  The pointer arrays
+// live on the device, so every workgroup checks all layers: then either every
+// layer is committed or none is.  Called by every thread of the workgroup.
+__device__ bool layers_misaligned(const uint4* const* kl, const uint4* const* vl,
+                                  const uint4* const* kt, const uint4* const* vt,
+                                  int num_layers) {
+  uintptr_t bits = 0;
+  for (int l = threadIdx.x; l < num_layers; l += blockDim.x) {
+    bits |= reinterpret_cast<uintptr_t>(kl[l]) | reinterpret_cast<uintptr_t>(vl[l]);
+    if (kt != nullptr)
+      bits |= reinterpret_cast<uintptr_t>(kt[l]) | reinterpret_cast<uintptr_t>(vt[l]);
+  }
+  return __syncthreads_or((bits & 15) != 0);
+}
+
 // One workgroup per (sequence, layer): the in-place gather, or the gather
 // from the layer's scratch rows (kt != nullptr).  Only the layer-0 workgroup
 // reports a failed sequence; the length kernel skips it.
@@ -146,6 +162,10 @@ __global__ __launch_bounds__(NTL) void commit_layers_kernel(
   const int a = accept_len[b];
   const int L = prefix_len[b];
   if (a < 0) return;
+  if (layers_misaligned(kl, vl, kt, vt, (int)gridDim.y)) {
+    if (layer == 0 && threadIdx.x == 0) report(dev_error, SPEC_DEVERR_ALIGN);
+    return;
+  }
   const bool scratch = (kt != nullptr);
   const int err = load_path(path, b, a, L, kv, max_depth, scratch ? n_rows : 0, s_path, &s_moves);
   if (err) {
@@ -176,16 +196,17 @@ __global__ __launch_bounds__(NTL) void commit_layers_kernel(
 }
 
 // Advances the length of every sequence the copy kernel committed.
-__global__ __launch_bounds__(64) void commit_length_kernel(int32_t* prefix_len,
-                                                           const int32_t* path,
-                                                           const int32_t* accept_len, KvRows kv,
-                                                           int n_rows, int max_depth) {
+__global__ __launch_bounds__(64) void commit_length_kernel(
+    int32_t* prefix_len, const int32_t* path, const int32_t* accept_len, KvRows kv, int n_rows,
+    int max_depth, const uint4* const* kl, const uint4* const* vl, const uint4* const* kt,
+    const uint4* const* vt, int num_layers) {
   __shared__ int s_path[SPEC_MAX_NODES + 1];
   __shared__ int s_moves;
   const int b = blockIdx.x;
   const int a = accept_len[b];
   const int L = prefix_len[b];
   if (a < 0) return;
+  if (layers_misaligned(kl, vl, kt, vt, num_layers)) return;
   if (load_path(path, b, a, L, kv, max_depth, n_rows, s_path, &s_moves)) return;
   if (threadIdx.x == 0) prefix_len[b] = L + a + 1;
 }
@@ -214,6 +235,9 @@ extern "C" spec_status_t spec_kv_commit(void* k_cache, void* v_cache, int32_t* p
   if (!k_cache || !v_cache || !prefix_len || !path || !accept_len) return SPEC_E_NULL;
   const spec_status_t st = check_commit_shape(B, Hkv, head_dim, L_cap, max_depth, dtype);
   if (st != SPEC_OK) return st;
+  // rows move in 16-byte chunks
+  if (((reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) & 15) != 0)
+    return SPEC_E_SHAPE;
   const int esz = dtype == SPEC_F32 ? 4 : 2;
   const int row_chunks = head_dim * esz / 16;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
@@ -253,7 +277,11 @@ spec_status_t launch_commit_layers(void* const* k_layers, void* const* v_layers,
                      Hkv, row_chunks, kv, n_rows, max_depth, dev_error);
   SPEC_HIP_TRY(hipGetLastError());
   hipLaunchKernelGGL(commit_length_kernel, dim3(B), dim3(64), 0, strm, prefix_len, path,
-                     accept_len, kv, n_rows, max_depth);
+                     accept_len, kv, n_rows, max_depth,
+                     reinterpret_cast<const uint4* const*>(k_layers),
+                     reinterpret_cast<const uint4* const*>(v_layers),
+                     reinterpret_cast<const uint4* const*>(k_tree),
+                     reinterpret_cast<const uint4* const*>(v_tree), num_layers);
   SPEC_HIP_TRY(hipGetLastError());
   return SPEC_OK;
 }

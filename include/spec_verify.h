@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define SPEC_ABI_VERSION 1
+#define SPEC_ABI_VERSION 2
 #define SPEC_MAX_NODES 64
 #define SPEC_TREE_MAX_TOP_K 16  /* children per expanded node (tree construction) */
 #define SPEC_TREE_MAX_DEPTH 16  /* levels of a constructed tree                   */
@@ -80,19 +80,24 @@ enum {
 
 enum { SPEC_F32 = 0, SPEC_BF16 = 1 };
 
+/* How spec_accept_tree_ex launches the walk (its `launch` argument). */
+enum { SPEC_LAUNCH_ORDINARY = 0, SPEC_LAUNCH_COOPERATIVE = 1 };
+
 enum {
   SPEC_DEVERR_TREE = 1,       /* n_nodes outside [1, n_max], bad parents, depth > max_depth */
   SPEC_DEVERR_TOKEN = 2,      /* a draft token outside [0, V)                              */
   SPEC_DEVERR_NONFINITE = 4,  /* NaN/Inf in a logits or draft-probability entry read       */
   SPEC_DEVERR_CAPACITY = 8,   /* prefix_len < 0 or prefix_len + n_nodes > L_cap            */
-  SPEC_DEVERR_SYNC = 16       /* an inter-workgroup wait hit its bound (walk abandoned;
+  SPEC_DEVERR_SYNC = 16,      /* an inter-workgroup wait hit its bound (walk abandoned;
                                  spec_accept_tree outputs of the batch unspecified)        */
+  SPEC_DEVERR_ALIGN = 32      /* a per-layer buffer of spec_kv_commit_layers(_paged) off
+                                 16-byte alignment (nothing of the call committed)         */
 };
 
 /* One near-tie record of spec_accept_tree (kind 0: accept test, 1: sample,
  * 2: residual whose mass fell below 1e-12 of the previous one, so rounding
  * may decide whether it is zero, 3: top-p boundary of spec_accept_tree_ex
- * within 1e-6 of a kept or dropped token's mass above). */
+ * within 1e-8 of a kept or dropped token's mass above). */
 typedef struct {
   int32_t b;      /* sequence                                             */
   int32_t node;   /* child tested (kinds 0, 2) or node visited (1, 3)     */
@@ -241,11 +246,16 @@ spec_status_t spec_tree_kv_write(const void* k_new, const void* v_new, void* k_c
  * Device errors: SPEC_DEVERR_TREE, _TOKEN, _NONFINITE, _SYNC.
  * The workgroups that share one sequence's vocabulary exchange partial sums
  * and must be resident together; the call sizes its launch so that they are
- * on an otherwise idle GPU and uses an ordinary launch.  Where other work may
- * hold the GPU's compute units, set SPEC_ACCEPT_COOPERATIVE=1 in the
- * environment to have the runtime guarantee residency (a cooperative launch,
- * slower to start).  Either way every wait is bounded: a walk that cannot
- * complete sets SPEC_DEVERR_SYNC instead of hanging.
+ * on an otherwise idle GPU and uses an ordinary launch (spec_accept_tree_ex
+ * takes the launch mode as an argument).  Every wait is bounded: a walk whose
+ * workgroups could not all be resident sets SPEC_DEVERR_SYNC instead of
+ * hanging, and then every output of the call (all B sequences) is
+ * unspecified.  The caller then discards them (they must not reach
+ * spec_kv_commit), zeroes *dev_error and repeats the call on the same inputs,
+ * which it has not changed, with launch = SPEC_LAUNCH_COOPERATIVE, where the
+ * runtime guarantees residency.  A caller that shares the GPU with other
+ * work can pass SPEC_LAUNCH_COOPERATIVE from the start (about 17 us more per
+ * call).
  */
 spec_status_t spec_accept_tree(
     const int32_t* tokens, const int32_t* parents, const int32_t* n_nodes,
@@ -311,7 +321,7 @@ spec_status_t spec_accept_tree_noalloc(
  *                 the acceptance tests, residuals and samples.  k <= 0 or
  *                 k >= V, and p <= 0 or p >= 1, turn a filter off for that
  *                 sequence; a NaN p fails it with SPEC_DEVERR_NONFINITE.
- *                 Boundaries within 1e-6 of p are logged (tie kind 3).
+ *                 Boundaries within 1e-8 of p are logged (tie kind 3).
  *   d2t, Vd       NULL (draft_p rows hold V entries), or [Vd] int32 device
  *                 array with 1 <= Vd <= V: draft_p rows hold Vd entries over
  *                 the draft vocabulary, and the draft probability of target
@@ -324,7 +334,15 @@ spec_status_t spec_accept_tree_noalloc(
  *                 top_k or top_p is given); with d2t it also holds the
  *                 inverse map, which the call builds first, and with filters
  *                 the per-round histograms the workgroups exchange
- * Everything else as spec_accept_tree, which is this call with all four NULL.
+ *   launch        SPEC_LAUNCH_ORDINARY: an ordinary launch, sized so that
+ *                 all workgroups of a sequence are resident on an otherwise
+ *                 idle GPU; SPEC_LAUNCH_COOPERATIVE: a cooperative launch,
+ *                 for which the runtime guarantees residency (for a GPU
+ *                 shared with other work, and the repeat after
+ *                 SPEC_DEVERR_SYNC).  The outputs are the same bits either
+ *                 way.  Any other value returns SPEC_E_VALUE.
+ * Everything else as spec_accept_tree, which is this call with all four NULL
+ * and launch = SPEC_LAUNCH_ORDINARY.
  */
 spec_status_t spec_accept_tree_ex(
     const int32_t* tokens, const int32_t* parents, const int32_t* n_nodes,
@@ -335,7 +353,8 @@ spec_status_t spec_accept_tree_ex(
     const float* u_accept, const float* u_sample,
     int32_t* accept_len, int32_t* path, int32_t* out_tokens, int32_t* n_out,
     float* final_dist, spec_tie_t* tie_log, int32_t tie_cap, int32_t* tie_count,
-    void* workspace, size_t workspace_bytes, int32_t* dev_error, void* stream);
+    void* workspace, size_t workspace_bytes, int32_t launch, int32_t* dev_error,
+    void* stream);
 
 size_t spec_accept_tree_ex_workspace_size(int32_t B, int32_t n_max, int32_t V, int32_t Vd,
                                           int32_t filters);
@@ -350,7 +369,8 @@ size_t spec_accept_tree_ex_workspace_size(int32_t B, int32_t n_max, int32_t V, i
  * bytes (logical truncation).  Sequences with accept_len < 0 are untouched.
  * Not idempotent: call exactly once per step, after spec_accept_tree.
  *
- *   k_cache, v_cache [B][Hkv][L_cap][head_dim], dtype (in/out)
+ *   k_cache, v_cache [B][Hkv][L_cap][head_dim], dtype (in/out); 16-byte
+ *                    aligned (rows move in 16-byte chunks), else SPEC_E_SHAPE
  *   prefix_len       [B] int32 (in/out)
  *   path, accept_len as written by spec_accept_tree with the same max_depth
  * Device errors: SPEC_DEVERR_TREE (path not increasing / out of range),
@@ -387,10 +407,13 @@ spec_status_t spec_kv_commit(
  *   prefix_len, path, accept_len, B, Hkv, head_dim, L_cap, max_depth, dtype
  *                       as for spec_kv_commit
  * The pointer arrays are read by the kernels: they must stay valid until the
- * stream work completes.
+ * stream work completes.  Every pointer in them must be 16-byte aligned, as
+ * for spec_kv_commit; the host cannot read device arrays, so the kernels
+ * check: if any is not, no sequence of any layer is committed, no length
+ * advances, and SPEC_DEVERR_ALIGN is set.
  * Device errors: as spec_kv_commit; in the scratch form also SPEC_DEVERR_TREE
- * for a path entry >= n_max.  A failed sequence is left untouched in every
- * layer.
+ * for a path entry >= n_max; SPEC_DEVERR_ALIGN.  A failed sequence is left
+ * untouched in every layer.
  */
 spec_status_t spec_kv_commit_layers(
     void* const* k_layers, void* const* v_layers, const void* const* k_tree,
@@ -543,7 +566,8 @@ spec_status_t spec_tree_kv_write_paged(
 
 /* spec_kv_commit_layers on paged caches: k_layers / v_layers point at each
  * layer's pool (one block table serves every layer); in place or from
- * scratch rows exactly as spec_kv_commit_layers. */
+ * scratch rows exactly as spec_kv_commit_layers, whose 16-byte alignment
+ * rule and SPEC_DEVERR_ALIGN apply to the pools. */
 spec_status_t spec_kv_commit_layers_paged(
     void* const* k_layers, void* const* v_layers, const void* const* k_tree,
     const void* const* v_tree, int32_t num_layers, const int32_t* block_table,

@@ -26,7 +26,8 @@ than itself).
 from .attention import tree_attention, ancestors, path_to_root  # noqa: F401
 from .accept import (AcceptResult, accept_tree, keep_probability, remove_draft_mass,  # noqa: F401
                      target_distribution, sample_inverse_cdf, draft_p_to_target, filter_keep,
-                     terminal_distribution, TIE_BAND, SAMPLE_BAND, DEGENERATE_BAND)
+                     terminal_distribution, TIE_BAND, SAMPLE_BAND, FILTER_BAND,
+                     DEGENERATE_BAND)
 from .commit import kv_commit, kv_commit_from_buffer  # noqa: F401
 from .tree import TreeBuilder, build_tree  # noqa: F401
 from .rope import rope_rotate, node_positions, tree_kv_write  # noqa: F401

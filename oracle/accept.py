@@ -41,9 +41,14 @@ the rule itself is unchanged, so the output follows the filtered q.
 
 Near ties.  Decisions whose |u - min(1, ratio)| < TIE_BAND, samples whose
 threshold u * W lies within SAMPLE_BAND * W of an edge of the chosen bucket,
-and residuals whose mass is a positive fraction below DEGENERATE_BAND of the
-distribution they came from are flagged; a flagged sequence-step is excluded
-from bit-exact comparison with another implementation and logged.
+top-p boundaries within FILTER_BAND of p, and residuals whose mass is a
+positive fraction below DEGENERATE_BAND of the distribution they came from
+are flagged; a flagged sequence-step is excluded from bit-exact comparison
+with another implementation and logged.  The bands are readings, not the
+pages': each is at least ten times the rounding an implementation that sums
+the same float64 quantities in another order (or, for the top-p masses, in
+fixed point of 2^-47 per entry, at most V * 2^-47 < 1e-9 for V up to 128k)
+can make.
 """
 from dataclasses import dataclass, field
 from typing import List, Optional
@@ -54,6 +59,7 @@ from .validate import ERR_NONFINITE, ERR_TOKEN, ERR_TREE, validate_tree
 
 TIE_BAND = 1e-6
 SAMPLE_BAND = 1e-9
+FILTER_BAND = 1e-8
 DEGENERATE_BAND = 1e-12
 
 
@@ -260,7 +266,7 @@ def accept_tree(tokens, parents, n_nodes, draft_p, logits, T, u_accept, u_sample
 
     Near ties (flag `near_tie`): a test with |u - keep probability| <
     TIE_BAND, a sample whose threshold lies within SAMPLE_BAND of an edge of
-    the chosen bucket, a top-p boundary within TIE_BAND, and a residual whose
+    the chosen bucket, a top-p boundary within FILTER_BAND, and a residual whose
     mass is positive but below DEGENERATE_BAND of the distribution it came
     from (rounding then decides what is left).
     """
@@ -321,8 +327,10 @@ def accept_tree(tokens, parents, n_nodes, draft_p, logits, T, u_accept, u_sample
 
 def _is_near_tie(record):
     kind, margin = record[2], record[5]
-    if kind in ("accept-test", "filter"):
+    if kind == "accept-test":
         return margin < TIE_BAND
+    if kind == "filter":
+        return margin < FILTER_BAND
     if kind == "sample":
         return margin < SAMPLE_BAND
     if kind == "residual":

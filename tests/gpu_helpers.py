@@ -72,7 +72,7 @@ def compare_attention(w, attn, nodes_per_seq=None, heads=None, seqs=None, rng=No
 # Near-tie bands of the oracle by the kind a GPU tie record carries:
 # 0 child test, 1 terminal sample, 2 degenerate residual, 3 top-p boundary.
 TIE_BANDS = {0: oracle.TIE_BAND, 1: oracle.SAMPLE_BAND, 2: oracle.DEGENERATE_BAND,
-             3: oracle.TIE_BAND}
+             3: oracle.FILTER_BAND}
 CONFIRM = 10.0   # a GPU tie record counts only if the oracle's margin is under 10x its band
 # (test id, sequences compared, excluded sequences) of every walk comparison,
 # printed in the session's terminal summary

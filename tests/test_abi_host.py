@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.spec_abi_version() == 1
+    assert lib.spec_abi_version() == 2
     for s in range(-8, 1):
         assert len(lib.spec_status_string(s)) > 0
     assert lib.spec_status_string(-99) == b"unknown status"
@@ -168,6 +168,11 @@ def test_commit_host_checks(lib):
     assert f(*bad) == SPEC_E_SHAPE
     bad = list(args); bad[10] = 3          # dtype
     assert f(*bad) == SPEC_E_DTYPE
+    # rows move in 16-byte chunks: a cache view 2 bytes off is refused
+    off = ctypes.c_void_p(((P.value + 15) & ~15) + 2)
+    for i in (0, 1):
+        bad = list(args); bad[i] = off
+        assert f(*bad) == SPEC_E_SHAPE, i
 
 
 def test_commit_layers_host_checks(lib):
@@ -265,10 +270,13 @@ def test_accept_ex_host_checks(lib):
     f = lib.spec_accept_tree_ex
     # tokens, parents, n_nodes, draft_p, logits, B, n_max, V, max_depth, T, temps, top_k,
     # top_p, d2t, Vd, u_accept, u_sample, accept_len, path, out_tokens, n_out, final_dist,
-    # tie_log, tie_cap, tie_count, workspace, ws_bytes, dev_error, stream
+    # tie_log, tie_cap, tie_count, workspace, ws_bytes, launch, dev_error, stream
     args = ([P] * 5 + [2, 6, 100, 5, 1.0, None, None, None, None, 0] + [P] * 6 +
-            [None, None, 0, None, P, 1 << 20, None, None])
+            [None, None, 0, None, P, 1 << 20, 0, None, None])
     assert f(*([None] + args[1:])) == SPEC_E_NULL
+    for launch in (-1, 2, 7):              # only ordinary (0) and cooperative (1)
+        bad = list(args); bad[27] = launch
+        assert f(*bad) == SPEC_E_VALUE
     bad = list(args); bad[9] = -1.0        # scalar temperature checked without the array
     assert f(*bad) == SPEC_E_VALUE
     bad = list(args); bad[13] = P; bad[14] = 0     # d2t needs 1 <= Vd <= V

@@ -21,13 +21,13 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(api, w, dev, draft_p, *, temperatures=None, d2t=None, T=None, tokens=None, top_k=None,
-         top_p=None, logits=None):
+         top_p=None, logits=None, launch="ordinary"):
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     res = api.accept_tree(tokens if tokens is not None else dev["tokens"], dev["parents"],
                           dev["n_nodes"], draft_p, dev["logits"] if logits is None else logits,
                           w.T if T is None else T, dev["u_accept"], dev["u_sample"], w.max_depth,
                           final_dist=True, tie_cap=4096, dev_error=err, temperatures=temperatures,
-                          d2t=d2t, top_k=top_k, top_p=top_p)
+                          d2t=d2t, top_k=top_k, top_p=top_p, launch=launch)
     torch.cuda.synchronize()
     host = {k: v.cpu().numpy() for k, v in res.items() if isinstance(v, torch.Tensor) and k != "tie_log"}
     host["ties"] = api.decode_ties(res["tie_log"], res["tie_count"])
@@ -316,3 +316,37 @@ def test_top_k_alone(hip_lib, name):
         v = int(host["path"][b, host["accept_len"][b]])
         keep, _ = oracle.filter_keep(logits[b, v], float(w.T), int(k[b]), 0.0)
         assert np.all(host["final_dist"][b][~keep] == 0.0), b
+
+
+@pytest.mark.parametrize("cfg,variant", [(4, "plain"), (4, "filters"), (5, "plain"),
+                                         (2, "draft-vocab")])
+def test_cooperative_launch_same_bits(hip_lib, cfg, variant):
+    """The cooperative launch of the walk gives the ordinary launch's outputs
+    bit for bit at full size (the same kernel, only the launch differs), and
+    both match the oracle."""
+    api = hip_lib
+    w = make_workload(cfg, T=1.0)
+    dev = to_device(w)
+    kw = {}
+    p_rows, draft_p = (lambda b: w.draft_p[b]), dev["draft_p"]
+    top_k = top_p = None
+    if variant == "filters":
+        rng = np.random.default_rng(91)
+        top_k = rng.choice(np.array([0, 1, 20, 1000], np.int32), size=w.B)
+        # (0.99 lies in the 128k vocabulary's flat tail, where token masses
+        # are ~1e-7 and many boundaries fall inside the near-tie band)
+        top_p = rng.choice(np.array([0.0, 0.5, 0.8, 0.9], np.float32), size=w.B)
+        kw = dict(top_k=torch.from_numpy(top_k).to("cuda"), top_p=torch.from_numpy(top_p).to("cuda"))
+    tokens = w.tokens
+    if variant == "draft-vocab":
+        d2t, pd, tokens = _draft_vocab(w, 32000, 92)
+        draft_p = torch.from_numpy(pd).to("cuda")
+        kw = dict(d2t=torch.from_numpy(d2t).to("cuda"), tokens=torch.from_numpy(tokens).to("cuda"))
+        p_rows = lambda b: oracle.draft_p_to_target(pd[b], d2t, w.V)
+    say(f"[gpu] cooperative launch {variant}: B={w.B} V={w.V} n_max={w.n_max}")
+    ordinary = _run(api, w, dev, draft_p, launch="ordinary", **kw)
+    coop = _run(api, w, dev, draft_p, launch="cooperative", **kw)
+    assert ordinary["dev_error"] == 0 and coop["dev_error"] == 0
+    for k in ("accept_len", "path", "out_tokens", "n_out", "final_dist", "tie_count"):
+        np.testing.assert_array_equal(coop[k], ordinary[k], err_msg=k)
+    compare_walks(w, coop, p_rows=p_rows, tokens=tokens, top_k=top_k, top_p=top_p)

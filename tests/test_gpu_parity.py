@@ -220,8 +220,9 @@ def test_commit_in_place_hazard(hip_lib):
 def test_accept_wait_bound_reports_sync(hip_lib, monkeypatch):
     """A host-set negative wait bound makes every vocabulary exchange give up:
     the call must end normally with SPEC_DEVERR_SYNC set and the failed
-    sequences marked, and the next call with the default bound on the same
-    workspace must be exact again."""
+    sequences marked.  The remedy the header gives, the same call repeated
+    with the cooperative launch, and then an ordinary call, both with the
+    default bound on the same workspace, must be exact again."""
     import torch
     from eagle_tree_verification_amd import api
     w = make_workload(4, batch=8, prefix=(64, 64), vocab=128256, drafts=12, depth=4, seed=5)
@@ -230,11 +231,11 @@ def test_accept_wait_bound_reports_sync(hip_lib, monkeypatch):
                      device="cuda")
     say(f"[gpu] wait bound: B={w.B} V={w.V}, forced give-up then default")
 
-    def call():
+    def call(launch="ordinary"):
         err = torch.zeros(1, dtype=torch.int32, device="cuda")
         r = api.accept_tree(dev["tokens"], dev["parents"], dev["n_nodes"], dev["draft_p"],
                             dev["logits"], w.T, dev["u_accept"], dev["u_sample"], w.max_depth,
-                            workspace=ws, dev_error=err)
+                            workspace=ws, dev_error=err, launch=launch)
         torch.cuda.synchronize()
         return r, int(err.item())
 
@@ -243,12 +244,13 @@ def test_accept_wait_bound_reports_sync(hip_lib, monkeypatch):
     assert e0 & api.DEVERR_SYNC, e0
     assert (r0["accept_len"].cpu().numpy() == -1).all()
     monkeypatch.delenv("SPEC_ACCEPT_SPIN_LIMIT")
-    r, e1 = call()
-    assert e1 == 0
-    host = {k: v.cpu().numpy() for k, v in r.items() if isinstance(v, torch.Tensor)}
-    host["ties"] = np.zeros(0, dtype=api.TIE_DTYPE)
-    host["final_dist"] = None
-    compare_accept(w, host)
+    for launch in ("cooperative", "ordinary"):
+        r, e1 = call(launch)
+        assert e1 == 0, launch
+        host = {k: v.cpu().numpy() for k, v in r.items() if isinstance(v, torch.Tensor)}
+        host["ties"] = np.zeros(0, dtype=api.TIE_DTYPE)
+        host["final_dist"] = None
+        compare_accept(w, host)
 
 
 def _layer_setup(nl, seed):
@@ -304,6 +306,47 @@ def test_commit_layers_parity(hip_lib, scratch):
                 k2, v2, _ = oracle.kv_commit(kc[l][b], vc[l][b], L, path[b, : a + 1], a)
             np.testing.assert_array_equal(kg[b], k2)
             np.testing.assert_array_equal(vg[b], v2)
+
+
+@pytest.mark.parametrize("which", ["cache", "scratch"])
+def test_commit_layers_misaligned_layer(hip_lib, which):
+    """One layer buffer 2 bytes off 16-byte alignment (a cache in the in-place
+    form, a scratch buffer in the other): the kernels refuse the whole call,
+    so no layer of any sequence changes, no length advances, and
+    SPEC_DEVERR_ALIGN is set.  The misaligned pointer is only compared, never
+    dereferenced; its buffer is an in-bounds view of a larger allocation."""
+    import torch
+    from eagle_tree_verification_amd import api
+    nl = 3
+    w, path, acc, kc, vc, kt, vt, dev = _layer_setup(nl, 53)
+    say(f"[gpu] commit_layers: misaligned {which} buffer of layer 1")
+
+    def shifted(a):  # the same contents at an address 2 bytes past 16-byte alignment
+        t = dev(a)
+        backing = torch.empty(t.numel() + 8, dtype=t.dtype, device="cuda")
+        view = backing[1:1 + t.numel()].view(t.shape)
+        view.copy_(t)
+        assert view.data_ptr() % 16 == 2
+        return view
+
+    kd, vd = [dev(a) for a in kc], [dev(a) for a in vc]
+    td = None
+    if which == "cache":
+        kd[1] = shifted(kc[1])
+    else:
+        td = ([dev(a) for a in kt], [dev(a) for a in vt])
+        td[1][1] = shifted(vt[1])
+    plen = torch.from_numpy(w.prefix_len.copy()).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    api.kv_commit_layers(kd, vd, plen, torch.from_numpy(path).cuda(), torch.from_numpy(acc).cuda(),
+                         w.max_depth, k_tree=None if td is None else td[0],
+                         v_tree=None if td is None else td[1], dev_error=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == api.DEVERR_ALIGN
+    np.testing.assert_array_equal(plen.cpu().numpy(), w.prefix_len)
+    for l in range(nl):
+        np.testing.assert_array_equal(kd[l].view(torch.int16).cpu().numpy().view(np.uint16), kc[l])
+        np.testing.assert_array_equal(vd[l].view(torch.int16).cpu().numpy().view(np.uint16), vc[l])
 
 
 def test_commit_layers_bad_path_and_forms_agree(hip_lib):

@@ -609,6 +609,12 @@ def test_top_p_boundary_is_a_near_tie():
     r = oracle.accept_tree(ids, par, 2, dp, logits, 1.0, [0.0, 0.99], [0.5, 0.5], 1,
                            top_p=6 / 9.5)
     assert r.near_tie
+    # the band: 5e-9 off the boundary is a near tie, 2e-8 off is not (a
+    # sample threshold of 0.3 stays clear of every bucket edge)
+    for dp_off, flagged in ((5e-9, True), (-5e-9, True), (2e-8, False), (-2e-8, False)):
+        r = oracle.accept_tree(ids, par, 2, dp, logits, 1.0, [0.0, 0.99], [0.3, 0.3], 1,
+                               top_p=6 / 9.5 + dp_off)
+        assert r.near_tie == flagged, dp_off
     r = oracle.accept_tree(ids, par, 2, dp, logits, 1.0, [0.0, 0.99], [0.5, 0.5], 1, top_p=0.7)
     assert not r.near_tie
     # token 0 is outside the nucleus at 0.7: q(0) = 0, so it is rejected
