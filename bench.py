@@ -11,8 +11,12 @@ Prints one JSON line.  `value` is verified tree tokens per second (draft nodes
 per step / mean step time); committed tokens per second are reported beside
 it.  `roofline` covers the attention kernel, the dominant one, with
 algorithmic bytes (what the method must move) over its mean event-timed
-duration.  `cpu_baseline` times the oracle on a bounded sample of the same
-workload on the host cores.
+duration.  `configs` holds the same step timed on every other configuration
+(tiny chain at T=0 and T=1, Llama-3-8B-shaped batch 1, Vicuna-13B-shaped
+batch 1 at T=0 and T=1, Llama-3.3-70B-shaped batch 16), each with its
+verified and committed tokens/s, per-kernel times and algorithmic rates.
+`cpu_baseline` times the oracle on a bounded sample of the headline workload
+on the host cores.
 
     python bench.py [--steps K] [--warmup W] [--config 4] [--gpus 1]
 """
@@ -115,8 +119,11 @@ def cpu_baseline(w, budget_s=12.0):
     import oracle
     from threadpoolctl import threadpool_limits
 
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    host_cores = os.cpu_count()
+    avail = len(os.sched_getaffinity(0))
+    cores = min(avail, 16)
     t0 = time.perf_counter()
+    c0 = time.process_time()
     drafts = 0
     done = 0
     with threadpool_limits(limits=cores):
@@ -134,11 +141,142 @@ def cpu_baseline(w, budget_s=12.0):
             if time.perf_counter() - t0 > budget_s:
                 break
     dt = time.perf_counter() - t0
+    busy = (time.process_time() - c0) / dt
     return {"value": drafts / dt, "unit": "verified tree tokens/s", "cores": cores,
+            "host_cores": host_cores, "host_cores_available": avail,
+            "cpu_seconds_per_second": round(busy, 2),
             "kind": "oracle",
             "sample": f"first {done} of {w.B} sequences of the same workload (all nodes and heads "
                       f"of tree attention in float64, the acceptance walk and the commit), "
-                      f"{dt:.1f} s on {cores} host threads"}
+                      f"{dt:.1f} s; numpy's thread pools capped at {cores} of the "
+                      f"{avail} cores this process may use ({host_cores} on the host); "
+                      f"{busy:.2f} CPU-seconds per second on average (the Python walk "
+                      f"runs on one thread)"}
+
+
+def time_steps(w, dev, steps, warmup):
+    """Warm-up, then `steps` timed verify steps of workload w (attention,
+    walk, commit on one stream, HIP events between the calls); returns the
+    per-call times, the last step's walk outputs and the attention
+    workspace."""
+    import torch
+
+    from eagle_tree_verification_amd import api
+
+    kv_dt = api.SPEC_BF16 if w.kv_dtype == "bf16" else api.SPEC_F32
+    ws_attn = torch.empty(max(1, api.verify_tree_attn_workspace_size(
+        w.B, w.n_max, w.Hq, w.Hkv, w.d, w.L_cap, kv_dt)), dtype=torch.uint8, device="cuda")
+    ws_acc = torch.empty(api.accept_tree_workspace_size(w.B, w.n_max, w.V), dtype=torch.uint8,
+                         device="cuda")
+    out = torch.empty((w.B, w.n_max, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    outs = {"accept_len": torch.empty(w.B, dtype=torch.int32, device="cuda"),
+            "path": torch.empty((w.B, w.max_depth + 1), dtype=torch.int32, device="cuda"),
+            "out_tokens": torch.empty((w.B, w.max_depth + 1), dtype=torch.int32, device="cuda"),
+            "n_out": torch.empty(w.B, dtype=torch.int32, device="cuda")}
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    plen0 = dev["prefix_len"].clone()
+
+    def step(ev=None):
+        dev["prefix_len"].copy_(plen0)
+        if ev:
+            ev[0].record()
+        api.verify_tree_attn(dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"],
+                             dev["n_nodes"], dev["parents"], out=out, workspace=ws_attn,
+                             dev_error=err)
+        if ev:
+            ev[1].record()
+        api.accept_tree(dev["tokens"], dev["parents"], dev["n_nodes"], dev["draft_p"],
+                        dev["logits"], w.T, dev["u_accept"], dev["u_sample"], w.max_depth,
+                        workspace=ws_acc, dev_error=err, outputs=outs)
+        if ev:
+            ev[2].record()
+        api.kv_commit(dev["k_cache"], dev["v_cache"], dev["prefix_len"], outs["path"],
+                      outs["accept_len"], w.max_depth, dev_error=err)
+        if ev:
+            ev[3].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if int(err.item()) != 0:
+        raise RuntimeError(f"device error bits {int(err.item())}")
+    dev["prefix_len"].copy_(plen0)
+    torch.cuda.synchronize()
+    return {"attn": np.array([e[0].elapsed_time(e[1]) for e in events]),
+            "accept": np.array([e[1].elapsed_time(e[2]) for e in events]),
+            "commit": np.array([e[2].elapsed_time(e[3]) for e in events]),
+            "step": np.array([e[0].elapsed_time(e[3]) for e in events]),
+            "wall": wall, "outs": outs, "plen0": plen0, "ws_attn": ws_attn, "ws_acc": ws_acc}
+
+
+def step_summary(w, t):
+    """Throughput, per-kernel times and algorithmic rates of timed steps."""
+    ms = float(t["step"].mean())
+    accept_len = t["outs"]["accept_len"].cpu().numpy()
+    path = t["outs"]["path"].cpu().numpy()
+    committed = int((accept_len + 1).sum())
+    a_bytes, a_flops = attention_cost(w)
+    acc_b = accept_bytes(w, accept_len, path)
+    com_b = commit_bytes(w, accept_len, path)
+    km = {k: float(t[k].mean()) for k in ("attn", "accept", "commit")}
+    gbps = lambda nbytes, m: round(nbytes / (m * 1e-3) / 1e9, 1)
+    return {
+        "verified_tokens_per_s": round(w.verified_tokens / (ms * 1e-3), 1),
+        "committed_tokens_per_s": round(committed / (ms * 1e-3), 1),
+        "ms_per_step": round(ms, 4),
+        "tokens_per_step": {"verified": int(w.verified_tokens), "committed": committed},
+        "kernels_ms": {"verify_tree_attn": round(km["attn"], 4),
+                       "accept_tree": round(km["accept"], 4),
+                       "kv_commit": round(km["commit"], 4)},
+        "algorithmic_bytes": {"verify_tree_attn": a_bytes, "accept_tree": int(acc_b),
+                              "kv_commit": int(com_b)},
+        "algorithmic_GBps": {"verify_tree_attn": gbps(a_bytes, km["attn"]),
+                             "accept_tree": gbps(acc_b, km["accept"]),
+                             "kv_commit": gbps(com_b, km["commit"]),
+                             "step": gbps(a_bytes + acc_b + com_b, ms)},
+        "attn_frac_hbm_peak": round(a_bytes / (km["attn"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "attn_mfma_tflops": round(a_flops / (km["attn"] * 1e-3) / 1e12, 2),
+        "attn_frac_mfma_peak": round(a_flops / (km["attn"] * 1e-3) / 1e12
+                                     / BF16_MFMA_PEAK_TFLOPS, 4),
+        "mean_accept_len": round(float(accept_len.mean()), 3),
+    }
+
+
+# The configurations besides the headline one, each timed as its own step:
+# (config id, temperature)
+OTHER_CONFIGS = [(1, 0.0), (1, 1.0), (2, 1.0), (3, 0.0), (3, 1.0), (5, 1.0)]
+
+
+def configs_bench(steps=20, warmup=3):
+    """Every other configuration's step, timed like the headline one."""
+    import torch
+
+    from eagle_tree_verification_amd.workloads import CONFIGS, make_workload, to_device
+
+    res = {}
+    for cfg_id, T in OTHER_CONFIGS:
+        cfg = CONFIGS[cfg_id]
+        w = make_workload(cfg_id, T=T)
+        dev = to_device(w)
+        t = time_steps(w, dev, steps, warmup)
+        rec = {"workload": f"{cfg.name}: batch {w.B}, {w.Hq} q / {w.Hkv} kv heads, head_dim "
+                           f"{w.d}, {w.kv_dtype} KV, prefix {cfg.prefix[0]}-{cfg.prefix[1]}, "
+                           f"{cfg.drafts}-draft depth-{cfg.depth} trees, vocab {w.V}, T={T:g}",
+               "steps": steps, "warmup": warmup}
+        rec.update(step_summary(w, t))
+        res[f"{cfg.name}-T{T:g}"] = rec
+        log(f"[bench] {cfg.name} T={T:g}: {rec['ms_per_step']} ms/step, "
+            f"{rec['verified_tokens_per_s']} verified tokens/s")
+        del dev, t
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return res
 
 
 def commit_layers_bench(w, dev, outs, plen0, layers, reps=20):
@@ -564,6 +702,8 @@ def main():
                     help="skip timing tree attention over a paged (block-table) cache")
     ap.add_argument("--no-shard", action="store_true",
                     help="skip timing one GPU's share of an 8-way tensor-parallel target")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other configurations' steps")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="run one plain device copy of this size first (counter calibration)")
     args = ap.parse_args()
@@ -592,63 +732,12 @@ def main():
         torch.cuda.synchronize()
         del a, b_
 
-    kv_dt = api.SPEC_BF16 if w.kv_dtype == "bf16" else api.SPEC_F32
-    ws_attn = torch.empty(max(1, api.verify_tree_attn_workspace_size(
-        w.B, w.n_max, w.Hq, w.Hkv, w.d, w.L_cap, kv_dt)), dtype=torch.uint8, device="cuda")
-    ws_acc = torch.empty(api.accept_tree_workspace_size(w.B, w.n_max, w.V), dtype=torch.uint8,
-                         device="cuda")
-    out = torch.empty((w.B, w.n_max, w.Hq, w.d), dtype=torch.float32, device="cuda")
-    outs = {"accept_len": torch.empty(w.B, dtype=torch.int32, device="cuda"),
-            "path": torch.empty((w.B, w.max_depth + 1), dtype=torch.int32, device="cuda"),
-            "out_tokens": torch.empty((w.B, w.max_depth + 1), dtype=torch.int32, device="cuda"),
-            "n_out": torch.empty(w.B, dtype=torch.int32, device="cuda")}
-    err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    plen0 = dev["prefix_len"].clone()
-
-    def step(ev=None):
-        dev["prefix_len"].copy_(plen0)
-        if ev:
-            ev[0].record()
-        api.verify_tree_attn(dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"],
-                             dev["n_nodes"], dev["parents"], out=out, workspace=ws_attn,
-                             dev_error=err)
-        if ev:
-            ev[1].record()
-        api.accept_tree(dev["tokens"], dev["parents"], dev["n_nodes"], dev["draft_p"],
-                        dev["logits"], w.T, dev["u_accept"], dev["u_sample"], w.max_depth,
-                        workspace=ws_acc, dev_error=err, outputs=outs)
-        if ev:
-            ev[2].record()
-        api.kv_commit(dev["k_cache"], dev["v_cache"], dev["prefix_len"], outs["path"],
-                      outs["accept_len"], w.max_depth, dev_error=err)
-        if ev:
-            ev[3].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(events[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    if int(err.item()) != 0:
-        raise RuntimeError(f"device error bits {int(err.item())}")
-
-    t_attn = np.array([e[0].elapsed_time(e[1]) for e in events])
-    t_acc = np.array([e[1].elapsed_time(e[2]) for e in events])
-    t_com = np.array([e[2].elapsed_time(e[3]) for e in events])
-    t_step = np.array([e[0].elapsed_time(e[3]) for e in events])
-    ms = float(t_step.mean())
-    accept_len = outs["accept_len"].cpu().numpy()
-    path = outs["path"].cpu().numpy()
-    verified = w.verified_tokens
-    committed = int((accept_len + 1).sum())
+    t = time_steps(w, dev, args.steps, args.warmup)
+    outs, plen0, ws_attn, ws_acc = t["outs"], t["plen0"], t["ws_attn"], t["ws_acc"]
+    summ = step_summary(w, t)
+    ms = summ["ms_per_step"]
     a_bytes, a_flops = attention_cost(w)
-    acc_b = accept_bytes(w, accept_len, path)
-    com_b = commit_bytes(w, accept_len, path)
-    attn_ms = float(t_attn.mean())
+    attn_ms = float(t["attn"].mean())
     achieved = a_bytes / (attn_ms * 1e-3) / 1e9
     intensity = a_flops / a_bytes
     ridge = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
@@ -667,7 +756,7 @@ def main():
                      "unit": "TFLOP/s", "frac": roof["mfma_frac"]})
     rec = {
         "metric": "verified tree tokens/s + committed tokens/s at 1 GPU; % peak HBM GB/s",
-        "value": round(verified / (ms * 1e-3), 1),
+        "value": summ["verified_tokens_per_s"],
         "unit": "verified tree tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
@@ -680,13 +769,14 @@ def main():
                    "global_batch": w.B, "prefix_mean": float(w.prefix_len.mean()),
                    "tree_drafts": cfg.drafts, "tree_depth": cfg.depth, "vocab": w.V,
                    "temperature": w.T, "parallelism": "single GPU"},
-        "committed_tokens_per_s": round(committed / (ms * 1e-3), 1),
-        "tokens_per_step": {"verified": verified, "committed": committed},
-        "kernels_ms": {"verify_tree_attn": round(attn_ms, 4), "accept_tree": round(float(t_acc.mean()), 4),
-                       "kv_commit": round(float(t_com.mean()), 4)},
-        "step_algorithmic_GBps": round((a_bytes + acc_b + com_b) / (ms * 1e-3) / 1e9, 1),
-        "accept_algorithmic_GBps": round(acc_b / (t_acc.mean() * 1e-3) / 1e9, 1),
-        "ms_per_step_wall_incl_length_restore": round(wall / args.steps * 1e3, 4),
+        "committed_tokens_per_s": summ["committed_tokens_per_s"],
+        "tokens_per_step": summ["tokens_per_step"],
+        "kernels_ms": summ["kernels_ms"],
+        "algorithmic_GBps": summ["algorithmic_GBps"],
+        "step_algorithmic_GBps": summ["algorithmic_GBps"]["step"],
+        "accept_algorithmic_GBps": summ["algorithmic_GBps"]["accept_tree"],
+        "mean_accept_len": summ["mean_accept_len"],
+        "ms_per_step_wall_incl_length_restore": round(t["wall"] / args.steps * 1e3, 4),
         "roofline": roof,
     }
     if args.commit_layers > 0:
@@ -702,6 +792,8 @@ def main():
         rec["paged"] = paged_bench(w, dev, ws_attn)
     if not args.no_shard:
         rec["shard"] = shard_bench(args.config)
+    if not args.no_configs:
+        rec["configs"] = configs_bench()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)
