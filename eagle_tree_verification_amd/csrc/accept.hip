@@ -346,28 +346,31 @@ __device__ bool exchange(const AcceptArgs& a, int bl, int part, int& gen, double
   }
   const int nw = a.KP * 8;
   int bad = 0;
+  // every word this thread reads is requested at once, then re-polled until
+  // its tag is current: one memory round trip when the words are there
+  constexpr int kRounds = (SPEC_MAX_NODES * 8 + NT - 1) / NT;
+  uint64_t w[kRounds];
 #pragma unroll
-  for (int r = 0; r < (SPEC_MAX_NODES * 8 + NT - 1) / NT; ++r) {
+  for (int r = 0; r < kRounds; ++r) {
     const int i = t + r * NT;  // word i: part i / 8, value (i / 4) % 2, bits 16 (i % 4)
-    uint64_t w = 0;
+    w[r] = i < nw ? __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+  }
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int i = t + r * NT;
     if (i < nw) {
       int spins = 0;
-      for (;;) {
-        w = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (a.spin_limit < 0) {  // test hook: every wait gives up at once
-          bad = 1;
-          break;
-        }
-        if ((w >> 16) == tag) break;
-        if (++spins > a.spin_limit) {
+      while (a.spin_limit < 0 || (w[r] >> 16) != tag) {
+        if (a.spin_limit < 0 || ++spins > a.spin_limit) {  // a negative bound: test hook
           bad = 1;
           break;
         }
         __builtin_amdgcn_s_sleep(1);
+        w[r] = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     // the four words of one value sit in four consecutive lanes
-    const uint64_t p0 = w & 0xffffull;
+    const uint64_t p0 = w[r] & 0xffffull;
     const uint64_t p1 = __shfl_down(p0, 1);
     const uint64_t p2 = __shfl_down(p0, 2);
     const uint64_t p3 = __shfl_down(p0, 3);
@@ -758,6 +761,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   constexpr int BG2 = NG < 2 ? NG : 2;
   __shared__ int s_par[SPEC_MAX_NODES];
   __shared__ int s_tok[SPEC_MAX_NODES];
+  __shared__ unsigned long long s_kids[SPEC_MAX_NODES];  // bit c set: node c is a child
   __shared__ int s_path[SPEC_MAX_NODES + 1];
   __shared__ int s_out[SPEC_MAX_NODES + 1];
   __shared__ double red[2 * (NT / 64)];
@@ -849,6 +853,13 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
     if (writer0) write_failure(a, b, err);
     return;
   }
+  // each node's children as a bit mask (lowest set bit = lowest id), so that a
+  // visit walks its own children only
+  static_assert(SPEC_MAX_NODES <= 64, "children masks are 64 bits");
+  if (tid < SPEC_MAX_NODES) s_kids[tid] = 0ull;
+  __syncthreads();
+  if (tid > 0 && tid < n) atomicOr(&s_kids[s_par[tid]], 1ull << tid);
+  __syncthreads();
 
   int gen = 0;
   int v = 0, depth = 0;
@@ -896,11 +907,13 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
         return;
       }
       int nxt = -1;
-      for (int c = v + 1; c < n; ++c)
-        if (s_par[c] == v && s_tok[c] == gi) {
+      for (unsigned long long m = s_kids[v]; m; m &= m - 1) {
+        const int c = __ffsll(m) - 1;
+        if (s_tok[c] == gi) {
           nxt = c;
           break;
         }
+      }
       __syncthreads();
       if (tid == 0) s_out[depth] = gi;
       if (nxt >= 0) {
@@ -1059,8 +1072,8 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
     // ---- children in ascending id against the running residual ------------
     double C = 0.0, Z = 1.0;
     int nxt = -1;
-    for (int c = v + 1; c < n; ++c) {
-      if (s_par[c] != v) continue;
+    for (unsigned long long km = s_kids[v]; km; km &= km - 1) {
+      const int c = __ffsll(km) - 1;
       const int xt = s_tok[c];
       const float pxf = s_kp[c];
       if (!isfinite(pxf)) {
