@@ -570,6 +570,9 @@ constexpr int kHistBatch = 4;  // workgroups whose words one thread loads at onc
 // different banks), which cuts same-address serialisation when many lanes
 // share a digit; the copies are folded into copy 0 before the exchange.
 constexpr int kCopies = 4;
+// A wave gathers a filtered row's kept entries for a residual pass when none
+// of its threads holds more than this many; otherwise it streams its slices.
+constexpr int kMaskMax = 2;
 
 __device__ bool exchange_hist(const AcceptArgs& a, int bl, int part, int& gen,
                               const uint32_t* h_cnt, const uint64_t* h_mass, int jb,
@@ -781,6 +784,9 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   __shared__ int s_or, s_hit, s_first;
   __shared__ float s_kp[SPEC_MAX_NODES], s_kl[SPEC_MAX_NODES], s_ku[SPEC_MAX_NODES], s_us;
   __shared__ double s_tab[kTab];
+  // filtered rows: bit g * W + j set where this thread's entry j of group g is
+  // kept (all bits once a negative draft entry is seen)
+  __shared__ unsigned long long s_keep[FILT ? NT : 1];
 
   const int bl = blockIdx.x / a.KP;   // sequence within this launch's group
   const int b = a.b0 + bl;
@@ -1007,9 +1013,10 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
     float lcut = -INFINITY;  // q is restricted to logits >= lcut
     // kept(x): x passes the filters (always, in a variant without them)
     auto kept = [&](float x) { return !FILT || x >= lcut; };
+    bool masks = false;  // s_keep holds this row's kept entries
     if (FILT && (fk > 0 || fP > 0)) {
       double fmargin;
-      if (!filter_threshold<NG, W, 1>(a, bl, part, gen, lrow, lo, hi, invT, M, S, fk, fP, s_tab,
+      if (!filter_threshold<NG, W, BG2>(a, bl, part, gen, lrow, lo, hi, invT, M, S, fk, fP, s_tab,
                                         reinterpret_cast<uint32_t*>(&scan[4][0]),
                                         reinterpret_cast<uint64_t*>(&scan[0][0]), fsh, &s_or, lcut,
                                         fmargin)) {
@@ -1019,6 +1026,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       if (writer0 && tid == 0 && fmargin < kFilterBand)
         log_tie(a, b, v, 3, a.top_p[b], fmargin);
       double ek = 0.0;
+      unsigned long long km = 0;
       stream_slice<NG, W, BG2, false>(lrow, -INFINITY, lrow, 0.f, lo, hi,
           [&](int g0, float (*xv)[W], float (*)[W]) {
 #pragma unroll
@@ -1026,11 +1034,17 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
               double sg = 0.0;
 #pragma unroll
               for (int j = 0; j < W; ++j)
-                if (kept(xv[gb][j])) sg += exp_tab(fma((double)xv[gb][j], invT, -M), s_tab);
+                if (kept(xv[gb][j])) {
+                  sg += exp_tab(fma((double)xv[gb][j], invT, -M), s_tab);
+                  if (elem_index<W>(lo, (g0 + gb) * W + j) < hi)
+                    km |= 1ull << ((g0 + gb) * W + j);
+                }
               ek += sg;
               scan[g0 + gb][tid] = sg;
             }
           });
+      s_keep[tid] = km;
+      masks = true;
       scan_rel = false;  // the filter's histograms overwrote scan; it now holds kept sums
       ek = block_sum(ek, red);
       if (!exchange(a, bl, part, gen, ek, 0.0, xs, &s_or)) {
@@ -1072,6 +1086,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
     // ---- children in ascending id against the running residual ------------
     double C = 0.0, Z = 1.0;
     int nxt = -1;
+    bool p_read = false;  // a residual pass has read (and checked) the draft row
     for (unsigned long long km = s_kids[v]; km; km &= km - 1) {
       const int c = __ffsll(km) - 1;
       const int xt = s_tok[c];
@@ -1100,22 +1115,57 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       double zp = 0.0;
       int pnf = 0;
       const double CnS = Cn * S;
-      stream_slice<NG, W, BG2, true, MAPPED>(lrow, -INFINITY, prow, 0.f, lo, hi,
-          [&](int g0, float (*xv)[W], float (*pv)[W]) {
+      if (FILT && masks && p_read && !__any(__popcll(s_keep[tid]) > kMaskMax)) {
+        // A later rejection at a filtered node: only kept entries contribute
+        // (q is 0 elsewhere and the draft row, already checked, has no
+        // negative entry), so each thread gathers just those.  The group sums
+        // are the streamed pass's bit for bit (its other terms are zeros).
+        const unsigned long long km = s_keep[tid];
+#pragma unroll 1
+        for (int g = 0; g < NG; ++g) {
+          double sg = 0.0;
+          const unsigned gm = (unsigned)(km >> (g * W)) & ((1u << W) - 1u);
+          if (gm) {
 #pragma unroll
-            for (int gb = 0; gb < BG2; ++gb) {
-              double sg = 0.0;
-#pragma unroll
-              for (int j = 0; j < W; ++j) {
-                pnf |= !isfinite(pv[gb][j]);
-                const double e =
-                    kept(xv[gb][j]) ? exp_tab(fma((double)xv[gb][j], invT, -M), s_tab) : 0.0;
-                sg += fmax(0.0, e - CnS * (double)pv[gb][j]);
+            for (int j = 0; j < W; ++j)
+              if (gm & (1u << j)) {
+                const int i = elem_index<W>(lo, g * W + j);
+                float pe;
+                if constexpr (MAPPED) {
+                  const int t = a.t2d[i];
+                  pe = t >= 0 ? prow[t] : 0.f;
+                } else {
+                  pe = prow[i];
+                }
+                const double e = exp_tab(fma((double)lrow[i], invT, -M), s_tab);
+                sg += fmax(0.0, e - CnS * (double)pe);
               }
-              zp += sg;
-              scan[g0 + gb][tid] = sg;
-            }
-          }, a.t2d);
+          }
+          zp += sg;
+          scan[g][tid] = sg;
+        }
+      } else {
+        bool pneg = false;
+        stream_slice<NG, W, BG2, true, MAPPED>(lrow, -INFINITY, prow, 0.f, lo, hi,
+            [&](int g0, float (*xv)[W], float (*pv)[W]) {
+#pragma unroll
+              for (int gb = 0; gb < BG2; ++gb) {
+                double sg = 0.0;
+#pragma unroll
+                for (int j = 0; j < W; ++j) {
+                  pnf |= !isfinite(pv[gb][j]);
+                  if (FILT) pneg |= pv[gb][j] < 0.f;
+                  const double e =
+                      kept(xv[gb][j]) ? exp_tab(fma((double)xv[gb][j], invT, -M), s_tab) : 0.0;
+                  sg += fmax(0.0, e - CnS * (double)pv[gb][j]);
+                }
+                zp += sg;
+                scan[g0 + gb][tid] = sg;
+              }
+            }, a.t2d);
+        if (FILT && masks && pneg) s_keep[tid] = ~0ull;
+      }
+      p_read = true;
       pnf = block_or(pnf, &s_or);
       zp = block_sum(zp, red);
       if (!exchange(a, bl, part, gen, zp, (double)pnf, xs, &s_or)) {
