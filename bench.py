@@ -9,9 +9,12 @@ values but not the amount of work.
 
 Prints one JSON line.  `value` is verified tree tokens per second (draft nodes
 per step / mean step time); committed tokens per second are reported beside
-it.  `roofline` covers the attention kernel, the dominant one, with
-algorithmic bytes (what the method must move) over its mean event-timed
-duration.  `configs` holds the same step timed on every other configuration
+it.  The step is timed as the three calls captured once into a HIP graph and
+replayed, with HIP events only at its start and end; the per-call times
+(`kernels_ms`) come from as many eagerly issued steps with events between the
+calls, whose own step time is `ms_per_step_with_call_events`.  `roofline`
+covers the attention kernel, the dominant one, with algorithmic bytes (what
+the method must move) over its mean event-timed duration.  `configs` holds the same step timed on every other configuration
 (tiny chain at T=0 and T=1, Llama-3-8B-shaped batch 1, Vicuna-13B-shaped
 batch 1 at T=0 and T=1, Llama-3.3-70B-shaped batch 16), each with its
 verified and committed tokens/s, per-kernel times and algorithmic rates.
@@ -155,10 +158,18 @@ def cpu_baseline(w, budget_s=12.0):
 
 
 def time_steps(w, dev, steps, warmup):
-    """Warm-up, then `steps` timed verify steps of workload w (attention,
-    walk, commit on one stream, HIP events between the calls); returns the
-    per-call times, the last step's walk outputs and the attention
-    workspace."""
+    """Warm-up, then two timed phases of `steps` verify steps of workload w
+    (attention, walk, commit on one stream):
+
+    - the step: the three calls captured once as a HIP graph and replayed,
+      with HIP events only at the step's start and end (eagerly issued calls
+      with the same two events if capture fails);
+    - the per-call breakdown: eagerly issued steps with events between the
+      calls (each event in the stream adds a few microseconds to the step,
+      which is why the step itself is timed without them).
+
+    Returns the per-call times (breakdown), the step times (graph), the last
+    step's walk outputs and the workspaces."""
     import torch
 
     from eagle_tree_verification_amd import api
@@ -176,10 +187,7 @@ def time_steps(w, dev, steps, warmup):
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     plen0 = dev["prefix_len"].clone()
 
-    def step(ev=None):
-        dev["prefix_len"].copy_(plen0)
-        if ev:
-            ev[0].record()
+    def calls(ev=None):
         api.verify_tree_attn(dev["q"], dev["k_cache"], dev["v_cache"], dev["prefix_len"],
                              dev["n_nodes"], dev["parents"], out=out, workspace=ws_attn,
                              dev_error=err)
@@ -192,16 +200,46 @@ def time_steps(w, dev, steps, warmup):
             ev[2].record()
         api.kv_commit(dev["k_cache"], dev["v_cache"], dev["prefix_len"], outs["path"],
                       outs["accept_len"], w.max_depth, dev_error=err)
-        if ev:
-            ev[3].record()
 
     for _ in range(warmup):
-        step()
+        dev["prefix_len"].copy_(plen0)
+        calls()
     torch.cuda.synchronize()
+
+    # per-call breakdown
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for k in range(steps):
+        dev["prefix_len"].copy_(plen0)
+        events[k][0].record()
+        calls(events[k])
+        events[k][3].record()
+    torch.cuda.synchronize()
+
+    # the step as a replayed graph
+    graph = None
+    try:
+        dev["prefix_len"].copy_(plen0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            calls()
+        torch.cuda.synchronize()
+        graph = g
+    except RuntimeError as exc:  # capture refused: time eagerly issued calls
+        log(f"[bench] graph capture failed ({exc}); timing eagerly issued calls")
+        torch.cuda.synchronize()
+    run = graph.replay if graph is not None else calls
+    for _ in range(2):
+        dev["prefix_len"].copy_(plen0)
+        run()
+    torch.cuda.synchronize()
+    step_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     t0 = time.perf_counter()
     for k in range(steps):
-        step(events[k])
+        dev["prefix_len"].copy_(plen0)
+        step_ev[k][0].record()
+        run()
+        step_ev[k][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     if int(err.item()) != 0:
@@ -211,7 +249,9 @@ def time_steps(w, dev, steps, warmup):
     return {"attn": np.array([e[0].elapsed_time(e[1]) for e in events]),
             "accept": np.array([e[1].elapsed_time(e[2]) for e in events]),
             "commit": np.array([e[2].elapsed_time(e[3]) for e in events]),
-            "step": np.array([e[0].elapsed_time(e[3]) for e in events]),
+            "step_with_call_events": np.array([e[0].elapsed_time(e[3]) for e in events]),
+            "step": np.array([e[0].elapsed_time(e[1]) for e in step_ev]),
+            "step_timing": "hip graph replay" if graph is not None else "eager calls",
             "wall": wall, "outs": outs, "plen0": plen0, "ws_attn": ws_attn, "ws_acc": ws_acc}
 
 
@@ -230,6 +270,8 @@ def step_summary(w, t):
         "verified_tokens_per_s": round(w.verified_tokens / (ms * 1e-3), 1),
         "committed_tokens_per_s": round(committed / (ms * 1e-3), 1),
         "ms_per_step": round(ms, 4),
+        "step_timing": t["step_timing"],
+        "ms_per_step_with_call_events": round(float(t["step_with_call_events"].mean()), 4),
         "tokens_per_step": {"verified": int(w.verified_tokens), "committed": committed},
         "kernels_ms": {"verify_tree_attn": round(km["attn"], 4),
                        "accept_tree": round(km["accept"], 4),
@@ -760,6 +802,8 @@ def main():
         "unit": "verified tree tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_timing": summ["step_timing"],
+        "ms_per_step_with_call_events": summ["ms_per_step_with_call_events"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.kv_dtype == "bf16" else "f32",
         "data": "synthetic",
