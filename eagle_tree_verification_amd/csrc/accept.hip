@@ -754,6 +754,10 @@ __device__ bool filter_threshold(const AcceptArgs& a, int bl, int part, int& gen
   }
 }
 
+// Read in place of a per-sequence array the call does not pass.
+__device__ const int32_t kZeroI32 = 0;
+__device__ const float kZeroF32 = 0.f;
+
 // FILT: the sampling filters are compiled in (the variant used when the call
 // passes top_k or top_p); without it every q is unfiltered.
 template <int NG, int W, bool MAPPED, bool FILT>
@@ -797,16 +801,28 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   const int hi = min(a.V, lo + a.chunk);
   const bool writer0 = (part == 0);
 
+  // Every per-sequence value the prologue checks, and the tree rows, are
+  // requested at once, before the table is built: the loads are
+  // unconditional (a missing array reads a zero word instead), so none waits
+  // for another.
+  const int n = a.n_nodes[b];
+  const float T_b = *(a.temps ? a.temps + b : &kZeroF32);
+  const int k_b = *(FILT && a.top_k ? a.top_k + b : &kZeroI32);
+  const float p_b = *(FILT && a.top_p ? a.top_p + b : &kZeroF32);
+  const int bad_map = *(MAPPED ? a.t2d_bad : &kZeroI32);
+  const size_t tree_row = (size_t)b * a.n_max + (tid < a.n_max ? tid : a.n_max - 1);
+  const int par_b = a.parents[tree_row];
+  const int tok_b = a.tokens[tree_row];
+
   for (int j = tid; j < kTab; j += NT)
     s_tab[j] = 2.0 * exp_nonpos((double)(j - kTab) / kTab * 0.6931471805599453);
 
   // ---- validation (identical in every workgroup of the sequence) ----------
-  const int n = a.n_nodes[b];
   int err = 0;
   bool greedy = a.greedy;
   double invT = a.inv_T;
   if (a.temps) {  // this sequence's temperature
-    const float T = a.temps[b];
+    const float T = T_b;
     if (!(T >= 0.f) || !isfinite(T)) err = SPEC_DEVERR_NONFINITE;
     greedy = T == 0.f;
     invT = greedy ? 0.0 : 1.0 / (double)T;
@@ -814,15 +830,15 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   int fk = 0;          // top-k, 0 = off
   uint64_t fP = 0;     // top-p in units of 2^-47, 0 = off
   if (FILT && a.top_k) {
-    const int k = a.top_k[b];
+    const int k = k_b;
     if (k > 0 && k < a.V) fk = k;
   }
   if (FILT && a.top_p) {
-    const float pp = a.top_p[b];
+    const float pp = p_b;
     if (pp != pp) err = SPEC_DEVERR_NONFINITE;
     else if (pp > 0.f && pp < 1.f) fP = max((uint64_t)((double)pp * kMassOne), (uint64_t)1);
   }
-  if (MAPPED && *a.t2d_bad) err = SPEC_DEVERR_TOKEN;
+  if (MAPPED && bad_map) err = SPEC_DEVERR_TOKEN;
   if (err) {
     // a bad temperature, top-p or draft map: nothing else is checked
   } else if (n < 1 || n > a.n_max) {
@@ -830,8 +846,8 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   } else {
     int bad_tree = 0, bad_tok = 0;
     if (tid < n) {
-      const int p = a.parents[(size_t)b * a.n_max + tid];
-      const int tk = a.tokens[(size_t)b * a.n_max + tid];
+      const int p = par_b;
+      const int tk = tok_b;
       s_par[tid] = p;
       s_tok[tid] = tk;
       if (tid == 0) {
