@@ -158,6 +158,7 @@ struct AcceptArgs {
   uint64_t* hist;         // [B][2][KP][512] tagged histogram words
   int32_t* dev_error;
   int spin_limit;
+  uint32_t* seq_epoch;    // [B] per-sequence launch counters (workspace), see walk_epoch
 };
 
 // ---- wave-uniform values ------------------------------------------------------
@@ -309,10 +310,10 @@ __device__ void block_argmax(float& v, int& i, double* red) {
 __device__ __forceinline__ int block_or(int f, int*) { return __syncthreads_or(f); }
 
 // ---- inter-workgroup exchange ---------------------------------------------
-// Tag of exchange number gen of this launch: 32 bits of launch id, 16 of
-// exchange number (a walk makes well under 2^16 exchanges), 48 bits in all.
-__device__ __forceinline__ uint64_t exchange_tag(const AcceptArgs& a, int gen) {
-  return ((a.epoch & 0xFFFFFFFFull) << 16) | (uint64_t)(gen & 0xffff);
+// Tag of exchange number gen: 32 bits of launch id, 16 of exchange number (a
+// walk makes well under 2^16 exchanges), 48 bits in all.
+__device__ __forceinline__ uint64_t exchange_tag(uint32_t ep, int gen) {
+  return ((uint64_t)ep << 16) | (uint64_t)(gen & 0xffff);
 }
 
 // Publishes this workgroup's two partials and gathers all KP workgroups'
@@ -324,8 +325,8 @@ __device__ __forceinline__ uint64_t exchange_tag(const AcceptArgs& a, int gen) {
 // nothing to clear between calls.  Slots alternate between two buffers; a
 // workgroup reuses a buffer only after every workgroup has published the next
 // exchange, which each does only after reading this one.
-__device__ bool exchange(const AcceptArgs& a, int bl, int part, int& gen, double v0, double v1,
-                         double (*xs)[2], int* s_or) {
+__device__ bool exchange(const AcceptArgs& a, uint32_t ep, int bl, int part, int& gen, double v0,
+                         double v1, double (*xs)[2], int* s_or) {
   const int t = threadIdx.x;
   __syncthreads();  // xs of the previous exchange is no longer read
   if (a.KP == 1) {
@@ -336,7 +337,7 @@ __device__ bool exchange(const AcceptArgs& a, int bl, int part, int& gen, double
     __syncthreads();
     return true;
   }
-  const uint64_t tag = exchange_tag(a, gen);
+  const uint64_t tag = exchange_tag(ep, gen);
   uint64_t* slot = a.slots + ((size_t)bl * 2 + (gen & 1)) * (size_t)a.KP * 8;
   ++gen;
   if (t < 8) {
@@ -377,7 +378,13 @@ __device__ bool exchange(const AcceptArgs& a, int bl, int part, int& gen, double
     if (i < nw && (i & 3) == 0)
       xs[i >> 3][(i >> 2) & 1] = __longlong_as_double((long long)(p0 | (p1 << 16) | (p2 << 32) | (p3 << 48)));
   }
-  return !block_or(bad, s_or);
+  const bool ok = !block_or(bad, s_or);
+  // Every workgroup of the sequence has published its first word, so has
+  // read the sequence's launch counter: the next launch may advance it.
+  if (ok && gen == 1 && part == 0 && t == 0)
+    __hip_atomic_store(a.seq_epoch + a.b0 + bl, ep - (uint32_t)a.epoch + 1u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  return ok;
 }
 
 __device__ void log_tie(const AcceptArgs& a, int b, int node, int kind, float u, double margin) {
@@ -574,7 +581,7 @@ constexpr int kCopies = 4;
 // of its threads holds more than this many; otherwise it streams its slices.
 constexpr int kMaskMax = 2;
 
-__device__ bool exchange_hist(const AcceptArgs& a, int bl, int part, int& gen,
+__device__ bool exchange_hist(const AcceptArgs& a, uint32_t ep, int bl, int part, int& gen,
                               const uint32_t* h_cnt, const uint64_t* h_mass, int jb,
                               uint64_t& cnt, uint64_t& mass, int* s_or) {
   const int t = threadIdx.x;
@@ -583,7 +590,7 @@ __device__ bool exchange_hist(const AcceptArgs& a, int bl, int part, int& gen,
     mass = h_mass[jb * kCopies];
     return true;
   }
-  const uint64_t tag = (((0x80000ull | (a.epoch & 0x7FFFFull)) << 12) | (uint64_t)(gen & 0xfff))
+  const uint64_t tag = (((0x80000ull | (ep & 0x7FFFFull)) << 12) | (uint64_t)(gen & 0xfff))
                        << 32;
   uint64_t* data = a.hist + ((size_t)bl * 2 + (gen & 1)) * (size_t)a.KP * 512;
   ++gen;
@@ -643,7 +650,7 @@ __device__ bool exchange_hist(const AcceptArgs& a, int bl, int part, int& gen,
 // to the masses above and at the threshold (in units of q), or a large
 // value when top-p cannot flip a kept token.
 template <int NG, int W, int BG>
-__device__ bool filter_threshold(const AcceptArgs& a, int bl, int part, int& gen,
+__device__ bool filter_threshold(const AcceptArgs& a, uint32_t ep, int bl, int part, int& gen,
                                  const float* lrow, int lo, int hi, double invT, double M,
                                  double S, int fk, uint64_t P, const double* tab,
                                  uint32_t* h_cnt, uint64_t* h_mass, FilterShared& fs, int* s_or,
@@ -700,7 +707,7 @@ __device__ bool filter_threshold(const AcceptArgs& a, int bl, int part, int& gen
     }
     __syncthreads();
     uint64_t cnt, mass;
-    if (!exchange_hist(a, bl, part, gen, h_cnt, h_mass, jb, cnt, mass, s_or)) return false;
+    if (!exchange_hist(a, ep, bl, part, gen, h_cnt, h_mass, jb, cnt, mass, s_or)) return false;
     // suffix sums over buckets (prefix sums over threads)
     uint64_t c = cnt, m = mass;
 #pragma unroll
@@ -813,6 +820,17 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   const size_t tree_row = (size_t)b * a.n_max + (tid < a.n_max ? tid : a.n_max - 1);
   const int par_b = a.parents[tree_row];
   const int tok_b = a.tokens[tree_row];
+  // The launch id of this sequence's exchange tags: the host's id of the
+  // launch plus the sequence's counter in the workspace, which the sequence's
+  // first workgroup advances once every workgroup has read it (after the
+  // first exchange).  A launch replayed from a captured graph repeats the
+  // host's id, and the counter still makes its tags new, so no word a
+  // previous launch left in the workspace reads as current.
+  const uint32_t ep = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)((uint32_t)a.epoch +
+            (a.KP > 1 ? __hip_atomic_load(a.seq_epoch + b, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT)
+                      : 0u)));
 
   for (int j = tid; j < kTab; j += NT)
     s_tab[j] = 2.0 * exp_nonpos((double)(j - kTab) / kTab * 0.6931471805599453);
@@ -910,7 +928,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
           });
       nf = block_or(nf, &s_or);
       block_argmax(bv, bi, red);
-      if (!exchange(a, bl, part, gen, (double)bv, nf ? -1.0 : (double)bi, xs, &s_or)) {
+      if (!exchange(a, ep, bl, part, gen, (double)bv, nf ? -1.0 : (double)bi, xs, &s_or)) {
         fail_sync(a, b, writer0);
         return;
       }
@@ -1009,7 +1027,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
     bool scan_ok = true, scan_rel = true;
     nf = block_or(nf, &s_or);
     block_lse(m, es, red);
-    if (!exchange(a, bl, part, gen, m, nf ? -1.0 : es, xs, &s_or)) {
+    if (!exchange(a, ep, bl, part, gen, m, nf ? -1.0 : es, xs, &s_or)) {
       fail_sync(a, b, writer0);
       return;
     }
@@ -1032,7 +1050,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
     bool masks = false;  // s_keep holds this row's kept entries
     if (FILT && (fk > 0 || fP > 0)) {
       double fmargin;
-      if (!filter_threshold<NG, W, BG2>(a, bl, part, gen, lrow, lo, hi, invT, M, S, fk, fP, s_tab,
+      if (!filter_threshold<NG, W, BG2>(a, ep, bl, part, gen, lrow, lo, hi, invT, M, S, fk, fP, s_tab,
                                         reinterpret_cast<uint32_t*>(&scan[4][0]),
                                         reinterpret_cast<uint64_t*>(&scan[0][0]), fsh, &s_or, lcut,
                                         fmargin)) {
@@ -1063,7 +1081,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       masks = true;
       scan_rel = false;  // the filter's histograms overwrote scan; it now holds kept sums
       ek = block_sum(ek, red);
-      if (!exchange(a, bl, part, gen, ek, 0.0, xs, &s_or)) {
+      if (!exchange(a, ep, bl, part, gen, ek, 0.0, xs, &s_or)) {
         fail_sync(a, b, writer0);
         return;
       }
@@ -1184,7 +1202,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       p_read = true;
       pnf = block_or(pnf, &s_or);
       zp = block_sum(zp, red);
-      if (!exchange(a, bl, part, gen, zp, (double)pnf, xs, &s_or)) {
+      if (!exchange(a, ep, bl, part, gen, zp, (double)pnf, xs, &s_or)) {
         fail_sync(a, b, writer0);
         return;
       }
@@ -1453,8 +1471,9 @@ struct AcceptPlan {
   int NG = 1;      // element groups per thread
   int W = 1;       // entries per group: 4 when rows allow 16-byte loads
   int chunk = 0;   // entries per workgroup
-  size_t ws = 0;   // workspace bytes: exchange words | inverse draft map | histograms
-  size_t off_t2d = 0, off_hist = 0;
+  size_t ws = 0;   // workspace bytes: exchange words | inverse draft map | histograms |
+                   // per-sequence launch counters
+  size_t off_t2d = 0, off_hist = 0, off_seq = 0;
 };
 
 // Workgroups of the (W, NG) variant one compute unit holds at once, cached
@@ -1520,6 +1539,10 @@ AcceptPlan make_accept_plan(int B, int V, bool mapped = false, bool filters = fa
   if (filters && p.KP > 1) {
     p.off_hist = align(p.ws);
     p.ws = p.off_hist + (size_t)B * 2 * p.KP * 512 * sizeof(uint64_t);
+  }
+  if (p.KP > 1) {
+    p.off_seq = align(p.ws);
+    p.ws = p.off_seq + (size_t)B * sizeof(uint32_t);
   }
   return p;
 }
@@ -1589,6 +1612,8 @@ extern "C" spec_status_t spec_accept_tree_ex(
   a.KP = p.KP;
   a.chunk = p.chunk;
   a.slots = static_cast<uint64_t*>(workspace);
+  a.seq_epoch = p.KP > 1 ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + p.off_seq)
+                         : nullptr;
   a.dev_error = dev_error;
   // bound on the polls of one inter-workgroup wait; tests set a negative
   // bound, which makes every wait give up at once, to drive the failure path

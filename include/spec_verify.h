@@ -241,8 +241,11 @@ spec_status_t spec_tree_kv_write(const void* k_new, const void* v_new, void* k_c
  *   workspace              >= spec_accept_tree_workspace_size(...) bytes of
  *                          device memory; needs no initialisation (the words
  *                          workgroups exchange through it carry a per-launch
- *                          tag); calls sharing one workspace must be ordered
- *                          on one stream
+ *                          tag, made of the host's launch id and a
+ *                          per-sequence counter the walk advances in the
+ *                          workspace, so replays of a call captured in a HIP
+ *                          graph are tagged afresh too); calls sharing one
+ *                          workspace must be ordered on one stream
  * Device errors: SPEC_DEVERR_TREE, _TOKEN, _NONFINITE, _SYNC.
  * The workgroups that share one sequence's vocabulary exchange partial sums
  * and must be resident together; the call sizes its launch so that they are

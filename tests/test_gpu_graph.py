@@ -3,11 +3,15 @@
 The library's calls launch kernels only (no memset, no allocation, no host
 synchronisation), so a caller can capture a whole step.  Each case captures
 attention, the acceptance walk and the commit once, then replays the graph
-three times; before every replay the inputs (caches, lengths) are restored
-by eager copies and an eager call of the walk runs on the same stream, and
-after every replay every output (attention rows, walk outputs, committed
-caches and lengths, tie records) must equal the eagerly issued step's bit for
-bit.  The eager step itself is checked against the oracle.
+three times, each time on new uniforms (and so new walks): before every
+replay the caches and lengths are restored and the new uniforms copied in by
+eager copies, the eagerly issued step on the same inputs gives the
+reference, and an eager call of the walk runs on the same stream; after
+every replay every output (attention rows, walk outputs, committed caches
+and lengths, tie records) must equal the eager step's bit for bit.  A replay
+repeats the host's launch ids, so this also shows that no exchange word a
+previous launch left in the workspace is taken for a current one.  The
+eager steps are checked against the oracle.
 """
 import numpy as np
 import pytest
@@ -46,10 +50,17 @@ def _snapshot(bufs, res, dev):
     return snap
 
 
-@pytest.mark.parametrize("case", ["plain", "noalloc", "filters"])
+@pytest.mark.parametrize("case", ["plain", "noalloc", "filters", "tiny-trees"])
 def test_step_graph_replays_match_eager(hip_lib, case):
+    """tiny-trees: root-only and two- or three-node trees, whose walks make one
+    to three exchanges, with new logits as well as new uniforms each replay
+    (a launch whose tags repeated the previous one's could then take that
+    launch's words for its own first exchanges)."""
     api = hip_lib
-    w = make_workload(poison=True, **small_cases()["c4-mini"])
+    kw = dict(small_cases()["c4-mini"])
+    if case == "tiny-trees":
+        kw["drafts"] = [0, 1, 0, 2, 0]
+    w = make_workload(poison=True, **kw)
     dev = to_device(w)
     say(f"[gpu] graph of the verify step ({case}): B={w.B} V={w.V} n_max={w.n_max}")
     kv_dt = api.SPEC_BF16 if w.kv_dtype == "bf16" else api.SPEC_F32
@@ -82,21 +93,42 @@ def test_step_graph_replays_match_eager(hip_lib, case):
         dev["prefix_len"].copy_(len0)
         bufs["err"].zero_()
 
+    rng = np.random.default_rng(1234)
+    u_sets = [(dev["u_accept"].clone(), dev["u_sample"].clone(), dev["logits"].clone())]
+    for _ in range(3):
+        lg = w.logits
+        if case == "tiny-trees":  # the same values at other token ids
+            lg = np.ascontiguousarray(lg[:, :, rng.permutation(w.V)])
+        u_sets.append((torch.from_numpy(rng.random(w.u_accept.shape, dtype=np.float32)).cuda(),
+                       torch.from_numpy(rng.random(w.u_sample.shape, dtype=np.float32)).cuda(),
+                       torch.from_numpy(lg).cuda()))
+
+    def use(k):
+        dev["u_accept"].copy_(u_sets[k][0])
+        dev["u_sample"].copy_(u_sets[k][1])
+        dev["logits"].copy_(u_sets[k][2])
+
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
+        eager = []
+        for k in range(4):
+            restore()
+            use(k)
+            res = _step(api, w, dev, bufs, noalloc=noalloc, filters=filters)
+            torch.cuda.synchronize()
+            eager.append(_snapshot(bufs, res, dev))
+            assert int(eager[k]["err"].item()) == 0
         restore()
-        res = _step(api, w, dev, bufs, noalloc=noalloc, filters=filters)
-        torch.cuda.synchronize()
-        eager = _snapshot(bufs, res, dev)
-        assert int(eager["err"].item()) == 0
-        restore()
+        use(0)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
             gres = _step(api, w, dev, bufs, noalloc=noalloc, filters=filters)
         torch.cuda.synchronize()
-        for r in range(3):
+        changed = 0
+        for r in range(1, 4):
             restore()
+            use(r)
             # the program's own eager work between replays: a walk on the same stream
             api.accept_tree(dev["tokens"], dev["parents"], dev["n_nodes"], dev["draft_p"],
                             dev["logits"], w.T, dev["u_accept"], dev["u_sample"], w.max_depth,
@@ -105,21 +137,25 @@ def test_step_graph_replays_match_eager(hip_lib, case):
             g.replay()
             torch.cuda.synchronize()
             got = _snapshot(bufs, gres, dev)
-            for key, ref in eager.items():
+            ref = eager[r]
+            for key, val in ref.items():
                 if key == "tie_log":  # records append in any order: compared as sets below
                     continue
                 # bytes, so that the NaN the poisoned cache rows hold compare equal
                 assert torch.equal(got[key].contiguous().view(torch.uint8),
-                                   ref.contiguous().view(torch.uint8)), (
-                    f"replay {r}: {key} differs from the eager step")
+                                   val.contiguous().view(torch.uint8)), (
+                    f"replay {r}: {key} differs from the eager step on the same inputs")
             tie_key = lambda t: (int(t["b"]), int(t["node"]), int(t["kind"]))
             assert (sorted(map(tie_key, api.decode_ties(got["tie_log"], got["tie_count"])))
-                    == sorted(map(tie_key, api.decode_ties(eager["tie_log"], eager["tie_count"]))))
+                    == sorted(map(tie_key, api.decode_ties(ref["tie_log"], ref["tie_count"]))))
+            changed += not torch.equal(ref["out_tokens"], eager[r - 1]["out_tokens"])
             say(f"[gpu]   replay {r}: every output equals the eager step's")
+        assert changed >= 2, "the new uniforms should change the walks"
 
-    host = {k: eager[k].cpu().numpy() for k in ("accept_len", "path", "out_tokens", "n_out",
-                                                "final_dist")}
-    host["ties"] = api.decode_ties(eager["tie_log"], eager["tie_count"])
+    # the eager step on the workload's own uniforms against the oracle
+    host = {key: eager[0][key].cpu().numpy() for key in ("accept_len", "path", "out_tokens",
+                                                         "n_out", "final_dist")}
+    host["ties"] = api.decode_ties(eager[0]["tie_log"], eager[0]["tie_count"])
     if filters is None:
         compare_accept(w, host)
-    compare_attention(w, eager["out"].cpu().numpy())
+    compare_attention(w, eager[0]["out"].cpu().numpy())
