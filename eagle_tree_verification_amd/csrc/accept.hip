@@ -259,20 +259,19 @@ __device__ double block_sum(double v, double* red) {
 __device__ void block_lse(double& m, double& s, double* red) {
   const double wm = wave_max_d(m);
   const double ts = wave_sum_d(m == -INFINITY ? 0.0 : s * exp_nonpos(m - wm));
-  const int wv = threadIdx.x >> 6;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) {
+  if (lane == 0) {
     red[2 * wv] = wm;
     red[2 * wv + 1] = ts;
   }
   __syncthreads();
-  double mm = -INFINITY;
-#pragma unroll
-  for (int k = 0; k < NT / 64; ++k) mm = fmax(mm, red[2 * k]);
-  double ss = 0.0;
-#pragma unroll
-  for (int k = 0; k < NT / 64; ++k)
-    if (red[2 * k] != -INFINITY) ss += red[2 * k + 1] * exp_nonpos(red[2 * k] - mm);
+  // the waves' partials combined across lanes (lane k takes wave k's), so the
+  // rescaling exponentials run side by side rather than one after another
+  const bool has = lane < NT / 64;
+  const double km = has ? red[2 * lane] : -INFINITY;
+  const double mm = wave_max_d(km);
+  const double ss = wave_sum_d(has && km != -INFINITY ? red[2 * lane + 1] * exp_nonpos(km - mm) : 0.0);
   m = mm;
   s = ss;
 }
