@@ -256,9 +256,9 @@ __device__ double block_sum(double v, double* red) {
 // Combines per-thread (max, sum of exp relative to max) over the workgroup:
 // one wave max, one rescale per lane, one wave sum, then the NT / 64 wave
 // results.
-__device__ void block_lse(double& m, double& s, double* red) {
+__device__ void block_lse(double& m, double& s, double* red, const double* tab) {
   const double wm = wave_max_d(m);
-  const double ts = wave_sum_d(m == -INFINITY ? 0.0 : s * exp_nonpos(m - wm));
+  const double ts = wave_sum_d(m == -INFINITY ? 0.0 : s * exp_tab(m - wm, tab));
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   __syncthreads();
   if (lane == 0) {
@@ -271,7 +271,7 @@ __device__ void block_lse(double& m, double& s, double* red) {
   const bool has = lane < NT / 64;
   const double km = has ? red[2 * lane] : -INFINITY;
   const double mm = wave_max_d(km);
-  const double ss = wave_sum_d(has && km != -INFINITY ? red[2 * lane + 1] * exp_nonpos(km - mm) : 0.0);
+  const double ss = wave_sum_d(has && km != -INFINITY ? red[2 * lane + 1] * exp_tab(km - mm, tab) : 0.0);
   m = mm;
   s = ss;
 }
@@ -1025,7 +1025,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
     // scan holds this node's sums of exp(z - M) once rescaled by mref
     bool scan_ok = true, scan_rel = true;
     nf = block_or(nf, &s_or);
-    block_lse(m, es, red);
+    block_lse(m, es, red, s_tab);
     if (!exchange(a, ep, bl, part, gen, m, nf ? -1.0 : es, xs, &s_or)) {
       fail_sync(a, b, writer0);
       return;
@@ -1039,7 +1039,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       return;
     }
     const double M = uni(wave_max_d(pm));
-    double pterm = (has && pm != -INFINITY) ? ps * exp_nonpos(pm - M) : 0.0;
+    double pterm = (has && pm != -INFINITY) ? ps * exp_tab(pm - M, s_tab) : 0.0;
     double S = uni(wave_sum_d(pterm));
 
     // ---- sampling filters: threshold, then the kept mass per slice ----------
@@ -1133,13 +1133,20 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
         nxt = c;
         break;
       }
-      const double qx = kept(s_kl[c]) ? exp_nonpos((double)s_kl[c] * invT - M) / S : 0.0;
-      const double cur = fmax(0.0, qx - C * px) / Z;
-      const double thr = fmin(1.0, cur / px);
+      // u < min(1, cur / px), cur = max(0, exp(z - M) / S - C px) / Z, tested
+      // without divisions as u px Z S < max(0, exp(z - M) - C px S) (u < 1);
+      // the ratio itself is formed only for a near tie's record
+      const double e = kept(s_kl[c]) ? exp_tab((double)s_kl[c] * invT - M, s_tab) : 0.0;
+      const double pzs = px * Z * S;
+      const double rhs = fmax(0.0, e - C * px * S);
       const float uf = s_ku[c];
       const double u = (double)uf;
-      if (writer0 && tid == 0 && fabs(u - thr) < kTieBand) log_tie(a, b, c, 0, uf, fabs(u - thr));
-      if (u < thr) {
+      const double lhs = u * pzs;
+      if (writer0 && tid == 0 && fabs(lhs - fmin(rhs, pzs)) < 2.0 * kTieBand * pzs) {
+        const double thr = fmin(1.0, rhs / pzs);
+        if (fabs(u - thr) < kTieBand) log_tie(a, b, c, 0, uf, fabs(u - thr));
+      }
+      if (lhs < rhs) {
         nxt = c;
         break;
       }
