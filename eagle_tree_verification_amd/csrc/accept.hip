@@ -972,20 +972,25 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
 
     // What the child tests and the terminal sample read, loaded now so that
     // the loads overlap the statistics pass.
+    // The loads are unconditional, at indices valid for every thread (token 0
+    // and row 0 where the thread holds no child); only the children's values
+    // are used.  Loads under a branch would be waited for at once.
     const bool kid = tid > v && tid < n && s_par[tid] == v;
-    float k_p = 0.f, k_l = 0.f, k_u = 0.f, k_us = 0.f;
-    if (kid) {
-      const int xt = s_tok[tid];
+    float k_p = 0.f, k_l, k_u, k_us;
+    {
+      const int xt = kid ? s_tok[tid] : 0;
       if constexpr (MAPPED) {
-        const int dx = a.t2d[xt];
-        k_p = dx >= 0 ? prow[dx] : 0.f;
+        if (kid) {
+          const int dx = a.t2d[xt];
+          k_p = dx >= 0 ? prow[dx] : 0.f;
+        }
       } else {
         k_p = prow[xt];
       }
       k_l = lrow[xt];
-      k_u = a.u_accept[rows_b + tid];
+      k_u = a.u_accept[rows_b + (tid < a.n_max ? tid : 0)];
+      k_us = a.u_sample[rows_b + v];
     }
-    if (tid == 0) k_us = a.u_sample[rows_b + v];
 
     // ---- T > 0: max and sum of exp(z) over the slice, online per batch ----
     double m = -INFINITY, es = 0.0;
