@@ -496,11 +496,53 @@ __device__ __forceinline__ void load_group_p(const float* row, const int32_t* t2
   else load_group<W>(row, lo, hi, g, fill, x);
 }
 
+// Group g as load_group_p loads it, without the fill: entries past `hi` hold
+// what the clamped load returned until fill_batch replaces them.
+template <int W, bool MAPPED>
+__device__ __forceinline__ void load_group_raw(const float* row, const int32_t* t2d, int lo,
+                                               int hi, int g, float* x) {
+  const int i = elem_index<W>(lo, g * W);
+  const int ic = i < hi ? i : hi - W;
+  if (W == 4) {
+    if constexpr (MAPPED) {
+      const int4 t = *reinterpret_cast<const int4*>(t2d + ic);
+      const float p0 = row[max(t.x, 0)], p1 = row[max(t.y, 0)];
+      const float p2 = row[max(t.z, 0)], p3 = row[max(t.w, 0)];
+      x[0] = t.x >= 0 ? p0 : 0.f;
+      x[1] = t.y >= 0 ? p1 : 0.f;
+      x[2] = t.z >= 0 ? p2 : 0.f;
+      x[3] = t.w >= 0 ? p3 : 0.f;
+    } else {
+      const float4 f = *reinterpret_cast<const float4*>(row + ic);
+      x[0] = f.x;
+      x[1] = f.y;
+      x[2] = f.z;
+      x[3] = f.w;
+    }
+  } else {
+    if constexpr (MAPPED) {
+      const int t = t2d[ic];
+      const float p = row[max(t, 0)];
+      x[0] = t >= 0 ? p : 0.f;
+    } else {
+      x[0] = row[ic];
+    }
+  }
+}
+
+// Sets the entries of groups g0 .. g0+BG-1 that lie past `hi` to `fill`.  The
+// last entry any thread holds in the batch is lo + (g0 + BG) * NT * W - 1, so
+// a batch wholly inside the slice (the same answer for every thread: one
+// scalar branch) keeps its loaded values without a select per entry.
 template <int W, int BG>
-__device__ __forceinline__ void load_batch(const float* row, int lo, int hi, int g0, float fill,
-                                           float (*xv)[W]) {
+__device__ __forceinline__ void fill_batch(int lo, int hi, int g0, float fill, float (*xv)[W]) {
+  if (lo + (g0 + BG) * NT * W <= hi) return;
 #pragma unroll
-  for (int gb = 0; gb < BG; ++gb) load_group<W>(row, lo, hi, g0 + gb, fill, xv[gb]);
+  for (int gb = 0; gb < BG; ++gb) {
+    const bool ok = elem_index<W>(lo, (g0 + gb) * W) < hi;
+#pragma unroll
+    for (int j = 0; j < W; ++j) xv[gb][j] = ok ? xv[gb][j] : fill;
+  }
 }
 
 // Streams this thread's NG groups of a row slice (two rows when R2) through
@@ -512,21 +554,27 @@ __device__ __forceinline__ void stream_slice(const float* r1, float f1, const fl
                                              int lo, int hi, F body,
                                              const int32_t* t2d = nullptr) {
   float xa[BG][W], xb[BG][W], ya[BG][W], yb[BG][W];
-  auto load2 = [&](int g0, float (*y)[W]) {
+  auto load = [&](int g0, float (*x)[W], float (*y)[W]) {
 #pragma unroll
-    for (int gb = 0; gb < BG; ++gb) load_group_p<W, MAPPED>(r2, t2d, lo, hi, g0 + gb, f2, y[gb]);
+    for (int gb = 0; gb < BG; ++gb) load_group_raw<W, false>(r1, nullptr, lo, hi, g0 + gb, x[gb]);
+    if (R2) {
+#pragma unroll
+      for (int gb = 0; gb < BG; ++gb) load_group_raw<W, MAPPED>(r2, t2d, lo, hi, g0 + gb, y[gb]);
+    }
   };
-  load_batch<W, BG>(r1, lo, hi, 0, f1, xa);
-  if (R2) load2(0, ya);
+  auto run = [&](int g0, float (*x)[W], float (*y)[W]) {
+    fill_batch<W, BG>(lo, hi, g0, f1, x);
+    if (R2) fill_batch<W, BG>(lo, hi, g0, f2, y);
+    body(g0, x, y);
+  };
+  load(0, xa, ya);
 #pragma unroll 1
   for (int g0 = 0; g0 < NG; g0 += 2 * BG) {
-    load_batch<W, BG>(r1, lo, hi, g0 + BG, f1, xb);
-    if (R2) load2(g0 + BG, yb);
-    body(g0, xa, ya);
+    load(g0 + BG, xb, yb);
+    run(g0, xa, ya);
     if (g0 + BG >= NG) break;
-    load_batch<W, BG>(r1, lo, hi, g0 + 2 * BG, f1, xa);
-    if (R2) load2(g0 + 2 * BG, ya);
-    body(g0 + BG, xb, yb);
+    load(g0 + 2 * BG, xa, ya);
+    run(g0 + BG, xb, yb);
   }
 }
 
@@ -1020,9 +1068,11 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
           mref[g0 / BG1][tid] = m;
 #pragma unroll
           for (int gb = 0; gb < BG1; ++gb) {
-            double sg = 0.0;
+            // the terms are +0 or positive, so starting from the first one
+            // gives the same sum as starting from 0
+            double sg = exp_tab(fma((double)xv[gb][0], invT, -m), s_tab);
 #pragma unroll
-            for (int j = 0; j < W; ++j) sg += exp_tab(fma((double)xv[gb][j], invT, -m), s_tab);
+            for (int j = 1; j < W; ++j) sg += exp_tab(fma((double)xv[gb][j], invT, -m), s_tab);
             es += sg;
             scan[g0 + gb][tid] = sg;
           }
