@@ -151,7 +151,7 @@ struct AcceptArgs {
   int b0;       // first sequence of this launch
   int KP;       // workgroups per sequence
   int chunk;    // vocabulary entries per workgroup (NT * W * NG)
-  uint64_t* slots;  // [group size][2][KP][8] tagged exchange words
+  uint64_t* slots;  // [group size][2][KP][16] tagged exchange words
   uint64_t epoch;   // launch id (32 bits), part of every exchange tag
   const int32_t* top_k;   // per-sequence top-k (<= 0 or >= V: off), or null
   const float* top_p;     // per-sequence top-p (<= 0 or >= 1: off), or null
@@ -311,6 +311,8 @@ __device__ __forceinline__ int block_or(int f, int*) { return __syncthreads_or(f
 // ---- inter-workgroup exchange ---------------------------------------------
 // Tag of exchange number gen: 32 bits of launch id, 16 of exchange number (a
 // walk makes well under 2^16 exchanges), 48 bits in all.
+constexpr int kSlotWords = 16;  // exchange words per workgroup and buffer
+
 __device__ __forceinline__ uint64_t exchange_tag(uint32_t ep, int gen) {
   return ((uint64_t)ep << 16) | (uint64_t)(gen & 0xffff);
 }
@@ -321,7 +323,8 @@ __device__ __forceinline__ uint64_t exchange_tag(uint32_t ep, int gen) {
 // device-coherent 64-bit atomic accesses.  A word is valid once its tag is
 // current, whatever order the words arrive in, so the readers poll the data
 // itself: one memory round trip per exchange, with no counter, no fence and
-// nothing to clear between calls.  Slots alternate between two buffers; a
+// nothing to clear between calls.  Slots alternate between two buffers (16
+// words per workgroup each, room for exchange4's four partials); a
 // workgroup reuses a buffer only after every workgroup has published the next
 // exchange, which each does only after reading this one.
 __device__ bool exchange(const AcceptArgs& a, uint32_t ep, int bl, int part, int& gen, double v0,
@@ -337,12 +340,12 @@ __device__ bool exchange(const AcceptArgs& a, uint32_t ep, int bl, int part, int
     return true;
   }
   const uint64_t tag = exchange_tag(ep, gen);
-  uint64_t* slot = a.slots + ((size_t)bl * 2 + (gen & 1)) * (size_t)a.KP * 8;
+  uint64_t* slot = a.slots + ((size_t)bl * 2 + (gen & 1)) * (size_t)a.KP * kSlotWords;
   ++gen;
   if (t < 8) {
     const uint64_t bits = (uint64_t)__double_as_longlong(t < 4 ? v0 : v1);
     const uint64_t w = (tag << 16) | ((bits >> (16 * (t & 3))) & 0xffffull);
-    __hip_atomic_store(slot + part * 8 + t, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(slot + part * kSlotWords + t, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const int nw = a.KP * 8;
   int bad = 0;
@@ -353,7 +356,9 @@ __device__ bool exchange(const AcceptArgs& a, uint32_t ep, int bl, int part, int
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
     const int i = t + r * NT;  // word i: part i / 8, value (i / 4) % 2, bits 16 (i % 4)
-    w[r] = i < nw ? __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+    w[r] = i < nw ? __hip_atomic_load(slot + (i >> 3) * kSlotWords + (i & 7), __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT)
+                  : 0;
   }
 #pragma unroll
   for (int r = 0; r < kRounds; ++r) {
@@ -366,7 +371,8 @@ __device__ bool exchange(const AcceptArgs& a, uint32_t ep, int bl, int part, int
           break;
         }
         __builtin_amdgcn_s_sleep(1);
-        w[r] = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        w[r] = __hip_atomic_load(slot + (i >> 3) * kSlotWords + (i & 7), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     // the four words of one value sit in four consecutive lanes
@@ -376,6 +382,78 @@ __device__ bool exchange(const AcceptArgs& a, uint32_t ep, int bl, int part, int
     const uint64_t p3 = __shfl_down(p0, 3);
     if (i < nw && (i & 3) == 0)
       xs[i >> 3][(i >> 2) & 1] = __longlong_as_double((long long)(p0 | (p1 << 16) | (p2 << 32) | (p3 << 48)));
+  }
+  const bool ok = !block_or(bad, s_or);
+  // Every workgroup of the sequence has published its first word, so has
+  // read the sequence's launch counter: the next launch may advance it.
+  if (ok && gen == 1 && part == 0 && t == 0)
+    __hip_atomic_store(a.seq_epoch + a.b0 + bl, ep - (uint32_t)a.epoch + 1u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  return ok;
+}
+
+// exchange() for four partials (a statistics pass that also covers a node's
+// first child): the same tagged words, 16 per workgroup.
+__device__ bool exchange4(const AcceptArgs& a, uint32_t ep, int bl, int part, int& gen,
+                          double v0, double v1, double v2, double v3, double (*xs)[4],
+                          int* s_or) {
+  constexpr int NV = 4;
+  constexpr int kWords = 4 * NV;  // words per workgroup
+  const int t = threadIdx.x;
+  __syncthreads();  // xs of the previous exchange is no longer read
+  if (a.KP == 1) {
+    if (t == 0) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) xs[0][k] = k == 0 ? v0 : k == 1 ? v1 : k == 2 ? v2 : v3;
+    }
+    __syncthreads();
+    return true;
+  }
+  const uint64_t tag = exchange_tag(ep, gen);
+  uint64_t* slot = a.slots + ((size_t)bl * 2 + (gen & 1)) * (size_t)a.KP * kSlotWords;
+  ++gen;
+  if (t < kWords) {
+    const int k = t >> 2;
+    const double x = k == 0 ? v0 : k == 1 ? v1 : k == 2 ? v2 : v3;
+    const uint64_t bits = (uint64_t)__double_as_longlong(x);
+    const uint64_t w = (tag << 16) | ((bits >> (16 * (t & 3))) & 0xffffull);
+    __hip_atomic_store(slot + part * kSlotWords + t, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const int nw = a.KP * kWords;
+  int bad = 0;
+  // every word this thread reads is requested at once, then re-polled until
+  // its tag is current: one memory round trip when the words are there
+  constexpr int kRounds = (SPEC_MAX_NODES * kWords + NT - 1) / NT;
+  uint64_t w[kRounds];
+  // word i: part i / kWords, value (i / 4) % NV, bits 16 (i % 4)
+  auto addr = [&](int i) { return slot + (i / kWords) * kSlotWords + i % kWords; };
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int i = t + r * NT;
+    w[r] = i < nw ? __hip_atomic_load(addr(i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+  }
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int i = t + r * NT;
+    if (i < nw) {
+      int spins = 0;
+      while (a.spin_limit < 0 || (w[r] >> 16) != tag) {
+        if (a.spin_limit < 0 || ++spins > a.spin_limit) {  // a negative bound: test hook
+          bad = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        w[r] = __hip_atomic_load(addr(i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    // the four words of one value sit in four consecutive lanes
+    const uint64_t p0 = w[r] & 0xffffull;
+    const uint64_t p1 = __shfl_down(p0, 1);
+    const uint64_t p2 = __shfl_down(p0, 2);
+    const uint64_t p3 = __shfl_down(p0, 3);
+    if (i < nw && (i & 3) == 0)
+      xs[i / kWords][(i >> 2) % NV] =
+          __longlong_as_double((long long)(p0 | (p1 << 16) | (p2 << 32) | (p3 << 48)));
   }
   const bool ok = !block_or(bad, s_or);
   // Every workgroup of the sequence has published its first word, so has
@@ -575,6 +653,37 @@ __device__ __forceinline__ void stream_slice(const float* r1, float f1, const fl
     if (g0 + BG >= NG) break;
     load(g0 + 2 * BG, xa, ya);
     run(g0 + BG, xb, yb);
+  }
+}
+
+// One batch of a statistics pass over a row: the running max m of z = x / T
+// and the sum es of exp(z - m) over the slice's entries (those past the slice
+// hold -inf); nf flags a non-finite entry of the slice.
+template <int W, int BG>
+__device__ __forceinline__ void batch_stats(int lo, int hi, int g0, const float (*xv)[W],
+                                            double invT, double& m, double& es, int& nf,
+                                            const double* tab) {
+  float bmax = -INFINITY;
+#pragma unroll
+  for (int gb = 0; gb < BG; ++gb)
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      const bool valid = elem_index<W>(lo, (g0 + gb) * W + j) < hi;
+      nf |= valid && !isfinite(xv[gb][j]);
+      bmax = fmaxf(bmax, xv[gb][j]);
+    }
+  if (bmax == -INFINITY) return;  // nothing valid in this batch
+  const double zb = (double)bmax * invT;
+  if (zb > m) {
+    es *= exp_tab(m - zb, tab);  // m = -inf: es is still 0
+    m = zb;
+  }
+#pragma unroll
+  for (int gb = 0; gb < BG; ++gb) {
+    double sg = exp_tab(fma((double)xv[gb][0], invT, -m), tab);
+#pragma unroll
+    for (int j = 1; j < W; ++j) sg += exp_tab(fma((double)xv[gb][j], invT, -m), tab);
+    es += sg;
   }
 }
 
@@ -828,6 +937,9 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   __shared__ double red[2 * (NT / 64)];
   __shared__ double xs[SPEC_MAX_NODES][2];
   __shared__ double cur_sums[SPEC_MAX_NODES];
+  constexpr bool LOOK = !FILT && NG <= 2;  // first-child statistics in the parent's pass
+  __shared__ double la_sums[LOOK ? SPEC_MAX_NODES : 1];  // first child's slice masses
+  __shared__ double xs4[LOOK ? SPEC_MAX_NODES : 1][4];   // partials of exchange4
   // also the filters' histograms: [256][kCopies] uint64 masses in rows 0-3,
   // [256][kCopies] uint32 counts in rows 4-5
   __shared__ double scan[FILT && NG < 6 ? 6 : (NG < 2 ? 2 : NG)][NT];
@@ -951,6 +1063,13 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   int gen = 0;
   int v = 0, depth = 0;
   if (tid == 0) s_path[0] = 0;
+  // Statistics of node la_node (max, sum and slice masses of its q), computed
+  // in its parent's pass: the first child is the one most often accepted.
+  // Worth it for short slices (NG <= 2), whose passes are bound by latency
+  // rather than by the float64 work or HBM, and not with the filters.
+  int la_node = -1;
+  double la_M = 0.0, la_S = 0.0;
+  bool la_nf = false;
   const size_t rows_b = (size_t)b * a.n_max;
 
   for (;;) {
@@ -1040,62 +1159,119 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       k_us = a.u_sample[rows_b + v];
     }
 
-    // ---- T > 0: max and sum of exp(z) over the slice, online per batch ----
-    double m = -INFINITY, es = 0.0;
-    int nf = 0;
-    stream_slice<NG, W, BG1, false>(lrow, -INFINITY, lrow, 0.f, lo, hi,
-        [&](int g0, float (*xv)[W], float (*)[W]) {
-          float bmax = -INFINITY;
-#pragma unroll
-          for (int gb = 0; gb < BG1; ++gb)
-#pragma unroll
-            for (int j = 0; j < W; ++j) {
-              const bool valid = elem_index<W>(lo, (g0 + gb) * W + j) < hi;
-              nf |= valid && !isfinite(xv[gb][j]);
-              bmax = fmaxf(bmax, xv[gb][j]);
-            }
-          if (bmax == -INFINITY) {  // nothing valid in this batch
-#pragma unroll
-            for (int gb = 0; gb < BG1; ++gb) scan[g0 + gb][tid] = 0.0;
-            mref[g0 / BG1][tid] = -INFINITY;
-            return;
-          }
-          const double zb = (double)bmax * invT;
-          if (zb > m) {
-            es *= exp_tab(m - zb, s_tab);  // m = -inf: es is still 0
-            m = zb;
-          }
-          mref[g0 / BG1][tid] = m;
-#pragma unroll
-          for (int gb = 0; gb < BG1; ++gb) {
-            // the terms are +0 or positive, so starting from the first one
-            // gives the same sum as starting from 0
-            double sg = exp_tab(fma((double)xv[gb][0], invT, -m), s_tab);
-#pragma unroll
-            for (int j = 1; j < W; ++j) sg += exp_tab(fma((double)xv[gb][j], invT, -m), s_tab);
-            es += sg;
-            scan[g0 + gb][tid] = sg;
-          }
-        });
-    // scan holds this node's sums of exp(z - M) once rescaled by mref
-    bool scan_ok = true, scan_rel = true;
-    nf = block_or(nf, &s_or);
-    block_lse(m, es, red, s_tab);
-    if (!exchange(a, ep, bl, part, gen, m, nf ? -1.0 : es, xs, &s_or)) {
-      fail_sync(a, b, writer0);
-      return;
-    }
-    // combine the KP partials, lane k of every wave taking partial k
+    // ---- T > 0: max M and sum S of exp(z - M) over the row ------------------
     const bool has = lane < a.KP;
-    const double pm = has ? xs[lane][0] : -INFINITY;
-    const double ps = has ? xs[lane][1] : 0.0;
-    if (__any(has && ps < 0.0)) {
-      if (writer0) write_failure(a, b, SPEC_DEVERR_NONFINITE);
-      return;
+    bool scan_ok = true, scan_rel = true;  // scan: this node's sums of exp(z - M) (rescaled by mref)
+    double M, S, pterm;
+    const int c1 = s_kids[v] ? __ffsll((unsigned long long)s_kids[v]) - 1 : -1;
+    if (LOOK && v == la_node) {
+      // computed in the parent's pass; no per-group sums of this row, so a
+      // terminal sample here streams the row in the selected workgroup
+      la_node = -1;
+      if (la_nf) {
+        if (writer0) write_failure(a, b, SPEC_DEVERR_NONFINITE);
+        return;
+      }
+      M = la_M;
+      S = la_S;
+      pterm = has ? la_sums[lane] : 0.0;
+      scan_ok = false;
+    } else if (LOOK && c1 >= 0) {
+      // One pass over this row and the first child's.  This node has
+      // children, so its visit ends in an accepted child or after a
+      // rejection, whose pass rewrites scan: no per-group sums are kept.
+      la_node = -1;
+      const float* lrow2 = a.logits + (rows_b + c1) * (size_t)a.V;
+      double m = -INFINITY, es = 0.0, m2 = -INFINITY, es2 = 0.0;
+      int nf = 0, nf2 = 0;
+      stream_slice<NG, W, BG2, true>(lrow, -INFINITY, lrow2, -INFINITY, lo, hi,
+          [&](int g0, float (*xv)[W], float (*yv)[W]) {
+            batch_stats<W, BG2>(lo, hi, g0, xv, invT, m, es, nf, s_tab);
+            batch_stats<W, BG2>(lo, hi, g0, yv, invT, m2, es2, nf2, s_tab);
+          });
+      // (block_or is a predicate: one per row)
+      const int nfv = block_or(nf, &s_or);
+      const int nfc = block_or(nf2, &s_or);
+      block_lse(m, es, red, s_tab);
+      block_lse(m2, es2, red, s_tab);
+      if (!exchange4(a, ep, bl, part, gen, m, nfv ? -1.0 : es, m2, nfc ? -1.0 : es2, xs4,
+                     &s_or)) {
+        fail_sync(a, b, writer0);
+        return;
+      }
+      const double pm = has ? xs4[lane][0] : -INFINITY;
+      const double ps = has ? xs4[lane][1] : 0.0;
+      if (__any(has && ps < 0.0)) {
+        if (writer0) write_failure(a, b, SPEC_DEVERR_NONFINITE);
+        return;
+      }
+      M = uni(wave_max_d(pm));
+      pterm = (has && pm != -INFINITY) ? ps * exp_tab(pm - M, s_tab) : 0.0;
+      S = uni(wave_sum_d(pterm));
+      const double pm2 = has ? xs4[lane][2] : -INFINITY;
+      const double ps2 = has ? xs4[lane][3] : 0.0;
+      la_nf = __any(has && ps2 < 0.0);
+      la_M = uni(wave_max_d(pm2));
+      const double pt2 = (has && pm2 != -INFINITY && ps2 > 0.0) ? ps2 * exp_tab(pm2 - la_M, s_tab) : 0.0;
+      la_S = uni(wave_sum_d(pt2));
+      if (tid < a.KP) la_sums[tid] = pt2;  // wave 0: lane == tid
+      la_node = c1;
+      scan_ok = false;
+    } else {
+      la_node = -1;
+      double m = -INFINITY, es = 0.0;
+      int nf = 0;
+      stream_slice<NG, W, BG1, false>(lrow, -INFINITY, lrow, 0.f, lo, hi,
+          [&](int g0, float (*xv)[W], float (*)[W]) {
+            float bmax = -INFINITY;
+#pragma unroll
+            for (int gb = 0; gb < BG1; ++gb)
+#pragma unroll
+              for (int j = 0; j < W; ++j) {
+                const bool valid = elem_index<W>(lo, (g0 + gb) * W + j) < hi;
+                nf |= valid && !isfinite(xv[gb][j]);
+                bmax = fmaxf(bmax, xv[gb][j]);
+              }
+            if (bmax == -INFINITY) {  // nothing valid in this batch
+#pragma unroll
+              for (int gb = 0; gb < BG1; ++gb) scan[g0 + gb][tid] = 0.0;
+              mref[g0 / BG1][tid] = -INFINITY;
+              return;
+            }
+            const double zb = (double)bmax * invT;
+            if (zb > m) {
+              es *= exp_tab(m - zb, s_tab);  // m = -inf: es is still 0
+              m = zb;
+            }
+            mref[g0 / BG1][tid] = m;
+#pragma unroll
+            for (int gb = 0; gb < BG1; ++gb) {
+              // the terms are +0 or positive, so starting from the first one
+              // gives the same sum as starting from 0
+              double sg = exp_tab(fma((double)xv[gb][0], invT, -m), s_tab);
+#pragma unroll
+              for (int j = 1; j < W; ++j) sg += exp_tab(fma((double)xv[gb][j], invT, -m), s_tab);
+              es += sg;
+              scan[g0 + gb][tid] = sg;
+            }
+          });
+      nf = block_or(nf, &s_or);
+      block_lse(m, es, red, s_tab);
+      if (!exchange(a, ep, bl, part, gen, m, nf ? -1.0 : es, xs, &s_or)) {
+        fail_sync(a, b, writer0);
+        return;
+      }
+      // combine the KP partials, lane k of every wave taking partial k
+      const double pm = has ? xs[lane][0] : -INFINITY;
+      const double ps = has ? xs[lane][1] : 0.0;
+      if (__any(has && ps < 0.0)) {
+        if (writer0) write_failure(a, b, SPEC_DEVERR_NONFINITE);
+        return;
+      }
+      M = uni(wave_max_d(pm));
+      pterm = (has && pm != -INFINITY) ? ps * exp_tab(pm - M, s_tab) : 0.0;
+      S = uni(wave_sum_d(pterm));
     }
-    const double M = uni(wave_max_d(pm));
-    double pterm = (has && pm != -INFINITY) ? ps * exp_tab(pm - M, s_tab) : 0.0;
-    double S = uni(wave_sum_d(pterm));
 
     // ---- sampling filters: threshold, then the kept mass per slice ----------
     float lcut = -INFINITY;  // q is restricted to logits >= lcut
@@ -1592,7 +1768,7 @@ AcceptPlan make_accept_plan(int B, int V, bool mapped = false, bool filters = fa
   p.chunk = (int)(per_group * best_ng);
   p.KP = (V + p.chunk - 1) / p.chunk;
   auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  p.ws = p.KP > 1 ? (size_t)B * 2 * p.KP * 8 * sizeof(uint64_t) : 256;
+  p.ws = p.KP > 1 ? (size_t)B * 2 * p.KP * kSlotWords * sizeof(uint64_t) : 256;
   if (mapped) {
     p.off_t2d = align(p.ws);
     p.ws = p.off_t2d + (size_t)V * sizeof(int32_t) + 256;

@@ -286,7 +286,7 @@ size_t spec_accept_tree_workspace_size(int32_t B, int32_t n_max, int32_t V);
  * allocating library routine).  The array's device address is looked up once
  * per GPU, on the first call with that GPU current.  A batch needing more
  * than the array (spec_accept_tree_workspace_size(B, n_max, V) > 1 MiB, about
- * 1,000 sequences of a 128k vocabulary) returns SPEC_E_SCRATCH before any
+ * 500 sequences of a 128k vocabulary) returns SPEC_E_SCRATCH before any
  * launch.  The array keeps what the last call left in it; nothing in it needs
  * clearing (each exchange word carries its launch's tag).  Every call on one
  * GPU shares the array: calls that may overlap on one GPU (different streams

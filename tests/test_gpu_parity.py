@@ -147,6 +147,40 @@ def test_pipelined_order_is_bit_identical(hip_lib, monkeypatch, rope):
         compare_attention(w, outs[0].cpu().numpy(), nodes_per_seq=8, rng=np.random.default_rng(5))
 
 
+@pytest.mark.parametrize("vocab", [500, 32000])
+def test_first_child_rows_read_ahead(hip_lib, vocab):
+    """With short slices a node's statistics pass also covers its first
+    child's row.  A NaN there fails the sequence only if the walk enters that
+    child, as when every row is read at its own visit: NaN in an entered
+    node's row (even sequences) and in a first child the walk passes over
+    (odd ones)."""
+    w = make_workload(4, batch=8, prefix=(20, 40), vocab=vocab, poison=False, seed=11, T=1.0)
+    say(f"[gpu] first-child rows read ahead: V={w.V}")
+    entered, passed = [], []
+    for b in range(w.B):
+        r = oracle_accept(w, b)
+        path = [int(x) for x in r.path[: r.accept_len + 1]]
+        n = int(w.n_nodes[b])
+        if b % 2 == 0 and len(path) > 1:
+            w.logits[b, path[1], 7] = np.nan
+            entered.append(b)
+            continue
+        for d, v in enumerate(path):
+            kids = [c for c in range(v + 1, n) if w.parents[b, c] == v]
+            if kids and (d + 1 == len(path) or path[d + 1] != kids[0]):
+                w.logits[b, kids[0], 7] = np.nan
+                passed.append(b)
+                break
+    assert len(entered) >= 2 and len(passed) >= 2, (entered, passed)
+    dev = to_device(w)
+    host = run_gpu_step(w, dev, commit=False)
+    from eagle_tree_verification_amd import api
+    assert host["dev_error"] == api.DEVERR_NONFINITE
+    assert all(host["accept_len"][b] == -1 for b in entered)
+    assert all(host["accept_len"][b] >= 0 for b in passed)
+    compare_accept(w, host)
+
+
 def test_device_errors_are_reported(hip_lib):
     w = make_workload(4, batch=4, prefix=(20, 40), vocab=500, poison=False, seed=5)
     w.parents[0, 5] = 7          # parent after child: bad tree
