@@ -126,6 +126,35 @@ __device__ __forceinline__ double exp_tab(double y, const double* tab) {
   return ldexp(tab[ni & (kTab - 1)] * p, ni >> kTabBits);
 }
 
+// exp(y) for -700 <= y <= 0 (up to rounding; the caller checks the bound):
+// exp_tab without the clamp, and 2^k applied by an integer add to the
+// exponent field instead of ldexp.  tab2[j] is tab[j] with j << 12 taken off
+// its high word, so adding ni << 12 = (k << 20) + (j << 12) adds k to the
+// exponent; the scaled entry stays normal (k >= -1011), so the product
+// rounds exactly as exp_tab's does: the same bits.
+__device__ __forceinline__ double exp_fast(double y, const double* tab2) {
+  constexpr double kInvLn2xT = 369.3299304675746;  // 256 / ln2
+  constexpr double kShift = 6755399441055744.0;     // 1.5 * 2^52
+  constexpr double kLn2HiT = 6.93147180369123816490e-01 / kTab;
+  constexpr double kLn2LoT = 1.90821492927058770002e-10 / kTab;
+  const double t = fma(y, kInvLn2xT, kShift);
+  const double n = t - kShift;
+  const int ni = __double2loint(t);
+  double r = fma(-n, kLn2HiT, y);
+  r = fma(-n, kLn2LoT, r);
+  double p = 1.0 / 24.0;
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  const double tv = tab2[ni & (kTab - 1)];
+  const int hi = (int)((uint32_t)__double2hiint(tv) + ((uint32_t)ni << 12));
+  return p * __hiloint2double(hi, __double2loint(tv));
+}
+
+// Lower bound on z - m (the running max) under which a batch uses exp_fast.
+constexpr double kFastFloor = -700.0;
+
 struct AcceptArgs {
   const int32_t* tokens;
   const int32_t* parents;
@@ -662,8 +691,8 @@ __device__ __forceinline__ void stream_slice(const float* r1, float f1, const fl
 template <int W, int BG>
 __device__ __forceinline__ void batch_stats(int lo, int hi, int g0, const float (*xv)[W],
                                             double invT, double& m, double& es, int& nf,
-                                            const double* tab) {
-  float bmax = -INFINITY;
+                                            const double* tab, const double* tab2) {
+  float bmax = -INFINITY, bmin = INFINITY;
 #pragma unroll
   for (int gb = 0; gb < BG; ++gb)
 #pragma unroll
@@ -671,6 +700,7 @@ __device__ __forceinline__ void batch_stats(int lo, int hi, int g0, const float 
       const bool valid = elem_index<W>(lo, (g0 + gb) * W + j) < hi;
       nf |= valid && !isfinite(xv[gb][j]);
       bmax = fmaxf(bmax, xv[gb][j]);
+      bmin = fminf(bmin, xv[gb][j]);
     }
   if (bmax == -INFINITY) return;  // nothing valid in this batch
   const double zb = (double)bmax * invT;
@@ -678,12 +708,22 @@ __device__ __forceinline__ void batch_stats(int lo, int hi, int g0, const float 
     es *= exp_tab(m - zb, tab);  // m = -inf: es is still 0
     m = zb;
   }
+  if (__all(fma((double)bmin, invT, -m) >= kFastFloor)) {
 #pragma unroll
-  for (int gb = 0; gb < BG; ++gb) {
-    double sg = exp_tab(fma((double)xv[gb][0], invT, -m), tab);
+    for (int gb = 0; gb < BG; ++gb) {
+      double sg = exp_fast(fma((double)xv[gb][0], invT, -m), tab2);
 #pragma unroll
-    for (int j = 1; j < W; ++j) sg += exp_tab(fma((double)xv[gb][j], invT, -m), tab);
-    es += sg;
+      for (int j = 1; j < W; ++j) sg += exp_fast(fma((double)xv[gb][j], invT, -m), tab2);
+      es += sg;
+    }
+  } else {
+#pragma unroll
+    for (int gb = 0; gb < BG; ++gb) {
+      double sg = exp_tab(fma((double)xv[gb][0], invT, -m), tab);
+#pragma unroll
+      for (int j = 1; j < W; ++j) sg += exp_tab(fma((double)xv[gb][j], invT, -m), tab);
+      es += sg;
+    }
   }
 }
 
@@ -954,6 +994,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
   __shared__ int s_or, s_hit, s_first;
   __shared__ float s_kp[SPEC_MAX_NODES], s_kl[SPEC_MAX_NODES], s_ku[SPEC_MAX_NODES], s_us;
   __shared__ double s_tab[kTab];
+  __shared__ double s_tab2[FILT ? 1 : kTab];  // s_tab for exp_fast
   // filtered rows: bit g * W + j set where this thread's entry j of group g is
   // kept (all bits once a negative draft entry is seen)
   __shared__ unsigned long long s_keep[FILT ? NT : 1];
@@ -991,8 +1032,13 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
                                           __HIP_MEMORY_SCOPE_AGENT)
                       : 0u)));
 
-  for (int j = tid; j < kTab; j += NT)
-    s_tab[j] = 2.0 * exp_nonpos((double)(j - kTab) / kTab * 0.6931471805599453);
+  for (int j = tid; j < kTab; j += NT) {
+    const double tj = 2.0 * exp_nonpos((double)(j - kTab) / kTab * 0.6931471805599453);
+    s_tab[j] = tj;
+    if (!FILT)
+      s_tab2[j] = __hiloint2double((int)((uint32_t)__double2hiint(tj) - ((uint32_t)j << 12)),
+                                   __double2loint(tj));
+  }
 
   // ---- validation (identical in every workgroup of the sequence) ----------
   int err = 0;
@@ -1186,8 +1232,8 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       int nf = 0, nf2 = 0;
       stream_slice<NG, W, BG2, true>(lrow, -INFINITY, lrow2, -INFINITY, lo, hi,
           [&](int g0, float (*xv)[W], float (*yv)[W]) {
-            batch_stats<W, BG2>(lo, hi, g0, xv, invT, m, es, nf, s_tab);
-            batch_stats<W, BG2>(lo, hi, g0, yv, invT, m2, es2, nf2, s_tab);
+            batch_stats<W, BG2>(lo, hi, g0, xv, invT, m, es, nf, s_tab, s_tab2);
+            batch_stats<W, BG2>(lo, hi, g0, yv, invT, m2, es2, nf2, s_tab, s_tab2);
           });
       // (block_or is a predicate: one per row)
       const int nfv = block_or(nf, &s_or);
@@ -1223,7 +1269,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
       int nf = 0;
       stream_slice<NG, W, BG1, false>(lrow, -INFINITY, lrow, 0.f, lo, hi,
           [&](int g0, float (*xv)[W], float (*)[W]) {
-            float bmax = -INFINITY;
+            float bmax = -INFINITY, bmin = INFINITY;
 #pragma unroll
             for (int gb = 0; gb < BG1; ++gb)
 #pragma unroll
@@ -1231,6 +1277,7 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
                 const bool valid = elem_index<W>(lo, (g0 + gb) * W + j) < hi;
                 nf |= valid && !isfinite(xv[gb][j]);
                 bmax = fmaxf(bmax, xv[gb][j]);
+                if (!FILT) bmin = fminf(bmin, xv[gb][j]);
               }
             if (bmax == -INFINITY) {  // nothing valid in this batch
 #pragma unroll
@@ -1244,15 +1291,26 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
               m = zb;
             }
             mref[g0 / BG1][tid] = m;
+            // the terms are +0 or positive, so starting from the first one
+            // gives the same sum as starting from 0
+            if (!FILT && __all(fma((double)bmin, invT, -m) >= kFastFloor)) {
 #pragma unroll
-            for (int gb = 0; gb < BG1; ++gb) {
-              // the terms are +0 or positive, so starting from the first one
-              // gives the same sum as starting from 0
-              double sg = exp_tab(fma((double)xv[gb][0], invT, -m), s_tab);
+              for (int gb = 0; gb < BG1; ++gb) {
+                double sg = exp_fast(fma((double)xv[gb][0], invT, -m), s_tab2);
 #pragma unroll
-              for (int j = 1; j < W; ++j) sg += exp_tab(fma((double)xv[gb][j], invT, -m), s_tab);
-              es += sg;
-              scan[g0 + gb][tid] = sg;
+                for (int j = 1; j < W; ++j) sg += exp_fast(fma((double)xv[gb][j], invT, -m), s_tab2);
+                es += sg;
+                scan[g0 + gb][tid] = sg;
+              }
+            } else {
+#pragma unroll
+              for (int gb = 0; gb < BG1; ++gb) {
+                double sg = exp_tab(fma((double)xv[gb][0], invT, -m), s_tab);
+#pragma unroll
+                for (int j = 1; j < W; ++j) sg += exp_tab(fma((double)xv[gb][j], invT, -m), s_tab);
+                es += sg;
+                scan[g0 + gb][tid] = sg;
+              }
             }
           });
       nf = block_or(nf, &s_or);
@@ -1419,6 +1477,15 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
         bool pneg = false;
         stream_slice<NG, W, BG2, true, MAPPED>(lrow, -INFINITY, prow, 0.f, lo, hi,
             [&](int g0, float (*xv)[W], float (*pv)[W]) {
+              bool fast = false;
+              if (!FILT) {
+                float bmin = INFINITY;
+#pragma unroll
+                for (int gb = 0; gb < BG2; ++gb)
+#pragma unroll
+                  for (int j = 0; j < W; ++j) bmin = fminf(bmin, xv[gb][j]);
+                fast = __all(fma((double)bmin, invT, -M) >= kFastFloor);
+              }
 #pragma unroll
               for (int gb = 0; gb < BG2; ++gb) {
                 double sg = 0.0;
@@ -1426,8 +1493,10 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
                 for (int j = 0; j < W; ++j) {
                   pnf |= !isfinite(pv[gb][j]);
                   if (FILT) pneg |= pv[gb][j] < 0.f;
-                  const double e =
-                      kept(xv[gb][j]) ? exp_tab(fma((double)xv[gb][j], invT, -M), s_tab) : 0.0;
+                  const double y = fma((double)xv[gb][j], invT, -M);
+                  const double e = !kept(xv[gb][j]) ? 0.0
+                                   : fast           ? exp_fast(y, s_tab2)
+                                                    : exp_tab(y, s_tab);
                   sg += fmax(0.0, e - CnS * (double)pv[gb][j]);
                 }
                 zp += sg;
