@@ -1477,6 +1477,24 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
         bool pneg = false;
         stream_slice<NG, W, BG2, true, MAPPED>(lrow, -INFINITY, prow, 0.f, lo, hi,
             [&](int g0, float (*xv)[W], float (*pv)[W]) {
+              // one batch with the given exp (a separate loop for each, so
+              // that only the chosen one runs)
+              auto batch = [&](auto expf) {
+#pragma unroll
+                for (int gb = 0; gb < BG2; ++gb) {
+                  double sg = 0.0;
+#pragma unroll
+                  for (int j = 0; j < W; ++j) {
+                    pnf |= !isfinite(pv[gb][j]);
+                    if (FILT) pneg |= pv[gb][j] < 0.f;
+                    const double e =
+                        kept(xv[gb][j]) ? expf(fma((double)xv[gb][j], invT, -M)) : 0.0;
+                    sg += fmax(0.0, e - CnS * (double)pv[gb][j]);
+                  }
+                  zp += sg;
+                  scan[g0 + gb][tid] = sg;
+                }
+              };
               bool fast = false;
               if (!FILT) {
                 float bmin = INFINITY;
@@ -1486,22 +1504,8 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
                   for (int j = 0; j < W; ++j) bmin = fminf(bmin, xv[gb][j]);
                 fast = __all(fma((double)bmin, invT, -M) >= kFastFloor);
               }
-#pragma unroll
-              for (int gb = 0; gb < BG2; ++gb) {
-                double sg = 0.0;
-#pragma unroll
-                for (int j = 0; j < W; ++j) {
-                  pnf |= !isfinite(pv[gb][j]);
-                  if (FILT) pneg |= pv[gb][j] < 0.f;
-                  const double y = fma((double)xv[gb][j], invT, -M);
-                  const double e = !kept(xv[gb][j]) ? 0.0
-                                   : fast           ? exp_fast(y, s_tab2)
-                                                    : exp_tab(y, s_tab);
-                  sg += fmax(0.0, e - CnS * (double)pv[gb][j]);
-                }
-                zp += sg;
-                scan[g0 + gb][tid] = sg;
-              }
+              if (fast) batch([&](double y) { return exp_fast(y, s_tab2); });
+              else batch([&](double y) { return exp_tab(y, s_tab); });
             }, a.t2d);
         if (FILT && masks && pneg) s_keep[tid] = ~0ull;
       }
