@@ -147,15 +147,17 @@ def test_pipelined_order_is_bit_identical(hip_lib, monkeypatch, rope):
         compare_attention(w, outs[0].cpu().numpy(), nodes_per_seq=8, rng=np.random.default_rng(5))
 
 
+@pytest.mark.parametrize("T", [0.0, 1.0])
 @pytest.mark.parametrize("vocab", [500, 32000])
-def test_first_child_rows_read_ahead(hip_lib, vocab):
-    """With short slices a node's statistics pass also covers its first
-    child's row.  A NaN there fails the sequence only if the walk enters that
-    child, as when every row is read at its own visit: NaN in an entered
-    node's row (even sequences) and in a first child the walk passes over
-    (odd ones)."""
-    w = make_workload(4, batch=8, prefix=(20, 40), vocab=vocab, poison=False, seed=11, T=1.0)
-    say(f"[gpu] first-child rows read ahead: V={w.V}")
+def test_first_child_rows_read_ahead(hip_lib, vocab, T):
+    """With short slices a node's statistics pass (T > 0) also covers its
+    first child's row.  A NaN there fails the sequence only if the walk enters
+    that child, as when every row is read at its own visit: NaN in an entered
+    node's row (even sequences) and in a first child the walk passes over (odd
+    ones).  T = 0 checks the same for the greedy walk, which reads each row at
+    its own visit."""
+    w = make_workload(4, batch=8, prefix=(20, 40), vocab=vocab, poison=False, seed=11, T=T)
+    say(f"[gpu] first-child rows read ahead: V={w.V} T={T}")
     entered, passed = [], []
     for b in range(w.B):
         r = oracle_accept(w, b)
