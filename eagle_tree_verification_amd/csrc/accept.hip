@@ -1449,30 +1449,38 @@ __global__ __launch_bounds__(NT) void accept_kernel(AcceptArgs a) {
         // (q is 0 elsewhere and the draft row, already checked, has no
         // negative entry), so each thread gathers just those.  The group sums
         // are the streamed pass's bit for bit (its other terms are zeros).
+        // The thread's (at most kMaskMax = 2) kept entries, both loaded at
+        // once at valid indices (loads under a branch would be waited for one
+        // by one); every other group sum is zero.
+        static_assert(kMaskMax == 2, "two kept entries per thread");
         const unsigned long long km = s_keep[tid];
-#pragma unroll 1
-        for (int g = 0; g < NG; ++g) {
-          double sg = 0.0;
-          const unsigned gm = (unsigned)(km >> (g * W)) & ((1u << W) - 1u);
-          if (gm) {
-#pragma unroll
-            for (int j = 0; j < W; ++j)
-              if (gm & (1u << j)) {
-                const int i = elem_index<W>(lo, g * W + j);
-                float pe;
-                if constexpr (MAPPED) {
-                  const int t = a.t2d[i];
-                  pe = t >= 0 ? prow[t] : 0.f;
-                } else {
-                  pe = prow[i];
-                }
-                const double e = exp_tab(fma((double)lrow[i], invT, -M), s_tab);
-                sg += fmax(0.0, e - CnS * (double)pe);
-              }
-          }
-          zp += sg;
-          scan[g][tid] = sg;
+        const unsigned long long km1 = km & (km - 1);
+        const int k0 = km ? __ffsll(km) - 1 : -1;
+        const int k1 = km1 ? __ffsll(km1) - 1 : -1;
+        const int i0 = k0 >= 0 ? elem_index<W>(lo, k0) : lo;
+        const int i1 = k1 >= 0 ? elem_index<W>(lo, k1) : lo;
+        float p0, p1;
+        if constexpr (MAPPED) {
+          const int t0 = a.t2d[i0], t1 = a.t2d[i1];
+          const float q0 = prow[max(t0, 0)], q1 = prow[max(t1, 0)];
+          p0 = t0 >= 0 ? q0 : 0.f;
+          p1 = t1 >= 0 ? q1 : 0.f;
+        } else {
+          p0 = prow[i0];
+          p1 = prow[i1];
         }
+        const float z0 = lrow[i0], z1 = lrow[i1];
+        const double r0 = k0 < 0 ? 0.0
+            : fmax(0.0, exp_tab(fma((double)z0, invT, -M), s_tab) - CnS * (double)p0);
+        const double r1 = k1 < 0 ? 0.0
+            : fmax(0.0, exp_tab(fma((double)z1, invT, -M), s_tab) - CnS * (double)p1);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) scan[g][tid] = 0.0;
+        // the streamed pass adds the same terms in the same order (the others
+        // are +0), so these are its sums bit for bit
+        if (k0 >= 0) scan[k0 / W][tid] = r0;
+        if (k1 >= 0) scan[k1 / W][tid] = k1 / W == k0 / W ? r0 + r1 : r1;
+        zp = r0 + r1;
       } else {
         bool pneg = false;
         stream_slice<NG, W, BG2, true, MAPPED>(lrow, -INFINITY, prow, 0.f, lo, hi,
